@@ -41,7 +41,7 @@ def _load():
         lib.oracle_philox4x32_10.restype = None
         lib.oracle_qsdp_uniform.argtypes = [C.c_uint64, _I64]
         lib.oracle_qsdp_uniform.restype = C.c_uint32
-        lib.oracle_qsdp_quantize.argtypes = [_P, _I64, _I, _I, C.c_uint64, _P, _P, _P]
+        lib.oracle_qsdp_quantize.argtypes = [_P, _I64, _I, _I, C.c_uint64, _I64, _P, _P, _P]
         lib.oracle_qsdp_dequantize.argtypes = [_P, _P, _P, _I64, _I, _I, _P, _P]
         lib.oracle_f32_to_bf16.argtypes = [_F]
         lib.oracle_f32_to_bf16.restype = C.c_uint16
@@ -188,8 +188,8 @@ def qsdp_uniform(seed: int, i: int) -> int:
     return int(_load().oracle_qsdp_uniform(seed, i))
 
 
-def qsdp_quantize(x_bf16, *, bucket, bits, seed):
-    """x_bf16: uint16 bit patterns.  Returns (codes uint8, bucket_min f32, bucket_max f32)."""
+def qsdp_quantize(x_bf16, *, bucket, bits, seed, first_index=0):
+    """x_bf16: uint16 bit patterns (global indices first_index...).  Returns (codes, bucket_min, bucket_max)."""
     lib = _load()
     x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     n = x_bf16.size
@@ -197,7 +197,8 @@ def qsdp_quantize(x_bf16, *, bucket, bits, seed):
     codes = np.zeros(max((n + 1) // 2 if bits == 4 else n, 1), dtype=np.uint8)
     bmin = np.zeros(max(nb, 1), dtype=np.float32)
     bmax = np.zeros(max(nb, 1), dtype=np.float32)
-    _check(lib.oracle_qsdp_quantize(_ptr(x_bf16), n, bucket, bits, seed, _ptr(codes), _ptr(bmin), _ptr(bmax)),
+    _check(lib.oracle_qsdp_quantize(_ptr(x_bf16), n, bucket, bits, seed, first_index, _ptr(codes), _ptr(bmin),
+                                    _ptr(bmax)),
            "qsdp_quantize")
     return codes[:((n + 1) // 2 if bits == 4 else n)], bmin[:nb], bmax[:nb]
 

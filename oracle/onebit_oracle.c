@@ -411,15 +411,27 @@ uint32_t oracle_qsdp_uniform(uint64_t seed, int64_t i)
     return out[i & 3];
 }
 
+/* IEEE 754 totalOrder restricted to non-NaN values: like <, but -0 < +0.  The
+ * pages do not say which zero is a bucket's minimum; this reading makes min and
+ * max independent of the order in which the elements are visited. */
+static int total_order_less(float a, float b)
+{
+    return a < b || (a == b && signbit(a) && !signbit(b));
+}
+
 /* ------------------------------------------------- O5: QSDP quantize
  * [QSDP] "proposed method": an unbiased operator that stochastically rounds each
  * weight to one of the two nearest quantization levels, so the expectation equals
  * the weight.  Levels: 2^bits evenly spaced over the bucket's [min, max].
+ * first_index is the global index of x_bf16[0] (a multiple of the bucket): the
+ * Philox counter uses global element indices, so a slice of a larger vector can
+ * be checked on its own.
  */
 int oracle_qsdp_quantize(const uint16_t *x_bf16, int64_t n, int bucket, int nbits, uint64_t seed,
-                         uint8_t *codes, float *bucket_min, float *bucket_max)
+                         int64_t first_index, uint8_t *codes, float *bucket_min, float *bucket_max)
 {
-    if (n < 0 || bucket < 1 || (nbits != 4 && nbits != 8))
+    if (n < 0 || bucket < 1 || (nbits != 4 && nbits != 8) || first_index < 0 ||
+        first_index % bucket != 0 || (nbits == 4 && first_index % 2 != 0))
         return ORACLE_ERR_INVALID;
     if (n == 0)
         return ORACLE_OK;
@@ -435,9 +447,9 @@ int oracle_qsdp_quantize(const uint16_t *x_bf16, int64_t n, int bucket, int nbit
         float mn = oracle_bf16_to_f32(x_bf16[lo]), mx = mn;
         for (int64_t i = lo + 1; i < hi; ++i) {
             const float xi = oracle_bf16_to_f32(x_bf16[i]);
-            if (xi < mn)
+            if (total_order_less(xi, mn))
                 mn = xi;
-            if (xi > mx)
+            if (total_order_less(mx, xi))
                 mx = xi;
         }
         bucket_min[b] = mn;
@@ -453,7 +465,7 @@ int oracle_qsdp_quantize(const uint16_t *x_bf16, int64_t n, int bucket, int nbit
                     k = (float)L;
                 const float p = t - k;                                    /* exact */
                 const uint64_t thr = (uint64_t)floor((double)p * 4294967296.0); /* exact */
-                const uint32_t u = oracle_qsdp_uniform(seed, i);
+                const uint32_t u = oracle_qsdp_uniform(seed, first_index + i);
                 code = (uint32_t)k + ((uint64_t)u < thr ? 1u : 0u);
                 if (code > (uint32_t)L)
                     code = (uint32_t)L;

@@ -161,3 +161,20 @@ def test_philox_element_stream_matches_independent_implementations(which):
         got = _external("USE_TORCH", inc)
     want = [oracle.qsdp_uniform(s, i) for s, i in SAMPLES]
     assert got == want
+
+
+def test_signed_zero_order_and_slices():
+    """Reading: min/max follow IEEE totalOrder (-0 < +0); a slice quantized with its
+    global first index reproduces the same codes as the whole vector."""
+    x = bf16([0.0, -0.0, 1.0, 2.0, -1.0, -0.0, 0.0, -2.0])
+    codes, mn, mx = oracle.qsdp_quantize(x, bucket=4, bits=8, seed=3)
+    assert np.signbit(mn[0]) and mn[0] == 0 and mx[0] == 2.0
+    assert mn[1] == -2.0 and mx[1] == 0.0 and not np.signbit(mx[1])
+    rng = np.random.default_rng(9)
+    big = bf16(rng.standard_normal(4096) * 0.02)
+    for bits in (4, 8):
+        full, fmn, fmx = oracle.qsdp_quantize(big, bucket=1024, bits=bits, seed=77)
+        part, pmn, pmx = oracle.qsdp_quantize(big[2048:3072], bucket=1024, bits=bits, seed=77, first_index=2048)
+        per = 2 if bits == 4 else 1
+        np.testing.assert_array_equal(part, full[2048 // per:3072 // per])
+        assert pmn[0] == fmn[2] and pmx[0] == fmx[2]
