@@ -1,0 +1,284 @@
+"""Benchmark: fused 1-bit compress + frozen-v update on one MI355X.
+
+Headline (one JSON line on stdout): params/s of onebit_compress_update on the
+BERT-Large-shaped flat vector (335,143,938 fp32 params in 393 tensors, one scale
+per tensor, 8 masked tensors, one compressed step per call), with inputs
+resident in HBM.  A "step" is one such call.  Also reported:
+  roofline     the dominant kernel (the one-pass cooperative compression kernel):
+               algorithmic bytes per launch / its mean launch time from HIP events
+               recorded around each launch on the launch stream, against 8 TB/s;
+  cpu_baseline the CPU oracle (single thread) on a bounded sample of the same
+               workload, timed on this host;
+  rows         the other hot-path kernels measured the same way (warmup Adam step,
+               the GPT-2-XL-shaped bf16-gradient vector, the 16-worker simulated
+               all-reduce, QSDP quantize/dequantize) unless --headline-only.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+B_COMPRESS_F32 = 32.125      # read g,m,e,v,x (20 B); write m,e,x (12 B); bits (1/8 B)
+B_COMPRESS_BF16_COPY = 32.125  # read g bf16 (2),m,e,v,x (16); write m,e,x (12), x_bf16 (2); bits
+B_WARMUP = 28.0              # read g,m,v,x; write m,v,x
+B_WORKER = 16.125            # read g,m,e; write e; bits
+B_QSDP4, B_QSDP8 = 2.0 + 0.5 + 8.0 / 1024, 2.0 + 1.0 + 8.0 / 1024
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ensure_built():
+    from error_compensated_bit_amd import onebit
+    if not os.path.exists(onebit.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    onebit.load()
+
+
+class KernelTimer:
+    """Per-kernel-class HIP event timing over a region (library launch profiler)."""
+
+    def __enter__(self):
+        from error_compensated_bit_amd import onebit as ob
+        ob.onebit_profile_begin()
+        return self
+
+    def __exit__(self, *exc):
+        from error_compensated_bit_amd import onebit as ob
+        self.result = ob.onebit_profile_end()
+        return False
+
+    def mean_ms(self, cls):
+        ms, n = self.result[cls]
+        return ms / n if n else None
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    with KernelTimer() as kt:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    return (t1 - t0) / steps, kt
+
+
+def compress_setup(wl, dev):
+    import torch
+    from error_compensated_bit_amd import onebit as ob
+    from error_compensated_bit_amd import workloads as W
+    x, m, e, v = W.init_state(wl, device=dev)
+    g = W.gradient(wl, 1, device=dev)
+    plan = ob.onebit_plan_create(wl.chunk_off, wl.tensor_off, wl.tensor_keep)
+    bits = torch.zeros(ob.onebit_plan_words(plan), dtype=torch.int32, device=dev)
+    scales = torch.zeros(ob.onebit_plan_chunks(plan), dtype=torch.float32, device=dev)
+    ws = torch.zeros(ob.onebit_plan_workspace_bytes(plan) // 8, dtype=torch.int64, device=dev)
+    xb = torch.zeros(wl.n, dtype=torch.bfloat16, device=dev) if wl.x_bf16_copy else None
+    hp = dict(lr=wl.hyper["lr"], beta1=wl.hyper["beta1"], eps=wl.hyper["eps"], weight_decay=wl.hyper["weight_decay"])
+
+    def step():
+        ob.onebit_compress_update(plan, g, m, e, v, x, xb, bits, scales, workspace=ws, **hp)
+
+    return plan, step, ws
+
+
+def onepass_elements(wl, plan):
+    """Elements of the chunks the one-pass kernel handles (chunks <= capacity tiles)."""
+    import numpy as np
+    from error_compensated_bit_amd import onebit as ob
+    cap = ob.onebit_plan_stats(plan)["coop_capacity"]
+    lens = np.diff(wl.chunk_off)
+    tiles = np.maximum(1, (lens + 4095) // 4096)
+    return int(lens[tiles <= cap].sum())
+
+
+def bench_compress(wl, steps, warmup, dev, bpe):
+    from error_compensated_bit_amd import onebit as ob
+    plan, step, ws = compress_setup(wl, dev)
+    t, kt = timed(step, steps, warmup)
+    assert ob.onebit_workspace_status(ws) == 0, "a cross-workgroup wait timed out"
+    n1 = onepass_elements(wl, plan)
+    k_ms = kt.mean_ms("compress_onepass")
+    res = dict(seconds_per_call=t, params_per_s=wl.n / t, gbps=bpe * wl.n / t / 1e9,
+               onepass_elements=n1, onepass_ms=k_ms, plan=ob.onebit_plan_stats(plan),
+               kernels={k: v for k, v in kt.result.items() if v[1]})
+    if k_ms:
+        res["onepass_gbps"] = bpe * n1 / (k_ms * 1e-3) / 1e9
+    return res
+
+
+def cpu_baseline(wl, dev, budget_s=12.0):
+    """Time the CPU oracle on whole chunks of the workload until about budget_s of work."""
+    import numpy as np
+    import oracle
+    from error_compensated_bit_amd import workloads as W
+    state = W.init_state(wl, device=dev)
+    gd = W.gradient(wl, 1, device=dev)
+    gd = gd.float() if wl.grad_bf16 else gd
+    done = 0
+    spent = 0.0
+    chunks = []
+    order = np.random.default_rng(0).permutation(wl.n_chunks)
+    for j in order:
+        lo, hi = int(wl.chunk_off[j]), int(wl.chunk_off[j + 1])
+        off = np.array([0, hi - lo], np.int64)
+        keep_el = None
+        if wl.tensor_keep is not None:
+            t = int(np.searchsorted(wl.tensor_off, lo, side="right") - 1)
+            keep_el = (np.array([0, hi - lo], np.int64), wl.tensor_keep[t:t + 1])
+        x, m, e, v = (t[lo:hi].cpu().numpy() for t in state)
+        args = [gd[lo:hi].cpu().numpy(), m, e, v, x]
+        t0 = time.perf_counter()
+        oracle.compress_update(off, *args, tensor_off=keep_el[0] if keep_el else None,
+                               tensor_keep=keep_el[1] if keep_el else None, lr=1e-3, beta1=0.9, eps=1e-8)
+        spent += time.perf_counter() - t0
+        done += hi - lo
+        chunks.append(int(j))
+        if spent >= budget_s:
+            break
+    return dict(value=done / spent, unit="params/s", cores=1, kind="oracle",
+                sample=f"{len(chunks)} whole chunks ({done} params, {100.0 * done / wl.n:.1f}% of the vector) "
+                       f"of the same workload, one compressed step each, single-threaded C oracle",
+                seconds=spent)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="bert_large", choices=["bert_large", "gpt2_xl"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path: the compressed all-reduce is simulated inside one GPU's memory)", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    ensure_built()
+    from error_compensated_bit_amd import workloads as W
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    wl = W.bert_like() if args.workload == "bert_large" else W.gpt2_like()
+    bpe = B_COMPRESS_F32
+    log(f"[bench] workload {wl.name}: n={wl.n} chunks={wl.n_chunks}")
+    head = bench_compress(wl, args.steps, args.warmup, dev, bpe)
+    log(f"[bench] {head['params_per_s'] / 1e9:.1f} G params/s, {head['gbps']:.0f} GB/s algorithmic; "
+        f"kernels {head['kernels']}")
+    torch.cuda.empty_cache()
+
+    rows = {}
+    if not args.headline_only:
+        rows = secondary_rows(dev, args)
+
+    base = None if args.no_cpu_baseline else cpu_baseline(wl, dev)
+    if base:
+        log(f"[bench] cpu oracle {base['value'] / 1e6:.1f} M params/s on {base['sample']}")
+
+    k_ms = head.get("onepass_ms")
+    achieved = head.get("onepass_gbps")
+    line = {
+        "metric": "params/sec and HBM GB/s (% of peak) for fused 1-bit compress+update",
+        "value": head["params_per_s"],
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["seconds_per_call"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_gbps": head["gbps"],
+        "hbm_frac": head["gbps"] / PEAK_HBM_GBPS,
+        "config": {"workload": f"{wl.name} flat vector: {wl.n} fp32 params, {wl.n_chunks} chunks "
+                               f"(one per tensor), {int((wl.tensor_keep == 0).sum()) if wl.tensor_keep is not None else 0}"
+                               f" masked tensors, one compressed step per call",
+                   "params": wl.n, "chunks": wl.n_chunks, "grad_dtype": "bf16" if wl.grad_bf16 else "f32",
+                   "bytes_per_param": bpe, "plan": head["plan"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": (achieved / PEAK_HBM_GBPS) if achieved else None, "traffic": None,
+                     "kernel": "k_compress_onepass", "bytes_per_launch": bpe * head["onepass_elements"],
+                     "mean_launch_ms": k_ms},
+        "cpu_baseline": ({k: base[k] for k in ("value", "unit", "cores", "kind", "sample")} if base else None),
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def secondary_rows(dev, args):
+    import numpy as np
+    import torch
+    from error_compensated_bit_amd import onebit as ob
+    from error_compensated_bit_amd import workloads as W
+    rows = {}
+    steps = max(3, args.steps // 3)
+
+    # warmup Adam step on the BERT-Large-sized vector
+    n = 335_143_938
+    x = torch.zeros(n, device=dev)
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    g = torch.randn(n, device=dev) * 1e-3
+
+    def warm():
+        ob.onebit_adam_warmup_step(x, m, v, g, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                                   bias_correction=False, step=1)
+    t, kt = timed(warm, steps, 2)
+    km = kt.mean_ms("warmup")
+    rows["warmup_adam_bert_large"] = dict(params_per_s=n / t, gbps=B_WARMUP * n / t / 1e9,
+                                          kernel_gbps=B_WARMUP * n / (km * 1e-3) / 1e9)
+    del x, m, v, g
+    torch.cuda.empty_cache()
+    log(f"[bench] warmup {rows['warmup_adam_bert_large']}")
+
+    # QSDP on 1.3e9 bf16 weights
+    q = W.QsdpWorkload()
+    xq = W.qsdp_weights(q, device=dev)
+    nb = (q.n + q.bucket - 1) // q.bucket
+    bmin = torch.zeros(nb, device=dev)
+    bmax = torch.zeros(nb, device=dev)
+    for bits, bpe in ((4, B_QSDP4), (8, B_QSDP8)):
+        codes = torch.zeros(q.n if bits == 8 else (q.n + 1) // 2, dtype=torch.uint8, device=dev)
+        out = torch.zeros(q.n, dtype=torch.bfloat16, device=dev)
+        tq, ktq = timed(lambda: ob.qsdp_quantize(xq, q.bucket, bits, 0, codes, bmin, bmax), steps, 1)
+        td, ktd = timed(lambda: ob.qsdp_dequantize(codes, bmin, bmax, q.n, q.bucket, bits, out), steps, 1)
+        rows[f"qsdp{bits}_quantize"] = dict(elems_per_s=q.n / tq, gbps=bpe * q.n / tq / 1e9)
+        rows[f"qsdp{bits}_dequantize"] = dict(elems_per_s=q.n / td, gbps=bpe * q.n / td / 1e9)
+        del codes, out
+    del xq, bmin, bmax
+    torch.cuda.empty_cache()
+    log(f"[bench] qsdp {[(k, v) for k, v in rows.items() if 'qsdp' in k]}")
+
+    # GPT-2-XL-shaped vector, bf16 gradients, bf16 copy of x
+    wl = W.gpt2_like()
+    r = bench_compress(wl, steps, 1, dev, B_COMPRESS_BF16_COPY)
+    rows["compress_gpt2_xl_bf16"] = {k: r[k] for k in ("params_per_s", "gbps", "onepass_gbps", "plan")
+                                     if k in r}
+    torch.cuda.empty_cache()
+    log(f"[bench] gpt2 {rows['compress_gpt2_xl_bf16']}")
+    return rows
+
+
+if __name__ == "__main__":
+    main()

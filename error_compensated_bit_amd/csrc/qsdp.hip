@@ -1,0 +1,315 @@
+// qsdp.hip -- QSDP-style unbiased stochastic rounding of bf16 weights and its
+// inverse (QSDP review, "proposed method": each weight goes to one of its two
+// nearest quantization levels at random, with expectation equal to the weight).
+// Levels: 2^bits evenly spaced over each bucket's [min, max].  Random words:
+// Philox4x32-10 (Salmon et al., SC'11) keyed by the seed, counter = element
+// index / 4, word = element index % 4, so one Philox call serves four
+// consecutive elements.
+//
+// One wave64 per bucket: lane l handles element groups 4(l + 64k); the bucket's
+// min and max come from a wave-wide reduction on order-preserving integer keys
+// (so -0 < +0 and the result does not depend on reduction order).
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace onebit {
+
+// float -> int32 key whose signed order is the IEEE total order on non-NaN values
+__device__ __forceinline__ int32_t order_key(float f) {
+    const int32_t s = __float_as_int(f);
+    return s >= 0 ? s : (s ^ 0x7fffffff);
+}
+__device__ __forceinline__ float key_to_float(int32_t k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff)); }
+
+__device__ __forceinline__ int32_t wave_min_i(int32_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ int32_t wave_max_i(int32_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+struct QArgs {
+    const uint16_t *x;
+    int64_t n;
+    int64_t n_buckets;
+    int32_t bucket;
+    int32_t bits;
+    uint32_t k0, k1;  // Philox key (seed low / high word)
+    uint8_t *codes;
+    float *bmin, *bmax;
+    // dequantize
+    const uint8_t *in_codes;
+    const float *in_min, *in_max;
+    uint16_t *out_bf16;
+    float *out_f32;
+};
+
+// Stochastic rounding of one element given its uniform word.
+template <int BITS>
+__device__ __forceinline__ uint32_t sr_code(float x, float mn, float delta, uint32_t u) {
+    constexpr float L = (float)((1 << BITS) - 1);
+    if (delta == 0.0f) return 0u;
+    const float t = __fdiv_rn(sub_rn(x, mn), delta);
+    const float k = fminf(floorf(t), L);
+    const float p = sub_rn(t, k);                          // exact
+    // floor(p * 2^32), exact; p >= 1 only when k was clamped to L, where any
+    // threshold gives code L after the final clamp
+    const uint32_t thr = p < 1.0f ? (uint32_t)ldexpf(p, 32) : 0xffffffffu;
+    const uint32_t code = (uint32_t)k + (u < thr ? 1u : 0u);
+    return code > (uint32_t)L ? (uint32_t)L : code;
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_qsdp_quantize(QArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    constexpr float L = (float)((1 << BITS) - 1);
+    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+        const int64_t base = b * a.bucket;
+        const int32_t len = (int32_t)min((int64_t)a.bucket, a.n - base);
+        // pass over the bucket: min / max keys
+        int32_t kmin = 0x7fffffff, kmax = (int32_t)0x80000000;
+        for (int g4 = 4 * lane; g4 < len; g4 += 256) {
+            const int64_t i = base + g4;
+            if (g4 + 3 < len) {
+                const uint2 h = *reinterpret_cast<const uint2 *>(a.x + i);
+                const float f0 = bf16_bits_to_float(h.x & 0xffffu), f1 = bf16_bits_to_float(h.x >> 16);
+                const float f2 = bf16_bits_to_float(h.y & 0xffffu), f3 = bf16_bits_to_float(h.y >> 16);
+                kmin = min(kmin, min(min(order_key(f0), order_key(f1)), min(order_key(f2), order_key(f3))));
+                kmax = max(kmax, max(max(order_key(f0), order_key(f1)), max(order_key(f2), order_key(f3))));
+            } else {
+                for (int q = 0; q < 4 && g4 + q < len; ++q) {
+                    const int32_t k = order_key(bf16_bits_to_float(a.x[i + q]));
+                    kmin = min(kmin, k);
+                    kmax = max(kmax, k);
+                }
+            }
+        }
+        kmin = wave_min_i(kmin);
+        kmax = wave_max_i(kmax);
+        const float mn = key_to_float(kmin), mx = key_to_float(kmax);
+        const float delta = __fdiv_rn(sub_rn(mx, mn), L);
+        if (lane == 0) {
+            a.bmin[b] = mn;
+            a.bmax[b] = mx;
+        }
+        // second pass (the bucket is in L2 / L1): codes
+        for (int g4 = 4 * lane; g4 < len; g4 += 256) {
+            const int64_t i = base + g4;
+            float f[4];
+            if (g4 + 3 < len) {
+                const uint2 h = *reinterpret_cast<const uint2 *>(a.x + i);
+                f[0] = bf16_bits_to_float(h.x & 0xffffu);
+                f[1] = bf16_bits_to_float(h.x >> 16);
+                f[2] = bf16_bits_to_float(h.y & 0xffffu);
+                f[3] = bf16_bits_to_float(h.y >> 16);
+            } else {
+                for (int q = 0; q < 4; ++q) f[q] = (g4 + q < len) ? bf16_bits_to_float(a.x[i + q]) : mn;
+            }
+            const uint64_t blk = (uint64_t)i >> 2;
+            const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
+            uint32_t c0 = sr_code<BITS>(f[0], mn, delta, r.a);
+            uint32_t c1 = sr_code<BITS>(f[1], mn, delta, r.b);
+            uint32_t c2 = sr_code<BITS>(f[2], mn, delta, r.c);
+            uint32_t c3 = sr_code<BITS>(f[3], mn, delta, r.d);
+            if (g4 + 1 >= len) c1 = 0;
+            if (g4 + 2 >= len) c2 = 0;
+            if (g4 + 3 >= len) c3 = 0;
+            if (BITS == 4) {
+                if (g4 + 3 < len) {
+                    *reinterpret_cast<uint16_t *>(a.codes + (i >> 1)) =
+                        (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+                } else {
+                    a.codes[i >> 1] = (uint8_t)(c0 | (c1 << 4));
+                    if (g4 + 2 < len) a.codes[(i >> 1) + 1] = (uint8_t)(c2 | (c3 << 4));
+                }
+            } else {
+                if (g4 + 3 < len) {
+                    *reinterpret_cast<uint32_t *>(a.codes + i) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+                } else {
+                    a.codes[i] = (uint8_t)c0;
+                    if (g4 + 1 < len) a.codes[i + 1] = (uint8_t)c1;
+                    if (g4 + 2 < len) a.codes[i + 2] = (uint8_t)c2;
+                }
+            }
+        }
+    }
+}
+
+// Generic bucket size (not a multiple of 4): one Philox call per element.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_qsdp_quantize_generic(QArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    constexpr float L = (float)((1 << BITS) - 1);
+    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+        const int64_t base = b * a.bucket;
+        const int32_t len = (int32_t)min((int64_t)a.bucket, a.n - base);
+        int32_t kmin = 0x7fffffff, kmax = (int32_t)0x80000000;
+        for (int k = lane; k < len; k += 64) {
+            const int32_t key = order_key(bf16_bits_to_float(a.x[base + k]));
+            kmin = min(kmin, key);
+            kmax = max(kmax, key);
+        }
+        kmin = wave_min_i(kmin);
+        kmax = wave_max_i(kmax);
+        const float mn = key_to_float(kmin), mx = key_to_float(kmax);
+        const float delta = __fdiv_rn(sub_rn(mx, mn), L);
+        if (lane == 0) {
+            a.bmin[b] = mn;
+            a.bmax[b] = mx;
+        }
+        // 8-bit: one byte per element; 4-bit: bucket is even, each lane owns whole bytes
+        const int step = BITS == 4 ? 2 : 1;
+        for (int k = step * lane; k < len; k += 64 * step) {
+            uint32_t byte = 0;
+            for (int q = 0; q < step && k + q < len; ++q) {
+                const int64_t i = base + k + q;
+                const uint64_t blk = (uint64_t)i >> 2;
+                const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
+                const uint32_t w = (i & 3) == 0 ? r.a : (i & 3) == 1 ? r.b : (i & 3) == 2 ? r.c : r.d;
+                byte |= sr_code<BITS>(bf16_bits_to_float(a.x[i]), mn, delta, w) << (4 * q);
+            }
+            a.codes[BITS == 4 ? ((base + k) >> 1) : (base + k)] = (uint8_t)byte;
+        }
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_qsdp_dequantize(QArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    constexpr float L = (float)((1 << BITS) - 1);
+    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+        const int64_t base = b * a.bucket;
+        const int32_t len = (int32_t)min((int64_t)a.bucket, a.n - base);
+        const float mn = a.in_min[b];
+        const float delta = __fdiv_rn(sub_rn(a.in_max[b], mn), L);
+        const bool fast = (a.bucket & 3) == 0;
+        for (int g4 = 4 * lane; g4 < len; g4 += 256) {
+            const int64_t i = base + g4;
+            uint32_t c[4];
+            if (fast && g4 + 3 < len) {
+                if (BITS == 4) {
+                    const uint32_t w = *reinterpret_cast<const uint16_t *>(a.in_codes + (i >> 1));
+                    c[0] = w & 15u; c[1] = (w >> 4) & 15u; c[2] = (w >> 8) & 15u; c[3] = (w >> 12) & 15u;
+                } else {
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(a.in_codes + i);
+                    c[0] = w & 255u; c[1] = (w >> 8) & 255u; c[2] = (w >> 16) & 255u; c[3] = w >> 24;
+                }
+            } else {
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t j = i + q;
+                    c[q] = (g4 + q < len) ? (BITS == 4 ? (a.in_codes[j >> 1] >> ((j & 1) * 4)) & 15u : a.in_codes[j]) : 0u;
+                }
+            }
+            float y[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) y[q] = add_rn(mn, mul_rn((float)c[q], delta));
+            if (fast && g4 + 3 < len) {
+                if (a.out_f32) *reinterpret_cast<float4 *>(a.out_f32 + i) = make_float4(y[0], y[1], y[2], y[3]);
+                if (a.out_bf16) {
+                    uint2 pk;
+                    pk.x = float_to_bf16_bits(y[0]) | (float_to_bf16_bits(y[1]) << 16);
+                    pk.y = float_to_bf16_bits(y[2]) | (float_to_bf16_bits(y[3]) << 16);
+                    *reinterpret_cast<uint2 *>(a.out_bf16 + i) = pk;
+                }
+            } else {
+                for (int q = 0; q < 4 && g4 + q < len; ++q) {
+                    if (a.out_f32) a.out_f32[i + q] = y[q];
+                    if (a.out_bf16) a.out_bf16[i + q] = (uint16_t)float_to_bf16_bits(y[q]);
+                }
+            }
+        }
+    }
+}
+
+static unsigned grid_for(int64_t n_buckets) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    int64_t blocks = (n_buckets + 3) / 4;
+    const int64_t cap = (int64_t)cus * 32;
+    if (blocks > cap) blocks = cap;
+    return (unsigned)(blocks < 1 ? 1 : blocks);
+}
+
+}  // namespace onebit
+
+using namespace onebit;
+
+extern "C" onebit_status_t qsdp_quantize(const uint16_t *x_bf16, int64_t n, int bucket, int bits, uint64_t seed,
+                                         uint8_t *codes, float *bucket_min, float *bucket_max, void *stream) {
+    if (n < 0 || bucket < 1 || bucket > 65536 || (bits != 4 && bits != 8)) return ONEBIT_ERR_INVALID;
+    if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
+    if (n == 0) return ONEBIT_OK;
+    if (!x_bf16 || !codes || !bucket_min || !bucket_max) return ONEBIT_ERR_INVALID;
+    if (!aligned16(x_bf16) || !aligned_to(codes, 4) || !aligned_to(bucket_min, 4) || !aligned_to(bucket_max, 4))
+        return ONEBIT_ERR_ALIGN;
+    QArgs a{};
+    a.x = x_bf16;
+    a.n = n;
+    a.n_buckets = (n + bucket - 1) / bucket;
+    a.bucket = bucket;
+    a.bits = bits;
+    a.k0 = (uint32_t)seed;
+    a.k1 = (uint32_t)(seed >> 32);
+    a.codes = codes;
+    a.bmin = bucket_min;
+    a.bmax = bucket_max;
+    const unsigned grid = grid_for(a.n_buckets);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool fast = (bucket & 3) == 0;
+    prof_before(kProfQuantize, s);
+    if (bits == 4 && fast)
+        hipLaunchKernelGGL(k_qsdp_quantize<4>, dim3(grid), dim3(256), 0, s, a);
+    else if (bits == 4)
+        hipLaunchKernelGGL(k_qsdp_quantize_generic<4>, dim3(grid), dim3(256), 0, s, a);
+    else if (fast)
+        hipLaunchKernelGGL(k_qsdp_quantize<8>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_qsdp_quantize_generic<8>, dim3(grid), dim3(256), 0, s, a);
+    prof_after(s);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" onebit_status_t qsdp_dequantize(const uint8_t *codes, const float *bucket_min, const float *bucket_max,
+                                           int64_t n, int bucket, int bits, uint16_t *out_bf16, float *out_f32,
+                                           void *stream) {
+    if (n < 0 || bucket < 1 || bucket > 65536 || (bits != 4 && bits != 8)) return ONEBIT_ERR_INVALID;
+    if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
+    if (n == 0) return ONEBIT_OK;
+    if (!codes || !bucket_min || !bucket_max) return ONEBIT_ERR_INVALID;
+    if (!aligned_to(codes, 4) || !aligned_to(bucket_min, 4) || !aligned_to(bucket_max, 4)) return ONEBIT_ERR_ALIGN;
+    if ((out_bf16 && !aligned16(out_bf16)) || (out_f32 && !aligned16(out_f32))) return ONEBIT_ERR_ALIGN;
+    QArgs a{};
+    a.n = n;
+    a.n_buckets = (n + bucket - 1) / bucket;
+    a.bucket = bucket;
+    a.bits = bits;
+    a.in_codes = codes;
+    a.in_min = bucket_min;
+    a.in_max = bucket_max;
+    a.out_bf16 = out_bf16;
+    a.out_f32 = out_f32;
+    const unsigned grid = grid_for(a.n_buckets);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    prof_before(kProfDequantize, s);
+    if (bits == 4)
+        hipLaunchKernelGGL(k_qsdp_dequantize<4>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_qsdp_dequantize<8>, dim3(grid), dim3(256), 0, s, a);
+    prof_after(s);
+    return hip_status(hipGetLastError());
+}

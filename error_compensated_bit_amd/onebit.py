@@ -1,0 +1,228 @@
+"""Python binding of libonebit (include/onebit.h): same names, argument marshalling only.
+
+Device buffers are torch CUDA tensors (PyTorch supplies device memory and the
+stream); every computation runs in the library's HIP kernels.  A missing library
+raises immediately: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libonebit.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "onebit.h")
+
+ONEBIT_OK, ONEBIT_ERR_INVALID, ONEBIT_ERR_ALIGN, ONEBIT_ERR_HIP, ONEBIT_ERR_NOMEM, ONEBIT_ERR_UNSUPPORTED = range(6)
+ONEBIT_F32, ONEBIT_BF16 = 0, 1
+
+_P, _I64, _I, _D, _U64, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_double, C.c_uint64, C.c_size_t
+
+_SIGS = {
+    "onebit_status_string": (C.c_char_p, [_I]),
+    "onebit_plan_create": (_I, [_P, _I64, _P, _P, _I64, C.POINTER(_P)]),
+    "onebit_plan_destroy": (None, [_P]),
+    "onebit_plan_elements": (_I64, [_P]),
+    "onebit_plan_chunks": (_I64, [_P]),
+    "onebit_plan_words": (_I64, [_P]),
+    "onebit_plan_workspace_bytes": (_SZ, [_P]),
+    "onebit_workspace_init": (_I, [_P, _SZ, _P]),
+    "onebit_workspace_status": (_I, [_P, C.POINTER(_U64), _P]),
+    "onebit_device_coop_capacity": (C.c_int32, []),
+    "onebit_plan_stats": (None, [_P, _P]),
+    "onebit_profile_begin": (None, []),
+    "onebit_profile_end": (_I, [_P, _P]),
+    "onebit_adam_warmup_step": (_I, [_P, _P, _P, _P, _I, _I64, _D, _D, _D, _D, _D, _I, _I64, _P]),
+    "onebit_compress_update": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
+    "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "qsdp_quantize": (_I, [_P, _I64, _I, _I, _U64, _P, _P, _P, _P]),
+    "qsdp_dequantize": (_I, [_P, _P, _P, _I64, _I, _I, _P, _P, _P]),
+}
+
+_lib = None
+
+
+class OnebitError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {onebit_status_string(status)} (status {status})")
+
+
+def load():
+    """Load libonebit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950); there is no fallback implementation")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/onebit.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def _check(status, what):
+    if status != ONEBIT_OK:
+        raise OnebitError(status, what)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return ONEBIT_F32
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return ONEBIT_BF16
+    raise TypeError(f"gradient dtype {t.dtype} is not float32 or bfloat16")
+
+
+# ---------------------------------------------------------------- API
+
+def onebit_status_string(status: int) -> str:
+    return load().onebit_status_string(int(status)).decode()
+
+
+class Plan:
+    """Owning handle of an onebit_plan_t (destroyed with the object)."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.onebit_plan_destroy(self.handle)
+            self.handle = None
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+
+def onebit_plan_create(chunk_offsets, tensor_offsets=None, tensor_keep=None) -> Plan:
+    lib = load()
+    co = np.ascontiguousarray(chunk_offsets, dtype=np.int64)
+    to = None if tensor_offsets is None else np.ascontiguousarray(tensor_offsets, dtype=np.int64)
+    tk = None if tensor_keep is None else np.ascontiguousarray(tensor_keep, dtype=np.uint8)
+    out = _P()
+    n_tensors = 0 if to is None else to.size - 1
+    _check(lib.onebit_plan_create(co.ctypes.data, co.size - 1, None if to is None else to.ctypes.data,
+                                  None if tk is None else tk.ctypes.data, n_tensors, C.byref(out)),
+           "onebit_plan_create")
+    return Plan(out.value)
+
+
+def onebit_plan_destroy(plan: Plan):
+    if plan.handle:
+        load().onebit_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def onebit_plan_elements(plan) -> int:
+    return int(load().onebit_plan_elements(plan.handle))
+
+
+def onebit_plan_chunks(plan) -> int:
+    return int(load().onebit_plan_chunks(plan.handle))
+
+
+def onebit_plan_words(plan) -> int:
+    return int(load().onebit_plan_words(plan.handle))
+
+
+def onebit_plan_workspace_bytes(plan) -> int:
+    return int(load().onebit_plan_workspace_bytes(plan.handle))
+
+
+def onebit_plan_stats(plan) -> dict:
+    out = np.zeros(6, dtype=np.int64)
+    load().onebit_plan_stats(plan.handle, out.ctypes.data)
+    return dict(zip(("tiles", "onepass_tiles", "twopass_tiles", "coop_capacity", "max_chunk_tiles", "aligned"),
+                    out.tolist()))
+
+
+def onebit_device_coop_capacity() -> int:
+    return int(load().onebit_device_coop_capacity())
+
+
+PROFILE_CLASSES = ("warmup", "compress_pass1", "compress_onepass", "compress_pass2", "qsdp_quantize",
+                   "qsdp_dequantize", "server_pass1", "server_onepass", "server_pass2", "other")
+
+
+def onebit_profile_begin():
+    load().onebit_profile_begin()
+
+
+def onebit_profile_end() -> dict:
+    """{class: (total_ms, launches)} for the launches since onebit_profile_begin."""
+    ms = np.zeros(len(PROFILE_CLASSES), dtype=np.float64)
+    cnt = np.zeros(len(PROFILE_CLASSES), dtype=np.int64)
+    _check(load().onebit_profile_end(ms.ctypes.data, cnt.ctypes.data), "onebit_profile_end")
+    return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(PROFILE_CLASSES)}
+
+
+def onebit_workspace_init(workspace, stream=None):
+    _check(load().onebit_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "onebit_workspace_init")
+
+
+def onebit_workspace_status(workspace, stream=None) -> int:
+    out = _U64()
+    _check(load().onebit_workspace_status(_ptr(workspace), C.byref(out), _stream(stream)), "onebit_workspace_status")
+    return int(out.value)
+
+
+def onebit_adam_warmup_step(x, m, v, g, *, lr, beta1, beta2, eps, weight_decay, bias_correction, step,
+                            stream=None):
+    _check(load().onebit_adam_warmup_step(_ptr(x), _ptr(m), _ptr(v), _ptr(g), _dtype_code(g), x.numel(), lr, beta1,
+                                          beta2, eps, weight_decay, int(bias_correction), int(step),
+                                          _stream(stream)), "onebit_adam_warmup_step")
+
+
+def onebit_compress_update(plan, g, m, e, v, x, x_bf16, bits, scales, *, lr, beta1, eps, weight_decay,
+                           workspace, stream=None):
+    _check(load().onebit_compress_update(plan.handle, _ptr(g), _dtype_code(g), _ptr(m), _ptr(e), _ptr(v), _ptr(x),
+                                         _ptr(x_bf16), _ptr(bits), _ptr(scales), lr, beta1, eps, weight_decay,
+                                         _ptr(workspace), _stream(stream)), "onebit_compress_update")
+
+
+def onebit_server_reduce(plan, worker_bits, worker_scales, server_error, server_bits, server_scales, m_out,
+                         workspace, stream=None):
+    W = int(worker_scales.shape[0])
+    _check(load().onebit_server_reduce(plan.handle, W, _ptr(worker_bits), _ptr(worker_scales), _ptr(server_error),
+                                       _ptr(server_bits), _ptr(server_scales), _ptr(m_out), _ptr(workspace),
+                                       _stream(stream)), "onebit_server_reduce")
+
+
+def qsdp_quantize(x_bf16, bucket, bits, seed, codes, bucket_min, bucket_max, stream=None):
+    _check(load().qsdp_quantize(_ptr(x_bf16), x_bf16.numel(), int(bucket), int(bits), int(seed) & (2 ** 64 - 1),
+                                _ptr(codes), _ptr(bucket_min), _ptr(bucket_max), _stream(stream)), "qsdp_quantize")
+
+
+def qsdp_dequantize(codes, bucket_min, bucket_max, n, bucket, bits, out_bf16=None, out_f32=None, stream=None):
+    _check(load().qsdp_dequantize(_ptr(codes), _ptr(bucket_min), _ptr(bucket_max), int(n), int(bucket), int(bits),
+                                  _ptr(out_bf16), _ptr(out_f32), _stream(stream)), "qsdp_dequantize")

@@ -1,0 +1,187 @@
+/*
+ * onebit.h -- C ABI of the MI355X (gfx950) library for the data-parallel hot path
+ * of 1-bit Adam and for a QSDP-style stochastic-rounding quantizer.
+ *
+ * Sources ("the pages"):
+ *  [1BA]  nubint.ai review of "1-bit Adam: Communication Efficient Large-Scale
+ *         Training with Adam's Convergence Speed", "proposed method": full-precision
+ *         Adam warmup, then the frozen variance preconditions error-compensated
+ *         1-bit compressed momentum SGD.
+ *  [DSG]  yfxerp.com "DeepSpeed 1-bit Adam training optimisation ... complete
+ *         configuration guide": sec. 3.4 (lr, betas, eps, weight_decay,
+ *         bias_correction), sec. 3.5 (exp_avg_mask), sec. 4 (the two phases of
+ *         step(), compressed_allreduce with worker_error / server_error,
+ *         update = exp_avg / (sqrt(exp_avg_sq) + eps), 1 bit per value),
+ *         sec. 7 (errors reset on checkpoint load).
+ *  [QSDP] nubint.ai review of "Quantized Distributed Training of Large Models with
+ *         Convergence Guarantees", "proposed method": weights rounded at random to
+ *         one of the two nearest quantization levels, unbiased.
+ *  [PHX]  Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11.
+ *
+ * Conventions for every call:
+ *  - Every data pointer is a DEVICE pointer owned by the caller unless marked
+ *    (host).  Per-element arrays (x, m, v, e, g, x_bf16, server_error, m_out and
+ *    the QSDP weights and outputs) must be 16-byte aligned; packed words, scales,
+ *    codes and bucket min/max 4-byte aligned; the workspace 8-byte aligned
+ *    (ONEBIT_ERR_ALIGN otherwise).  Chunk offsets inside the arrays may be
+ *    arbitrary.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *    The returned status covers argument checks and launch errors; a fault during
+ *    execution surfaces at the caller's next synchronisation.  Nothing here
+ *    allocates device memory or synchronises, except onebit_plan_create /
+ *    onebit_plan_destroy (which own the plan's tables).
+ *  - Buffers passed to one call must not alias each other unless stated.
+ *  - Non-finite inputs are not checked and propagate.
+ *  - Hyperparameters are binary64 (as Python floats are); each is rounded to
+ *    binary32 once, and 1-beta is formed in binary64 before that rounding.
+ *  - Phase control is the caller's: warmup calls for steps t <= freeze_step, then
+ *    compressed calls ([DSG] sec. 3.1, sec. 4).  The error reset that [DSG] sec. 7
+ *    prescribes after a checkpoint load is the caller zeroing e and server_error.
+ */
+#ifndef ONEBIT_H
+#define ONEBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ONEBIT_OK = 0,
+    ONEBIT_ERR_INVALID = 1,     /* bad size, table, pointer or parameter */
+    ONEBIT_ERR_ALIGN = 2,       /* a base pointer misses its required alignment */
+    ONEBIT_ERR_HIP = 3,         /* a HIP runtime call or launch failed */
+    ONEBIT_ERR_NOMEM = 4,       /* plan tables could not be allocated */
+    ONEBIT_ERR_UNSUPPORTED = 5  /* valid request this build does not serve */
+} onebit_status_t;
+
+typedef enum { ONEBIT_F32 = 0, ONEBIT_BF16 = 1 } onebit_dtype_t;
+
+/* Opaque plan: device copies of the chunk, tile and mask tables for one flat
+ * parameter vector.  Library-owned, immutable after creation, usable from any
+ * stream of the device that was current at creation. */
+typedef struct onebit_plan_s *onebit_plan_t;
+
+/* Human-readable name of a status code (static storage). */
+const char *onebit_status_string(onebit_status_t status);
+
+/* Build a plan for a flat vector of n = chunk_offsets[n_chunks] elements.
+ *  chunk_offsets  (host) n_chunks+1 entries, [0] = 0, non-decreasing.  One fp32
+ *                 scale per chunk; chunk j owns ceil(n_j/32) consecutive packed
+ *                 words starting at sum_{k<j} ceil(n_k/32).
+ *  tensor_offsets (host, nullable) n_tensors+1 entries, [0] = 0, non-decreasing,
+ *                 last = n.  tensor_keep (host, nullable) n_tensors flags:
+ *                 0 = masked (the momentum mask of [DSG] sec. 3.5, per tensor).
+ *  n_chunks >= 0; n_chunks = 0 gives an empty plan whose calls do nothing.
+ * Allocates device memory (the only allocating call besides the workspace the
+ * caller provides). */
+onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int64_t n_chunks,
+                                   const int64_t *tensor_offsets, const uint8_t *tensor_keep,
+                                   int64_t n_tensors, onebit_plan_t *out);
+void onebit_plan_destroy(onebit_plan_t plan);
+int64_t onebit_plan_elements(onebit_plan_t plan); /* n */
+int64_t onebit_plan_chunks(onebit_plan_t plan);   /* n_chunks */
+int64_t onebit_plan_words(onebit_plan_t plan);    /* sum_j ceil(n_j / 32) */
+
+/* Device scratch (bytes) that onebit_compress_update / onebit_server_reduce need
+ * for this plan: per-tile partial norms and per-chunk arrival counters.  The
+ * caller allocates it and must zero it once before first use (onebit_workspace_init
+ * does that on a stream); every completed call leaves it ready for the next one,
+ * for this or any other plan whose workspace size fits.  One workspace must not be
+ * used by two calls that may overlap in time. */
+size_t onebit_plan_workspace_bytes(onebit_plan_t plan);
+onebit_status_t onebit_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/* Copy the workspace's error word to *out (host) and synchronise `stream`.
+ * 0: every cross-workgroup wait of the calls since the workspace was zeroed
+ * ended normally; non-zero: a bounded wait gave up (the outputs of that call are
+ * not valid).  Intended for tests and diagnostics. */
+onebit_status_t onebit_workspace_status(const void *workspace, uint64_t *out, void *stream);
+
+/* Diagnostics: co-resident workgroups of the one-pass compression kernel on the
+ * current device (0 when cooperative launch is unavailable), and a plan's tile
+ * split: out6 (host) = {tiles, one-pass tiles, two-pass tiles, capacity used,
+ * largest chunk in tiles, 1 if every chunk starts on a multiple of 4 elements}. */
+int32_t onebit_device_coop_capacity(void);
+void onebit_plan_stats(onebit_plan_t plan, int64_t *out6);
+
+/* Launch timing.  Between onebit_profile_begin and onebit_profile_end every kernel
+ * the library launches is bracketed by two HIP events on its own stream.
+ * onebit_profile_end synchronises on those events and returns, per kernel class,
+ * the summed elapsed milliseconds and the launch count (host arrays of
+ * ONEBIT_PROFILE_CLASSES entries, nullable).  Classes: 0 warmup, 1/2/3 worker
+ * compression pass 1 / one-pass / pass 2, 4 quantize, 5 dequantize, 6/7/8 server
+ * pass 1 / one-pass / pass 2, 9 other.  Not thread-safe; diagnostics only. */
+#define ONEBIT_PROFILE_CLASSES 10
+void onebit_profile_begin(void);
+onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
+
+/* Warmup step t (1-based) of full-precision Adam over n elements ([DSG] sec. 4,
+ * phase one; [1BA]):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   x -= lr * ( mhat / (sqrt(vhat) + eps) + weight_decay * x ),
+ * with mhat = m / (1-b1^t), vhat = v / (1-b2^t) when bias_correction != 0, else
+ * mhat = m, vhat = v.  x, m, v: fp32 [n] in place.  g: [n] fp32 or bf16. */
+onebit_status_t onebit_adam_warmup_step(float *x, float *m, float *v, const void *g,
+                                        onebit_dtype_t g_dtype, int64_t n, double lr,
+                                        double beta1, double beta2, double eps,
+                                        double weight_decay, int bias_correction, int64_t step,
+                                        void *stream);
+
+/* One compressed step on one worker's share ([DSG] sec. 4, phase two; sec. 3.5):
+ *   m1 = b1 m + (1-b1) g;  c = m1 + e                       (binary32, unfused)
+ *   scale_j = sqrt(sum_{i in j} c_i^2) / sqrt(n_j)          (fp64 sum, one rounding)
+ *   bit_i = (c_i < 0);  q_i = bit_i ? -scale_j : +scale_j;  e = c - q;  m = q
+ *   masked tensors: m = 0, e = 0 (bits and scale still from c)
+ *   x -= lr * ( m / (sqrt(v) + eps) + weight_decay * x );  x_bf16 = bf16(x)
+ * g: [n] fp32 or bf16.  m, e, x: fp32 [n] in place; v: fp32 [n] read-only (frozen).
+ * bits: uint32 [plan_words] out, least significant bit first, every chunk starting
+ * on a word boundary, pad bits 0.  scales: fp32 [n_chunks] out.  x_bf16: uint16
+ * [n] out, nullable.  Compress-only (the worker half of the compressed
+ * all-reduce): pass v = x = x_bf16 = NULL; then m is read and NOT written and only
+ * e, bits and scales are produced.  workspace: onebit_plan_workspace_bytes bytes. */
+onebit_status_t onebit_compress_update(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
+                                       float *m, float *e, const float *v, float *x,
+                                       uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
+                                       double beta1, double eps, double weight_decay,
+                                       void *workspace, void *stream);
+
+/* Server stage of the compressed all-reduce over W workers' streams held in one
+ * GPU's memory ([DSG] sec. 4, server_error; [1BA] "proposed method"):
+ *   a_i = fl32( (sum_{w=0..W-1} (bit_{w,i} ? -s_{w,j} : +s_{w,j})) / W )   (fp64)
+ *   c = a + server_error;  then the compressor above with server_error as e;
+ *   m_out = decompressed server result (nullable; may alias nothing else).
+ * worker_bits: uint32 [W][plan_words] row-major; worker_scales: fp32 [W][n_chunks].
+ * server_error: fp32 [n] in place; server_bits [plan_words], server_scales
+ * [n_chunks] out.  1 <= W <= 1024. */
+onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *worker_bits,
+                                     const float *worker_scales, float *server_error,
+                                     uint32_t *server_bits, float *server_scales, float *m_out,
+                                     void *workspace, void *stream);
+
+/* QSDP-style unbiased stochastic rounding of bf16 weights ([QSDP] "proposed
+ * method"), per bucket of `bucket` elements (the last one may be short):
+ *   min, max of the bucket (exact);  delta = fl32(fl32(max - min) / L), L = 2^bits - 1
+ *   t = fl32(fl32(x - min) / delta);  k = min(floor(t), L);  p = t - k
+ *   u = Philox4x32-10(key = seed, counter = (i >> 2, 0, 0))[i & 3]   ([PHX])
+ *   code = min(k + (u < floor(p * 2^32)), L);  code = 0 when delta == 0.
+ * bits 4: codes packed two per byte, even element in the low nibble, pad nibble 0,
+ * ceil(n/2) bytes.  bits 8: one byte per element.  bucket_min/max: fp32
+ * [ceil(n/bucket)] out.  1 <= bucket <= 65536, bucket even when bits == 4. */
+onebit_status_t qsdp_quantize(const uint16_t *x_bf16, int64_t n, int bucket, int bits,
+                              uint64_t seed, uint8_t *codes, float *bucket_min, float *bucket_max,
+                              void *stream);
+
+/* Inverse map: y = fl32(min + fl32(code * delta)) with delta as above.
+ * out_bf16: uint16 [n] (round to nearest even), nullable; out_f32: fp32 [n],
+ * nullable. */
+onebit_status_t qsdp_dequantize(const uint8_t *codes, const float *bucket_min,
+                                const float *bucket_max, int64_t n, int bucket, int bits,
+                                uint16_t *out_bf16, float *out_f32, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONEBIT_H */

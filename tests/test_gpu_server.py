@@ -1,0 +1,70 @@
+"""GPU parity of the simulated compressed all-reduce: W workers' compress-only
+steps (each with its own error buffer, a shared momentum) followed by the server
+stage, against the oracle, over 3 steps in which the server's decompressed
+result becomes the shared momentum."""
+import numpy as np
+import pytest
+import torch
+
+from error_compensated_bit_amd import onebit as ob
+from error_compensated_bit_amd import workloads as W
+from gpu_helpers import DEV, CompressBuffers, host, oracle_compress
+import oracle
+from parity import assert_bits_exact, assert_exact, check_err, check_scales, per_element, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_allreduce(chunk_off, Wn, steps, seed):
+    buf = CompressBuffers(chunk_off)
+    n, words, nch = buf.n, buf.words, buf.n_chunks
+    rng = np.random.default_rng(seed)
+    m = np.zeros(n, np.float32)
+    e = [(rng.standard_normal(n) * 1e-5).astype(np.float32) for _ in range(Wn)]
+    es = (rng.standard_normal(n) * 1e-5).astype(np.float32)
+    md = torch.from_numpy(m.copy()).to(DEV)
+    ed = [torch.from_numpy(a.copy()).to(DEV) for a in e]
+    esd = torch.from_numpy(es.copy()).to(DEV)
+    wbits = torch.zeros((Wn, max(words, 1)), dtype=torch.int32, device=DEV)
+    wscales = torch.zeros((Wn, max(nch, 1)), dtype=torch.float32, device=DEV)
+    sbits = torch.zeros(max(words, 1), dtype=torch.int32, device=DEV)
+    sscales = torch.zeros(max(nch, 1), dtype=torch.float32, device=DEV)
+    for s in range(steps):
+        say(f"  W={Wn} step {s}")
+        ref_b, ref_s = [], []
+        for w in range(Wn):
+            g = (np.random.default_rng(seed * 1000 + 100 * w + s).standard_normal(n) * 1e-3).astype(np.float32)
+            buf.bits = wbits[w]
+            buf.scales = wscales[w]
+            buf.step(torch.from_numpy(g).to(DEV), md, ed[w])
+            rb, rs, _ = oracle_compress(chunk_off, g, m, e[w])
+            ref_b.append(rb)
+            ref_s.append(rs)
+        torch.cuda.synchronize()
+        for w in range(Wn):
+            assert_bits_exact(f"worker {w} bits", host(wbits[w])[:words].view(np.uint32), ref_b[w])
+            assert check_scales(f"worker {w} scales", host(wscales[w])[:nch], ref_s[w]) == 0
+            assert_exact(f"worker {w} e", host(ed[w]), e[w])
+        ob.onebit_server_reduce(buf.plan, wbits, wscales, esd, sbits, sscales, md, buf.ws)
+        rb, rs, m_out = oracle.server_reduce(chunk_off, np.stack(ref_b), np.stack(ref_s), es)
+        torch.cuda.synchronize()
+        assert_bits_exact("server bits", host(sbits)[:words].view(np.uint32), rb)
+        ne = check_scales("server scales", host(sscales)[:nch], rs)
+        check_err("server e", host(esd), es, per_element(rs, chunk_off))
+        if ne == 0:
+            assert_exact("server e", host(esd), es)
+            assert_exact("server m", host(md), m_out)
+        m = m_out
+        assert ob.onebit_workspace_status(buf.ws) == 0
+
+
+@pytest.mark.parametrize("Wn", [1, 2, 3, 16])
+def test_server_ragged_chunks(Wn):
+    off = W.offsets_from_sizes([33, 64, 1, 4097, 70000, 31, 8192])
+    run_allreduce(off, Wn, 3, seed=40 + Wn)
+
+
+def test_server_two_pass_chunk():
+    cap = ob.onebit_device_coop_capacity()
+    off = W.offsets_from_sizes([max(cap, 1) * 4096 + 4097, 5000])
+    run_allreduce(off, 2, 2, seed=77)
