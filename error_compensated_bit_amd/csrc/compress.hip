@@ -8,13 +8,13 @@
 // q = +-scale, e = c - q, m = q (0 for masked tensors, with e = 0), and the
 // preconditioned step x -= lr (m / (sqrt(v) + eps) + wd x) with v frozen.
 //
-// How: the flat vector is cut into tiles of 4096 elements (256 threads x 16).
-// A tile computes its c into registers, writes its sign words, and posts its
-// fp64 partial sum of squares.  The chunk scale needs every tile of the chunk, so
-//  - chunks of at most R tiles (R = co-resident workgroups) are done in ONE pass
-//    by a cooperative persistent kernel: each tile keeps c in registers, waits for
-//    its chunk's scale, then finishes -- HBM sees each input once and each output
-//    once;
+// How: the flat vector is cut into tiles of 2048 elements (256 threads x 8).
+// A tile computes its c, writes its sign words, and posts its fp64 partial sum
+// of squares.  The chunk scale needs every tile of the chunk, so
+//  - chunks of at most 2R tiles (R = co-resident workgroups) are done in ONE pass
+//    by a cooperative persistent kernel: each tile parks c in LDS, waits for its
+//    chunk's scale while the next tile streams, then finishes -- HBM sees each
+//    input once and each output once;
 //  - larger chunks take two passes: pass 1 stores c in place of e, pass 2 reads it
 //    back with v and x once the chunk scale is known.
 // Cross-workgroup communication uses only single-location relaxed agent-scope
@@ -58,7 +58,7 @@ struct CompressArgs {
     float b1, ob1, lr, eps, wd;
     // workspace
     uint64_t *err;
-    uint64_t *chunk_words;
+    uint64_t *publish;
     uint64_t *slots;
     uint32_t spin_limit;
 };
@@ -73,74 +73,98 @@ __device__ __forceinline__ bool give_up(const CompressArgs &a, uint32_t spins) {
 }
 
 // ---------------------------------------------------------------- tile: c
+// Thread t of a tile owns elements 4(t + 256 r) .. +3, r < kGroups: every load
+// instruction of a workgroup covers 4 KiB of consecutive fp32.  Addresses are a
+// uniform per-tile base plus a 32-bit lane offset.  A tile is "full" when it
+// holds kTile elements and starts on a multiple of 4 (the common case); other
+// tiles take per-element guarded accesses.
+__device__ __forceinline__ bool tile_full(const CompressArgs &a, const TileDesc &t) {
+    return a.aligned && t.len == kTile;
+}
+__device__ __forceinline__ uint32_t lane_k0(int r) { return 4u * (threadIdx.x + kBlock * r); }
+
+template <bool GBF16>
+__device__ __forceinline__ void load_g4(const void *g, int64_t start, uint32_t k0, float (&g4)[4]) {
+    if (GBF16) {
+        const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + start + k0);
+        g4[0] = bf16_bits_to_float(h.x & 0xffffu);
+        g4[1] = bf16_bits_to_float(h.x >> 16);
+        g4[2] = bf16_bits_to_float(h.y & 0xffffu);
+        g4[3] = bf16_bits_to_float(h.y >> 16);
+    } else {
+        const float4 h = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + start + k0);
+        g4[0] = h.x; g4[1] = h.y; g4[2] = h.z; g4[3] = h.w;
+    }
+}
+
+__device__ __forceinline__ void load4(const float *base, uint32_t k0, float (&v)[4]) {
+    const float4 h = *reinterpret_cast<const float4 *>(base + k0);
+    v[0] = h.x; v[1] = h.y; v[2] = h.z; v[3] = h.w;
+}
+
 template <int MODE, bool GBF16>
 __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const TileDesc &t,
-                                               float (&c)[kPerThread], const double *s_wscale) {
-    const int tid = threadIdx.x;
+                                               float (&c)[kPerThread], const float *s_wscale) {
+    const bool full = tile_full(a, t);
+    if (MODE != kServer) {
+        const float *mb = a.m + t.start;
+        const float *eb = a.e + t.start;
 #pragma unroll
-    for (int r = 0; r < kGroups; ++r) {
-        const int k0 = 4 * (tid + kBlock * r);
-        const int64_t i0 = t.start + k0;
-        if (MODE != kServer) {
+        for (int r = 0; r < kGroups; ++r) {
+            const uint32_t k0 = lane_k0(r);
             float g4[4], m4[4], e4[4];
-            if (a.aligned && k0 + 3 < t.len) {
-                if (GBF16) {
-                    const uint2 gg = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.g) + i0);
-                    g4[0] = bf16_bits_to_float(gg.x & 0xffffu);
-                    g4[1] = bf16_bits_to_float(gg.x >> 16);
-                    g4[2] = bf16_bits_to_float(gg.y & 0xffffu);
-                    g4[3] = bf16_bits_to_float(gg.y >> 16);
-                } else {
-                    const float4 gg = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + i0);
-                    g4[0] = gg.x; g4[1] = gg.y; g4[2] = gg.z; g4[3] = gg.w;
-                }
-                const float4 mm = *reinterpret_cast<const float4 *>(a.m + i0);
-                const float4 ee = *reinterpret_cast<const float4 *>(a.e + i0);
-                m4[0] = mm.x; m4[1] = mm.y; m4[2] = mm.z; m4[3] = mm.w;
-                e4[0] = ee.x; e4[1] = ee.y; e4[2] = ee.z; e4[3] = ee.w;
+            if (full) {
+                load_g4<GBF16>(a.g, t.start, k0, g4);
+                load4(mb, k0, m4);
+                load4(eb, k0, e4);
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const bool in = k0 + q < t.len;
-                    const int64_t i = i0 + q;
-                    g4[q] = in ? (GBF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.g)[i])
-                                        : static_cast<const float *>(a.g)[i])
+                    const uint32_t k = k0 + q;
+                    const bool in = k < (uint32_t)t.len;
+                    g4[q] = in ? (GBF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.g)[t.start + k])
+                                        : static_cast<const float *>(a.g)[t.start + k])
                                : 0.0f;
-                    m4[q] = in ? a.m[i] : 0.0f;
-                    e4[q] = in ? a.e[i] : 0.0f;
+                    m4[q] = in ? mb[k] : 0.0f;
+                    e4[q] = in ? eb[k] : 0.0f;
                 }
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float m1 = add_rn(mul_rn(a.b1, m4[q]), mul_rn(a.ob1, g4[q]));
-                c[4 * r + q] = (k0 + q < t.len) ? add_rn(m1, e4[q]) : 0.0f;
+                const float cq = add_rn(m1, e4[q]);
+                c[4 * r + q] = (full || k0 + q < (uint32_t)t.len) ? cq : 0.0f;
             }
-        } else {
-            // server: average of the W workers' decompressed values, fp64 in worker order
-            double acc[4] = {0.0, 0.0, 0.0, 0.0};
-            if (k0 < t.len) {
-                const int64_t word = t.word + (k0 >> 5);
-                const int sh = k0 & 31;
-                for (int w = 0; w < a.W; ++w) {
-                    const uint32_t bw = a.wbits[(int64_t)w * a.plan_words + word] >> sh;
-                    const double s = s_wscale[w];
+        }
+    } else {
+        // server: average of the W workers' decompressed values, fp64 in worker order
+        const float *eb = a.e + t.start;
+        const double dW = (double)a.W;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = __dadd_rn(acc[q], ((bw >> q) & 1u) ? -s : s);
+        for (int r = 0; r < kGroups; ++r) {
+            const uint32_t k0 = lane_k0(r);
+            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            if (full || k0 < (uint32_t)t.len) {
+                const uint32_t *wb = a.wbits + t.word + (k0 >> 5);
+                const uint32_t sh = k0 & 31u;
+                for (int w = 0; w < a.W; ++w) {
+                    const uint32_t bw = wb[(int64_t)w * a.plan_words] >> sh;
+                    const double sw = (double)s_wscale[w];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = __dadd_rn(acc[q], ((bw >> q) & 1u) ? -sw : sw);
                 }
             }
             float es[4];
-            if (a.aligned && k0 + 3 < t.len) {
-                const float4 ee = *reinterpret_cast<const float4 *>(a.e + i0);
-                es[0] = ee.x; es[1] = ee.y; es[2] = ee.z; es[3] = ee.w;
+            if (full) {
+                load4(eb, k0, es);
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) es[q] = (k0 + q < t.len) ? a.e[i0 + q] : 0.0f;
+                for (int q = 0; q < 4; ++q) es[q] = (k0 + q < (uint32_t)t.len) ? eb[k0 + q] : 0.0f;
             }
-            const double dW = (double)a.W;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float avg = (float)__ddiv_rn(acc[q], dW);
-                c[4 * r + q] = (k0 + q < t.len) ? add_rn(avg, es[q]) : 0.0f;
+                c[4 * r + q] = (full || k0 + q < (uint32_t)t.len) ? add_rn(avg, es[q]) : 0.0f;
             }
         }
     }
@@ -149,14 +173,14 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
 // ------------------------------------------------------- tile: sign words
 __device__ __forceinline__ void tile_store_bits(const CompressArgs &a, const TileDesc &t,
                                                 const float (&c)[kPerThread]) {
-    const int tid = threadIdx.x;
+    uint32_t *wb = a.bits + t.word;
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
-        const int k0 = 4 * (tid + kBlock * r);
-        uint32_t nib = (c[4 * r + 0] < 0.0f ? 1u : 0u) | (c[4 * r + 1] < 0.0f ? 2u : 0u) |
-                       (c[4 * r + 2] < 0.0f ? 4u : 0u) | (c[4 * r + 3] < 0.0f ? 8u : 0u);
-        const uint32_t word = or_over_8_lanes(nib << (k0 & 31));
-        if ((tid & 7) == 0 && k0 < t.len) a.bits[t.word + (k0 >> 5)] = word;
+        const uint32_t k0 = lane_k0(r);
+        const uint32_t nib = (c[4 * r + 0] < 0.0f ? 1u : 0u) | (c[4 * r + 1] < 0.0f ? 2u : 0u) |
+                             (c[4 * r + 2] < 0.0f ? 4u : 0u) | (c[4 * r + 3] < 0.0f ? 8u : 0u);
+        const uint32_t word = or_over_8_lanes(nib << (k0 & 31u));
+        if ((threadIdx.x & 7) == 0 && k0 < (uint32_t)t.len) wb[k0 >> 5] = word;
     }
 }
 
@@ -187,82 +211,117 @@ __device__ __forceinline__ double tile_sum_squares(const float (&c)[kPerThread],
 
 __device__ __forceinline__ void spin_pause() { __builtin_amdgcn_s_sleep(2); }
 
-// The last tile of a chunk to arrive sums the chunk's partials (in tile order, so
-// the result does not depend on arrival order), publishes the scale, and leaves
-// the chunk's words and slots ready for the next call.
-__device__ float finalize_chunk(const CompressArgs &a, int chunk, uint32_t epoch, DD *s_red) {
-    const ChunkDesc ch = a.chunks[chunk];
+// Sum of a chunk's posted partials, read from its tile slots.  Each thread takes
+// a fixed subset in a fixed order and the waves combine in a fixed tree, so the
+// result does not depend on which tile finished last.  All loads of a batch are
+// in flight before any is checked; a slot that is not yet visible is re-polled.
+// Slots are cleared after reading (zero = empty for the next call).
+__device__ double chunk_sum(const CompressArgs &a, const ChunkDesc &ch, DD *s_red, double *s_total) {
     DD acc = {0.0, 0.0};
-    for (int k = threadIdx.x; k < ch.ntiles; k += kBlock) {
-        uint64_t *slot = a.slots + ch.first_tile + k;
-        uint64_t w = ld_agent(slot);
-        uint32_t spins = 0;
-        while (!(w & kTag) && !give_up(a, spins)) {
-            spin_pause();
-            w = ld_agent(slot);
-            ++spins;
+    constexpr int kBatch = 8;
+    for (int base = 0; base < ch.ntiles; base += kBlock * kBatch) {
+        uint64_t w[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int k = base + u * kBlock + (int)threadIdx.x;
+            w[u] = k < ch.ntiles ? ld_agent(a.slots + ch.first_tile + k) : kTag;
         }
-        if (!(w & kTag)) st_agent(a.err, 1);
-        dd_add_term(acc, untag_partial(w));
-        st_agent(slot, 0);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int k = base + u * kBlock + (int)threadIdx.x;
+            if (k < ch.ntiles) {
+                uint64_t *slot = a.slots + ch.first_tile + k;
+                uint32_t spins = 0;
+                while (!(w[u] & kTag) && !give_up(a, spins)) {
+                    spin_pause();
+                    w[u] = ld_agent(slot);
+                    ++spins;
+                }
+                if (!(w[u] & kTag)) st_agent(a.err, 1);
+                dd_add_term(acc, untag_partial(w[u]));
+                st_agent(slot, 0);
+            }
+        }
     }
     acc = wave_sum_dd(acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) s_red[wave] = acc;
     __syncthreads();
-    float scale = 0.0f;
     if (threadIdx.x == 0) {
         DD t = s_red[0];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) t = dd_add(t, s_red[w]);
-        const double S = __dadd_rn(t.hi, t.lo);
-        scale = ch.len > 0 ? (float)__ddiv_rn(__dsqrt_rn(S), __dsqrt_rn((double)ch.len)) : 0.0f;
-        a.scales[chunk] = scale;
-        const uint64_t next = (uint64_t)(uint32_t)(epoch + 1u) << 32;
-        st_agent(a.chunk_words + 2 * chunk + 1, next | (uint64_t)__float_as_uint(scale));
-        st_agent(a.chunk_words + 2 * chunk + 0, next);
+        *s_total = __dadd_rn(t.hi, t.lo);
     }
     __syncthreads();
-    return scale;  // meaningful in thread 0 only
+    const double total = *s_total;
+    __syncthreads();
+    return total;
 }
 
-// Post this tile's partial and arrive.  WAIT: block until the chunk scale is
-// published (one-pass path); otherwise return after arriving (pass 1 of two).
-template <bool WAIT>
-__device__ float arrive(const CompressArgs &a, int tile_id, int chunk, double partial, DD *s_red,
-                        float *s_scale, uint32_t *s_flag) {
+__device__ __forceinline__ float scale_of(double S, int64_t len) {
+    return len > 0 ? (float)__ddiv_rn(__dsqrt_rn(S), __dsqrt_rn((double)len)) : 0.0f;
+}
+
+// What a workgroup knows about a tile it has posted.
+struct Posted {
+    uint32_t epoch;  // publish epoch of the chunk read before posting
+    uint32_t mine;   // this workgroup finalized the chunk (it holds its last tile)
+    float scale;     // valid when mine
+};
+
+// Post a tile's partial: read the chunk's publish epoch (and wait for that read to
+// complete, so it precedes the post), then store the tagged partial in the tile's
+// own slot -- no read-modify-write, so tiles never contend for one word.  The
+// workgroup holding the chunk's last tile then sums all slots and publishes
+// {epoch + 1, scale}.  With at most coop_depth() tiles of a chunk per workgroup,
+// all earlier tiles of the chunk are posted by workgroups that do not wait on it.
+template <bool FINALIZE>
+__device__ Posted post_tile(const CompressArgs &a, int tile_id, int chunk, double partial, DD *s_red,
+                            uint32_t *s_u32, double *s_total) {
     if (threadIdx.x == 0) {
+        const uint64_t pw = ld_agent(a.publish + chunk);
+        s_u32[0] = (uint32_t)(pw >> 32);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         st_agent(a.slots + tile_id, tag_partial(partial));
-        const uint64_t old = add_agent(a.chunk_words + 2 * chunk, 1);
-        const uint32_t epoch = (uint32_t)(old >> 32);
-        const uint32_t count = (uint32_t)old;
-        s_flag[0] = (count + 1u == (uint32_t)a.chunks[chunk].ntiles) ? 1u : 0u;
-        s_flag[1] = epoch;
     }
     __syncthreads();
-    const bool last = s_flag[0] != 0;
-    const uint32_t epoch = s_flag[1];
-    float scale = 0.0f;
-    if (last) {
-        scale = finalize_chunk(a, chunk, epoch, s_red);
-        if (threadIdx.x == 0) *s_scale = scale;
-    } else if (WAIT) {
-        if (threadIdx.x == 0) {
-            const uint64_t *pub = a.chunk_words + 2 * chunk + 1;
-            const uint32_t want = epoch + 1u;
-            uint64_t w = ld_agent(pub);
-            uint32_t spins = ld_agent(a.err) != 0 ? a.spin_limit : 0u;
-            while ((uint32_t)(w >> 32) != want && !give_up(a, spins)) {
-                spin_pause();
-                w = ld_agent(pub);
-                ++spins;
+    Posted r{s_u32[0], 0u, 0.0f};
+    __syncthreads();
+    if (FINALIZE) {
+        const ChunkDesc ch = a.chunks[chunk];
+        if (tile_id == ch.first_tile + ch.ntiles - 1) {
+            r.mine = 1u;
+            r.scale = scale_of(chunk_sum(a, ch, s_red, s_total), ch.len);
+            if (threadIdx.x == 0) {
+                a.scales[chunk] = r.scale;
+                st_agent(a.publish + chunk,
+                         ((uint64_t)(uint32_t)(r.epoch + 1u) << 32) | (uint64_t)__float_as_uint(r.scale));
             }
-            if ((uint32_t)(w >> 32) != want) st_agent(a.err, 2);
-            *s_scale = __uint_as_float((uint32_t)w);
         }
     }
+    return r;
+}
+
+// Scale of a posted tile's chunk: computed here if this workgroup finalized it,
+// else read from the chunk's publish word once its epoch has advanced.
+__device__ float wait_scale(const CompressArgs &a, int chunk, const Posted &r, uint32_t *s_u32) {
+    if (r.mine) return r.scale;
+    if (threadIdx.x == 0) {
+        const uint64_t *pub = a.publish + chunk;
+        const uint32_t want = r.epoch + 1u;
+        uint64_t w = ld_agent(pub);
+        uint32_t spins = ld_agent(a.err) != 0 ? a.spin_limit : 0u;
+        while ((uint32_t)(w >> 32) != want && !give_up(a, spins)) {
+            spin_pause();
+            w = ld_agent(pub);
+            ++spins;
+        }
+        if ((uint32_t)(w >> 32) != want) st_agent(a.err, 2);
+        s_u32[1] = (uint32_t)w;
+    }
     __syncthreads();
-    scale = *s_scale;
+    const float scale = __uint_as_float(s_u32[1]);
     __syncthreads();
     return scale;
 }
@@ -273,17 +332,22 @@ __device__ __forceinline__ bool masked_at(const CompressArgs &a, const TileDesc 
     return mk;
 }
 
+__device__ __forceinline__ void store4(float *base, uint32_t k0, const float (&v)[4]) {
+    *reinterpret_cast<float4 *>(base + k0) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // ------------------------------------------------------- tile: finish
+// q = +-scale, e = c - q, masked -> 0, then the frozen-v step (update mode).
 template <int MODE, bool XB>
 __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDesc &t,
                                             const float (&c)[kPerThread], float scale) {
-    const int tid = threadIdx.x;
+    const bool full = tile_full(a, t);
     const bool all_masked = t.mask_lo < 0;
     const bool some_masked = t.mask_hi > t.mask_lo;
+    float *eb = a.e + t.start;
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
-        const int k0 = 4 * (tid + kBlock * r);
-        const int64_t i0 = t.start + k0;
+        const uint32_t k0 = lane_k0(r);
         float q4[4], e4[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -291,46 +355,47 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
             q4[q] = cq < 0.0f ? -scale : scale;
             e4[q] = sub_rn(cq, q4[q]);
             if (MODE != kServer) {
-                const bool mk = all_masked || (some_masked && masked_at(a, t, i0 + q));
+                const bool mk = all_masked || (some_masked && masked_at(a, t, t.start + k0 + q));
                 if (mk) {
                     q4[q] = 0.0f;
                     e4[q] = 0.0f;
                 }
             }
         }
-        const bool full = a.aligned && k0 + 3 < t.len;
         if (MODE == kServer) {
+            float *mo = a.m_out ? a.m_out + t.start : nullptr;
             if (full) {
-                *reinterpret_cast<float4 *>(a.e + i0) = make_float4(e4[0], e4[1], e4[2], e4[3]);
-                if (a.m_out) *reinterpret_cast<float4 *>(a.m_out + i0) = make_float4(q4[0], q4[1], q4[2], q4[3]);
+                store4(eb, k0, e4);
+                if (mo) store4(mo, k0, q4);
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (k0 + q < t.len) {
-                        a.e[i0 + q] = e4[q];
-                        if (a.m_out) a.m_out[i0 + q] = q4[q];
+                    if (k0 + q < (uint32_t)t.len) {
+                        eb[k0 + q] = e4[q];
+                        if (mo) mo[k0 + q] = q4[q];
                     }
             }
         } else if (MODE == kCompressOnly) {
             if (full) {
-                *reinterpret_cast<float4 *>(a.e + i0) = make_float4(e4[0], e4[1], e4[2], e4[3]);
+                store4(eb, k0, e4);
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (k0 + q < t.len) a.e[i0 + q] = e4[q];
+                    if (k0 + q < (uint32_t)t.len) eb[k0 + q] = e4[q];
             }
         } else {
+            const float *vb = a.v + t.start;
+            float *xb = a.x + t.start;
+            float *mb = a.m + t.start;
             float v4[4], x4[4];
             if (full) {
-                const float4 vv = *reinterpret_cast<const float4 *>(a.v + i0);
-                const float4 xx = *reinterpret_cast<const float4 *>(a.x + i0);
-                v4[0] = vv.x; v4[1] = vv.y; v4[2] = vv.z; v4[3] = vv.w;
-                x4[0] = xx.x; x4[1] = xx.y; x4[2] = xx.z; x4[3] = xx.w;
+                load4(vb, k0, v4);
+                load4(xb, k0, x4);
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    v4[q] = (k0 + q < t.len) ? a.v[i0 + q] : 1.0f;
-                    x4[q] = (k0 + q < t.len) ? a.x[i0 + q] : 0.0f;
+                    v4[q] = (k0 + q < (uint32_t)t.len) ? vb[k0 + q] : 1.0f;
+                    x4[q] = (k0 + q < (uint32_t)t.len) ? xb[k0 + q] : 0.0f;
                 }
             }
             float xn[4];
@@ -340,99 +405,163 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
                 xn[q] = x4[q] - a.lr * upd;
             }
             if (full) {
-                *reinterpret_cast<float4 *>(a.m + i0) = make_float4(q4[0], q4[1], q4[2], q4[3]);
-                *reinterpret_cast<float4 *>(a.e + i0) = make_float4(e4[0], e4[1], e4[2], e4[3]);
-                *reinterpret_cast<float4 *>(a.x + i0) = make_float4(xn[0], xn[1], xn[2], xn[3]);
+                store4(mb, k0, q4);
+                store4(eb, k0, e4);
+                store4(xb, k0, xn);
                 if (XB) {
                     uint2 pk;
                     pk.x = float_to_bf16_bits(xn[0]) | (float_to_bf16_bits(xn[1]) << 16);
                     pk.y = float_to_bf16_bits(xn[2]) | (float_to_bf16_bits(xn[3]) << 16);
-                    *reinterpret_cast<uint2 *>(a.xb + i0) = pk;
+                    *reinterpret_cast<uint2 *>(a.xb + t.start + k0) = pk;
                 }
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (k0 + q < t.len) {
-                        a.m[i0 + q] = q4[q];
-                        a.e[i0 + q] = e4[q];
-                        a.x[i0 + q] = xn[q];
-                        if (XB) a.xb[i0 + q] = (uint16_t)float_to_bf16_bits(xn[q]);
+                    if (k0 + q < (uint32_t)t.len) {
+                        mb[k0 + q] = q4[q];
+                        eb[k0 + q] = e4[q];
+                        xb[k0 + q] = xn[q];
+                        if (XB) a.xb[t.start + k0 + q] = (uint16_t)float_to_bf16_bits(xn[q]);
                     }
             }
         }
     }
 }
 
-__device__ __forceinline__ void load_worker_scales(const CompressArgs &a, int chunk, double *s_wscale) {
-    for (int w = threadIdx.x; w < a.W; w += kBlock) s_wscale[w] = (double)a.wscales[(int64_t)w * a.n_chunks + chunk];
+__device__ __forceinline__ void load_worker_scales(const CompressArgs &a, int chunk, float *s_wscale) {
+    for (int w = threadIdx.x; w < a.W; w += kBlock) s_wscale[w] = a.wscales[(int64_t)w * a.n_chunks + chunk];
     __syncthreads();
 }
 
 // Pass-1 stores c where e was (e is fully rewritten by pass 2).
 __device__ __forceinline__ void tile_store_c(const CompressArgs &a, const TileDesc &t, const float (&c)[kPerThread]) {
-    const int tid = threadIdx.x;
+    const bool full = tile_full(a, t);
+    float *eb = a.e + t.start;
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
-        const int k0 = 4 * (tid + kBlock * r);
-        const int64_t i0 = t.start + k0;
-        if (a.aligned && k0 + 3 < t.len) {
-            *reinterpret_cast<float4 *>(a.e + i0) = make_float4(c[4 * r], c[4 * r + 1], c[4 * r + 2], c[4 * r + 3]);
+        const uint32_t k0 = lane_k0(r);
+        if (full) {
+            *reinterpret_cast<float4 *>(eb + k0) = make_float4(c[4 * r], c[4 * r + 1], c[4 * r + 2], c[4 * r + 3]);
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (k0 + q < t.len) a.e[i0 + q] = c[4 * r + q];
+                if (k0 + q < (uint32_t)t.len) eb[k0 + q] = c[4 * r + q];
         }
     }
 }
 
 __device__ __forceinline__ void tile_load_c(const CompressArgs &a, const TileDesc &t, float (&c)[kPerThread]) {
-    const int tid = threadIdx.x;
+    const bool full = tile_full(a, t);
+    const float *eb = a.e + t.start;
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
-        const int k0 = 4 * (tid + kBlock * r);
-        const int64_t i0 = t.start + k0;
-        if (a.aligned && k0 + 3 < t.len) {
-            const float4 cc = *reinterpret_cast<const float4 *>(a.e + i0);
+        const uint32_t k0 = lane_k0(r);
+        if (full) {
+            const float4 cc = *reinterpret_cast<const float4 *>(eb + k0);
             c[4 * r] = cc.x; c[4 * r + 1] = cc.y; c[4 * r + 2] = cc.z; c[4 * r + 3] = cc.w;
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) c[4 * r + q] = (k0 + q < t.len) ? a.e[i0 + q] : 0.0f;
+            for (int q = 0; q < 4; ++q) c[4 * r + q] = (k0 + q < (uint32_t)t.len) ? eb[k0 + q] : 0.0f;
         }
     }
 }
 
 constexpr int kMaxW = 1024;
+constexpr int kOnepassWavesPerSimd = 6;
+
+// c of a posted tile waits in LDS (each thread reads back only what it wrote).
+__device__ __forceinline__ void park_c(float4 *s, const float (&c)[kPerThread]) {
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r)
+        s[r * kBlock + threadIdx.x] = make_float4(c[4 * r], c[4 * r + 1], c[4 * r + 2], c[4 * r + 3]);
+}
+__device__ __forceinline__ void unpark_c(const float4 *s, float (&c)[kPerThread]) {
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+        const float4 v = s[r * kBlock + threadIdx.x];
+        c[4 * r] = v.x;
+        c[4 * r + 1] = v.y;
+        c[4 * r + 2] = v.z;
+        c[4 * r + 3] = v.w;
+    }
+}
 
 // ------------------------------------------------------------- kernels
-// One pass, persistent and cooperative: every workgroup of the grid is resident,
-// so a tile may wait for the other tiles of its chunk.  Workgroup b takes list
-// positions b, b+G, b+2G, ...; a chunk spans at most G consecutive positions, so
-// its tiles sit in distinct workgroups and every wait ends.
+// One pass, persistent, cooperative (every workgroup of the grid is resident).
+// Workgroup b takes list positions b, b+G, b+2G, ... and keeps kDepth tiles in
+// flight: it computes and posts tile i+kDepth-1 (c parked in LDS) before it waits
+// for tile i's chunk scale and finishes tile i, so the chunk-norm exchange
+// overlaps streaming.  Termination: a workgroup posts tile i+kDepth-1 only after
+// finishing tile i-1; if a chunk spans at most kDepth*G list positions, every
+// workgroup has posted all its tiles of a chunk before it waits on that chunk,
+// so the lowest unfinished chunk always completes.
+constexpr int kDepth = 3;
+
+template <int MODE, bool GBF16>
+__device__ __forceinline__ Posted produce(const CompressArgs &a, int tile_id, const TileDesc &t, float4 *slot_c,
+                                          float *s_wscale, DD *s_red, uint32_t *s_u32, double *s_total) {
+    if (MODE == kServer) load_worker_scales(a, t.chunk, s_wscale);
+    float c[kPerThread];
+    tile_compute_c<MODE, GBF16>(a, t, c, s_wscale);
+    tile_store_bits(a, t, c);
+    park_c(slot_c, c);
+    return post_tile<true>(a, tile_id, t.chunk, tile_sum_squares(c, s_red), s_red, s_u32, s_total);
+}
+
 template <int MODE, bool GBF16, bool XB>
-__global__ __launch_bounds__(kBlock, 4) void k_compress_onepass(CompressArgs a) {
+__global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepass(CompressArgs a) {
+    __shared__ float4 s_c[kDepth][kGroups * kBlock];
+    __shared__ TileDesc s_tile[kDepth];
+    __shared__ Posted s_post[kDepth];
     __shared__ DD s_red[kWaves];
-    __shared__ float s_scale;
-    __shared__ uint32_t s_flag[2];
-    __shared__ double s_wscale[MODE == kServer ? kMaxW : 1];
-    for (int p = blockIdx.x; p < a.list_len; p += gridDim.x) {
-        const int tile_id = a.list[p];
-        const TileDesc t = a.tiles[tile_id];
-        if (MODE == kServer) load_worker_scales(a, t.chunk, s_wscale);
+    __shared__ uint32_t s_u32[2];
+    __shared__ double s_total;
+    __shared__ float s_wscale[MODE == kServer ? kMaxW : 1];
+    const int G = (int)gridDim.x;
+    const int b = (int)blockIdx.x;
+    const int mine = a.list_len > b ? (a.list_len - b + G - 1) / G : 0;  // tiles of this workgroup
+    // prologue: post the first kDepth-1 tiles
+    for (int i = 0; i < kDepth - 1 && i < mine; ++i) {
+        const int id = a.list[b + i * G];
+        const TileDesc t = a.tiles[id];
+        const Posted r = produce<MODE, GBF16>(a, id, t, s_c[i], s_wscale, s_red, s_u32, &s_total);
+        if (threadIdx.x == 0) {
+            s_tile[i] = t;
+            s_post[i] = r;
+        }
+    }
+    for (int i = 0; i < mine; ++i) {
+        const int ahead = i + kDepth - 1;
+        if (ahead < mine) {
+            const int id = a.list[b + ahead * G];
+            const TileDesc t = a.tiles[id];
+            const int sl = ahead % kDepth;
+            const Posted r = produce<MODE, GBF16>(a, id, t, s_c[sl], s_wscale, s_red, s_u32, &s_total);
+            if (threadIdx.x == 0) {
+                s_tile[sl] = t;
+                s_post[sl] = r;
+            }
+        }
+        __syncthreads();
+        const int sl = i % kDepth;
+        const TileDesc t = s_tile[sl];
+        const Posted r = s_post[sl];
+        const float scale = wait_scale(a, t.chunk, r, s_u32);
         float c[kPerThread];
-        tile_compute_c<MODE, GBF16>(a, t, c, s_wscale);
-        tile_store_bits(a, t, c);
-        const double part = tile_sum_squares(c, s_red);
-        const float scale = arrive<true>(a, tile_id, t.chunk, part, s_red, &s_scale, s_flag);
+        unpark_c(s_c[sl], c);
         tile_finish<MODE, XB>(a, t, c, scale);
     }
 }
 
+// Two passes for chunks too large for the one-pass kernel: pass 1 stores c in
+// place of e, its sign words and its partial; a per-chunk kernel sums the
+// partials; pass 2 finishes from c, v and x.
 template <int MODE, bool GBF16>
 __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     __shared__ DD s_red[kWaves];
-    __shared__ float s_scale;
-    __shared__ uint32_t s_flag[2];
-    __shared__ double s_wscale[MODE == kServer ? kMaxW : 1];
+    __shared__ uint32_t s_u32[2];
+    __shared__ double s_total;
+    __shared__ float s_wscale[MODE == kServer ? kMaxW : 1];
     const int tile_id = a.list[blockIdx.x];
     const TileDesc t = a.tiles[tile_id];
     if (MODE == kServer) load_worker_scales(a, t.chunk, s_wscale);
@@ -441,7 +570,18 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     tile_store_bits(a, t, c);
     tile_store_c(a, t, c);
     const double part = tile_sum_squares(c, s_red);
-    arrive<false>(a, tile_id, t.chunk, part, s_red, &s_scale, s_flag);
+    if (threadIdx.x == 0) st_agent(a.slots + tile_id, tag_partial(part));
+    (void)s_u32;
+    (void)s_total;
+}
+
+__global__ __launch_bounds__(kBlock) void k_finalize_chunks(CompressArgs a, const int32_t *chunk_list) {
+    __shared__ DD s_red[kWaves];
+    __shared__ double s_total;
+    const int chunk = chunk_list[blockIdx.x];
+    const ChunkDesc ch = a.chunks[chunk];
+    const double S = chunk_sum(a, ch, s_red, &s_total);
+    if (threadIdx.x == 0) a.scales[chunk] = scale_of(S, ch.len);
 }
 
 template <int MODE, bool XB>
@@ -458,7 +598,8 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass2(CompressArgs a) {
 template <int MODE, bool GBF16, bool XB>
 static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_t stream) {
     const int base = MODE == kServer ? kProfServerPass1 : kProfPass1;
-    // two-pass chunks first: pass 1 ...
+    // Two-pass chunks first, pass 2 right after pass 1 so that the c it re-reads
+    // is still in the memory-side cache; then the one-pass kernel for the rest.
     if (p->n_big > 0) {
         a.list = p->d_big_list;
         a.list_len = p->n_big;
@@ -467,11 +608,38 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
         prof_after(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e);
+        prof_before(kProfFinalize, stream);
+        hipLaunchKernelGGL(k_finalize_chunks, dim3(p->n_big_chunks), dim3(kBlock), 0, stream, a,
+                           (const int32_t *)p->d_big_chunks);
+        prof_after(stream);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_status(e);
+        prof_before(base + 2, stream);
+        hipLaunchKernelGGL((k_compress_pass2<MODE, XB>), dim3(p->n_big), dim3(kBlock), 0, stream, a);
+        prof_after(stream);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_status(e);
     }
     if (p->n_coop > 0) {
         a.list = p->d_coop_list;
         a.list_len = p->n_coop;
-        const int grid = p->n_coop < p->coop_capacity ? p->n_coop : p->coop_capacity;
+        // Each variant runs with its own resident capacity; the plan's one-pass /
+        // two-pass split was made for the smallest one, so kDepth * grid still
+        // covers every one-pass chunk.
+        static int32_t cap_cache[64] = {0};
+        const int dev = p->device;
+        int32_t cap = (dev >= 0 && dev < 64) ? cap_cache[dev] : 0;
+        if (cap <= 0) {
+            int per_cu = 0, cus = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu, reinterpret_cast<const void *>(&k_compress_onepass<MODE, GBF16, XB>), kBlock, 0) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+                return ONEBIT_ERR_HIP;
+            cap = per_cu * cus;
+            if (dev >= 0 && dev < 64) cap_cache[dev] = cap;
+        }
+        if (cap < p->coop_capacity) return ONEBIT_ERR_HIP;
+        const int grid = p->n_coop < cap ? p->n_coop : cap;
         void *args[] = {&a};
         prof_before(base + 1, stream);
         hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_compress_onepass<MODE, GBF16, XB>),
@@ -482,16 +650,6 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
             return hip_status(e);
         }
     }
-    // ... and pass 2 once every pass-1 scale is known.
-    if (p->n_big > 0) {
-        a.list = p->d_big_list;
-        a.list_len = p->n_big;
-        prof_before(base + 2, stream);
-        hipLaunchKernelGGL((k_compress_pass2<MODE, XB>), dim3(p->n_big), dim3(kBlock), 0, stream, a);
-        prof_after(stream);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return hip_status(e);
-    }
     return ONEBIT_OK;
 }
 
@@ -500,6 +658,8 @@ static int occupancy_of(const void *fn) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kBlock, 0) != hipSuccess) return 0;
     return blocks;
 }
+
+int32_t coop_depth() { return kDepth; }
 
 int32_t coop_capacity(int device) {
     static int32_t cached[64] = {0};
@@ -570,7 +730,7 @@ extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void
     a.wd = (float)weight_decay;
     const WorkspaceView ws = workspace_view(workspace, plan->n_chunks);
     a.err = ws.err;
-    a.chunk_words = ws.chunk_words;
+    a.publish = ws.publish;
     a.slots = ws.slots;
     a.spin_limit = kSpinLimit;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -612,7 +772,7 @@ extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const
     a.scales = server_scales;
     const WorkspaceView ws = workspace_view(workspace, plan->n_chunks);
     a.err = ws.err;
-    a.chunk_words = ws.chunk_words;
+    a.publish = ws.publish;
     a.slots = ws.slots;
     a.spin_limit = kSpinLimit;
     return launch<kServer, false, false>(plan, a, static_cast<hipStream_t>(stream));

@@ -11,9 +11,9 @@ namespace onebit {
 // ------------------------------------------------------------- geometry
 constexpr int kBlock = 256;                 // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kGroups = 4;                  // float4 groups held per thread
-constexpr int kPerThread = 4 * kGroups;     // 16 elements per thread
-constexpr int kTile = kBlock * kPerThread;  // 4096 elements per tile
+constexpr int kGroups = 2;                  // float4 groups per thread per tile
+constexpr int kPerThread = 4 * kGroups;     // 8 elements per thread
+constexpr int kTile = kBlock * kPerThread;  // 2048 elements per tile
 
 // ------------------------------------------------------ exact fp32 ops
 // Each is exactly one IEEE binary32 operation, round-to-nearest-even, never fused

@@ -28,11 +28,11 @@ struct ChunkDesc {
 
 // Workspace layout (all 8-byte words, zero = ready):
 //   [0]                      error word (non-zero after a spin timeout)
-//   [1 .. 1+2*n_chunks)      per chunk: arrival {epoch:32 | count:32}, publish {epoch:32 | scale bits:32}
+//   [1 .. 1+n_chunks)        per chunk: published {epoch:32 | scale bits:32}
 //   [.. + n_tiles)           per tile: tagged fp64 partial sum of squares (0 = empty)
 struct WorkspaceView {
     uint64_t *err;
-    uint64_t *chunk_words;
+    uint64_t *publish;
     uint64_t *slots;
 };
 
@@ -52,8 +52,10 @@ struct onebit_plan_s {
     int64_t *d_mask_iv = nullptr;     // 2*n_mask_iv: [a, b) pairs, sorted, disjoint
     int32_t *d_coop_list = nullptr;   // tiles of chunks small enough to stay resident
     int32_t *d_big_list = nullptr;    // tiles of the other chunks (two-pass)
+    int32_t *d_big_chunks = nullptr;  // the two-pass chunks
     int32_t n_coop = 0;
     int32_t n_big = 0;
+    int32_t n_big_chunks = 0;
     int32_t coop_capacity = 0;        // resident workgroups the split was made for
 };
 
@@ -65,8 +67,10 @@ bool aligned16(const void *p);
 bool aligned_to(const void *p, uintptr_t bytes);
 onebit_status_t hip_status(hipError_t e);
 
-// Largest number of co-resident workgroups of the compress kernels on this device.
+// Largest number of co-resident workgroups of the compress kernels on this device,
+// and the number of tiles each of them keeps in flight.
 int32_t coop_capacity(int device);
+int32_t coop_depth();
 
 // Launch timing (diagnostics): while a profiling session is open every kernel
 // launch of the library is bracketed by two events on its stream.
@@ -80,7 +84,7 @@ enum ProfClass {
     kProfServerPass1 = 6,
     kProfServerOnepass = 7,
     kProfServerPass2 = 8,
-    kProfOther = 9,
+    kProfFinalize = 9,
     kProfClasses = 10
 };
 void prof_before(int cls, hipStream_t s);

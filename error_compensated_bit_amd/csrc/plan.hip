@@ -12,13 +12,13 @@
 namespace onebit {
 
 size_t workspace_bytes_for(int64_t n_chunks, int64_t n_tiles) {
-    const size_t words = 1 + 2 * (size_t)n_chunks + (size_t)n_tiles;
+    const size_t words = 1 + (size_t)n_chunks + (size_t)n_tiles;
     return (words * 8 + 255) / 256 * 256;
 }
 
 WorkspaceView workspace_view(void *ws, int64_t n_chunks) {
     uint64_t *w = static_cast<uint64_t *>(ws);
-    return WorkspaceView{w, w + 1, w + 1 + 2 * n_chunks};
+    return WorkspaceView{w, w + 1, w + 1 + n_chunks};
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -111,6 +111,7 @@ extern "C" void onebit_plan_destroy(onebit_plan_t p) {
     (void)hipFree(p->d_mask_iv);
     (void)hipFree(p->d_coop_list);
     (void)hipFree(p->d_big_list);
+    (void)hipFree(p->d_big_chunks);
     if (prev >= 0) (void)hipSetDevice(prev);
     delete p;
 }
@@ -193,22 +194,28 @@ extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int6
     p->n_tiles = (int64_t)tiles.size();
     p->words = word;
 
-    // one-pass chunks (<= resident workgroups) and two-pass chunks
+    // one-pass chunks (at most coop_depth() times the resident workgroups: the
+    // one-pass kernel keeps that many tiles in flight per workgroup) and two-pass
+    // chunks
     p->coop_capacity = coop_capacity(p->device);
-    std::vector<int32_t> coop, big;
+    std::vector<int32_t> coop, big, big_chunks;
     for (int64_t j = 0; j < n_chunks; ++j) {
         const ChunkDesc &c = chunks[j];
-        std::vector<int32_t> &dst = (c.ntiles <= p->coop_capacity) ? coop : big;
+        const bool one_pass = (int64_t)c.ntiles <= (int64_t)coop_depth() * (int64_t)p->coop_capacity;
+        std::vector<int32_t> &dst = one_pass ? coop : big;
         for (int32_t k = 0; k < c.ntiles; ++k) dst.push_back(c.first_tile + k);
+        if (!one_pass) big_chunks.push_back((int32_t)j);
     }
     p->n_coop = (int32_t)coop.size();
     p->n_big = (int32_t)big.size();
+    p->n_big_chunks = (int32_t)big_chunks.size();
 
     hipError_t e = upload(&p->d_tiles, tiles);
     if (e == hipSuccess) e = upload(&p->d_chunks, chunks);
     if (e == hipSuccess) e = upload(&p->d_mask_iv, iv);
     if (e == hipSuccess) e = upload(&p->d_coop_list, coop);
     if (e == hipSuccess) e = upload(&p->d_big_list, big);
+    if (e == hipSuccess) e = upload(&p->d_big_chunks, big_chunks);
     if (e != hipSuccess) {
         onebit_plan_destroy(p);
         return hip_status(e);
@@ -279,6 +286,12 @@ extern "C" int32_t onebit_device_coop_capacity(void) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     return coop_capacity(dev);
+}
+
+extern "C" int64_t onebit_onepass_max_elements(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    return (int64_t)coop_depth() * (int64_t)coop_capacity(dev) * (int64_t)kTile;
 }
 
 extern "C" void onebit_plan_stats(onebit_plan_t p, int64_t *out6) {

@@ -33,6 +33,7 @@ _SIGS = {
     "onebit_workspace_status": (_I, [_P, C.POINTER(_U64), _P]),
     "onebit_device_coop_capacity": (C.c_int32, []),
     "onebit_plan_stats": (None, [_P, _P]),
+    "onebit_onepass_max_elements": (_I64, []),
     "onebit_profile_begin": (None, []),
     "onebit_profile_end": (_I, [_P, _P]),
     "onebit_adam_warmup_step": (_I, [_P, _P, _P, _P, _I, _I64, _D, _D, _D, _D, _D, _I, _I64, _P]),
@@ -169,8 +170,12 @@ def onebit_device_coop_capacity() -> int:
     return int(load().onebit_device_coop_capacity())
 
 
+def onebit_onepass_max_elements() -> int:
+    return int(load().onebit_onepass_max_elements())
+
+
 PROFILE_CLASSES = ("warmup", "compress_pass1", "compress_onepass", "compress_pass2", "qsdp_quantize",
-                   "qsdp_dequantize", "server_pass1", "server_onepass", "server_pass2", "other")
+                   "qsdp_dequantize", "server_pass1", "server_onepass", "server_pass2", "finalize")
 
 
 def onebit_profile_begin():

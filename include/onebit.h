@@ -86,7 +86,7 @@ int64_t onebit_plan_chunks(onebit_plan_t plan);   /* n_chunks */
 int64_t onebit_plan_words(onebit_plan_t plan);    /* sum_j ceil(n_j / 32) */
 
 /* Device scratch (bytes) that onebit_compress_update / onebit_server_reduce need
- * for this plan: per-tile partial norms and per-chunk arrival counters.  The
+ * for this plan: per-tile partial norms and per-chunk published scales.  The
  * caller allocates it and must zero it once before first use (onebit_workspace_init
  * does that on a stream); every completed call leaves it ready for the next one,
  * for this or any other plan whose workspace size fits.  One workspace must not be
@@ -106,6 +106,9 @@ onebit_status_t onebit_workspace_status(const void *workspace, uint64_t *out, vo
  * largest chunk in tiles, 1 if every chunk starts on a multiple of 4 elements}. */
 int32_t onebit_device_coop_capacity(void);
 void onebit_plan_stats(onebit_plan_t plan, int64_t *out6);
+/* Largest chunk (elements) the one-pass path takes on the current device;
+ * larger chunks take the two-pass path. */
+int64_t onebit_onepass_max_elements(void);
 
 /* Launch timing.  Between onebit_profile_begin and onebit_profile_end every kernel
  * the library launches is bracketed by two HIP events on its own stream.
@@ -113,7 +116,7 @@ void onebit_plan_stats(onebit_plan_t plan, int64_t *out6);
  * the summed elapsed milliseconds and the launch count (host arrays of
  * ONEBIT_PROFILE_CLASSES entries, nullable).  Classes: 0 warmup, 1/2/3 worker
  * compression pass 1 / one-pass / pass 2, 4 quantize, 5 dequantize, 6/7/8 server
- * pass 1 / one-pass / pass 2, 9 other.  Not thread-safe; diagnostics only. */
+ * pass 1 / one-pass / pass 2, 9 chunk-norm finalization of two-pass chunks.  Not thread-safe; diagnostics only. */
 #define ONEBIT_PROFILE_CLASSES 10
 void onebit_profile_begin(void);
 onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);

@@ -194,8 +194,8 @@ def test_weight_decay_and_hyperparameters():
 
 def test_two_pass_chunk_next_to_one_pass_chunks():
     cap = ob.onebit_device_coop_capacity()
-    say(f"device capacity {cap} workgroups")
-    big = max(cap, 1) * 4096 + 4097
+    say(f"device capacity {cap} workgroups, one-pass chunks up to {ob.onebit_onepass_max_elements()}")
+    big = max(ob.onebit_onepass_max_elements(), 1) + 4097
     off = W.offsets_from_sizes([5000, big, 3, 70001])
     buf = CompressBuffers(off)
     st = ob.onebit_plan_stats(buf.plan)

@@ -65,6 +65,5 @@ def test_server_ragged_chunks(Wn):
 
 
 def test_server_two_pass_chunk():
-    cap = ob.onebit_device_coop_capacity()
-    off = W.offsets_from_sizes([max(cap, 1) * 4096 + 4097, 5000])
+    off = W.offsets_from_sizes([max(ob.onebit_onepass_max_elements(), 1) + 4097, 5000])
     run_allreduce(off, 2, 2, seed=77)
