@@ -233,6 +233,66 @@ __global__ __launch_bounds__(256) void k_qsdp_dequantize(QArgs a) {
     }
 }
 
+// ------------------------------------------------------ error statistics
+// Fixed grid and fixed reduction tree: the sums are bitwise reproducible.
+constexpr int kStatBlocks = 1024;
+
+__device__ __forceinline__ double block_sum_d(double v, double *s_red) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0) t = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    __syncthreads();
+    return t;
+}
+
+// partials[2b] = sum (y - x), partials[2b+1] = sum (y - x)^2 over block b's share;
+// ysum += y when given.
+__global__ __launch_bounds__(256) void k_qsdp_stats(const uint16_t *x, const float *y, int64_t n, double *ysum,
+                                                     double *partials) {
+    __shared__ double s_red[4];
+    double s1 = 0.0, s2 = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+        const double d = (double)y[i] - (double)bf16_bits_to_float(x[i]);
+        s1 += d;
+        s2 += d * d;
+        if (ysum) ysum[i] += (double)y[i];
+    }
+    const double t1 = block_sum_d(s1, s_red);
+    const double t2 = block_sum_d(s2, s_red);
+    if (threadIdx.x == 0) {
+        partials[2 * blockIdx.x] = t1;
+        partials[2 * blockIdx.x + 1] = t2;
+    }
+}
+
+// partials[b] = sum |ysum / seeds - x| over block b's share
+__global__ __launch_bounds__(256) void k_qsdp_mae(const uint16_t *x, const double *ysum, int64_t n, double inv_seeds,
+                                                   double *partials) {
+    __shared__ double s_red[4];
+    double s = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+        s += fabs(ysum[i] * inv_seeds - (double)bf16_bits_to_float(x[i]));
+    const double t = block_sum_d(s, s_red);
+    if (threadIdx.x == 0) partials[blockIdx.x] = t;
+}
+
+// out[k] += sum_b partials[b * width + k], k < width, in block order
+__global__ __launch_bounds__(256) void k_reduce_partials(const double *partials, int width, double *out, int add) {
+    __shared__ double s_red[4];
+    for (int k = 0; k < width; ++k) {
+        double v = 0.0;
+        for (int b = threadIdx.x; b < kStatBlocks; b += 256) v += partials[b * width + k];
+        const double t = block_sum_d(v, s_red);
+        if (threadIdx.x == 0) out[k] = add ? out[k] + t : t;
+    }
+}
+
 static unsigned grid_for(int64_t n_buckets) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -311,5 +371,28 @@ extern "C" onebit_status_t qsdp_dequantize(const uint8_t *codes, const float *bu
     else
         hipLaunchKernelGGL(k_qsdp_dequantize<8>, dim3(grid), dim3(256), 0, s, a);
     prof_after(s);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" onebit_status_t qsdp_error_stats(const uint16_t *x_bf16, const float *y, int64_t n, double *ysum,
+                                            double *sums, double *partials, void *stream) {
+    if (n < 0 || !sums || !partials) return ONEBIT_ERR_INVALID;
+    if (n > 0 && (!x_bf16 || !y)) return ONEBIT_ERR_INVALID;
+    if (!aligned_to(sums, 8) || !aligned_to(partials, 8) || (ysum && !aligned_to(ysum, 8))) return ONEBIT_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    prof_before(kProfFinalize, s);
+    hipLaunchKernelGGL(k_qsdp_stats, dim3(kStatBlocks), dim3(256), 0, s, x_bf16, y, n, ysum, partials);
+    hipLaunchKernelGGL(k_reduce_partials, dim3(1), dim3(256), 0, s, (const double *)partials, 2, sums, 1);
+    prof_after(s);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" onebit_status_t qsdp_mean_abs_error(const uint16_t *x_bf16, const double *ysum, int64_t n, int seeds,
+                                               double *out, double *partials, void *stream) {
+    if (n < 1 || seeds < 1 || !x_bf16 || !ysum || !out || !partials) return ONEBIT_ERR_INVALID;
+    if (!aligned_to(ysum, 8) || !aligned_to(out, 8) || !aligned_to(partials, 8)) return ONEBIT_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(k_qsdp_mae, dim3(kStatBlocks), dim3(256), 0, s, x_bf16, ysum, n, 1.0 / (double)seeds, partials);
+    hipLaunchKernelGGL(k_reduce_partials, dim3(1), dim3(256), 0, s, (const double *)partials, 1, out, 0);
     return hip_status(hipGetLastError());
 }

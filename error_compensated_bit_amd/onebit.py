@@ -41,7 +41,11 @@ _SIGS = {
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "qsdp_quantize": (_I, [_P, _I64, _I, _I, _U64, _P, _P, _P, _P]),
     "qsdp_dequantize": (_I, [_P, _P, _P, _I64, _I, _I, _P, _P, _P]),
+    "qsdp_error_stats": (_I, [_P, _P, _I64, _P, _P, _P, _P]),
+    "qsdp_mean_abs_error": (_I, [_P, _P, _I64, _I, _P, _P, _P]),
 }
+
+QSDP_STATS_PARTIALS = 1024
 
 _lib = None
 
@@ -231,3 +235,13 @@ def qsdp_quantize(x_bf16, bucket, bits, seed, codes, bucket_min, bucket_max, str
 def qsdp_dequantize(codes, bucket_min, bucket_max, n, bucket, bits, out_bf16=None, out_f32=None, stream=None):
     _check(load().qsdp_dequantize(_ptr(codes), _ptr(bucket_min), _ptr(bucket_max), int(n), int(bucket), int(bits),
                                   _ptr(out_bf16), _ptr(out_f32), _stream(stream)), "qsdp_dequantize")
+
+
+def qsdp_error_stats(x_bf16, y, ysum, sums, partials, stream=None):
+    _check(load().qsdp_error_stats(_ptr(x_bf16), _ptr(y), y.numel(), _ptr(ysum), _ptr(sums), _ptr(partials),
+                                   _stream(stream)), "qsdp_error_stats")
+
+
+def qsdp_mean_abs_error(x_bf16, ysum, seeds, out, partials, stream=None):
+    _check(load().qsdp_mean_abs_error(_ptr(x_bf16), _ptr(ysum), ysum.numel(), int(seeds), _ptr(out), _ptr(partials),
+                                      _stream(stream)), "qsdp_mean_abs_error")

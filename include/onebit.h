@@ -183,6 +183,22 @@ onebit_status_t qsdp_dequantize(const uint8_t *codes, const float *bucket_min,
                                 const float *bucket_max, int64_t n, int bucket, int bits,
                                 uint16_t *out_bf16, float *out_f32, void *stream);
 
+/* Error statistics of one dequantized draw y (fp32 [n], e.g. out_f32 above)
+ * against the bf16 weights x, for the unbiasedness measurement over repeated
+ * seeds ([QSDP] "proposed method": the expectation of the quantized weight equals
+ * the weight):  sums[0] += sum_i (y_i - x_i),  sums[1] += sum_i (y_i - x_i)^2,
+ * both fp64 (device [2]); ysum (device fp64 [n], nullable): ysum_i += y_i.
+ * partials: device scratch of 2 * QSDP_STATS_PARTIALS doubles.  The reduction
+ * order is fixed, so results are bitwise reproducible. */
+#define QSDP_STATS_PARTIALS 1024
+onebit_status_t qsdp_error_stats(const uint16_t *x_bf16, const float *y, int64_t n, double *ysum,
+                                 double *sums, double *partials, void *stream);
+
+/* *out (device fp64) = sum_i | ysum_i / seeds - x_i |: with the mean abs error of
+ * the seed-averaged quantizer, divide by n.  Same partials scratch. */
+onebit_status_t qsdp_mean_abs_error(const uint16_t *x_bf16, const double *ysum, int64_t n, int seeds,
+                                    double *out, double *partials, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
