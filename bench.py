@@ -14,8 +14,21 @@ resident in HBM.  A "step" is one such call.  Also reported:
                all-reduce, QSDP quantize/dequantize) unless --headline-only.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
+
+Profiling (rocprofv3 runs the program itself, so these modes only do the work):
+  python bench.py --profile            headline workload, a few steps, then a
+                                       1 GiB device-to-device copy used to
+                                       calibrate the FETCH_SIZE/WRITE_SIZE counters
+  python bench.py --summarize-profile KT FETCH WRITE
+                                       turn three rocprofv3 CSV output directories
+                                       (kernel trace+stats, --pmc FETCH_SIZE,
+                                       --pmc WRITE_SIZE) into the text summary kept
+                                       under profiles/ (printed to stdout)
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -155,6 +168,117 @@ def cpu_baseline(wl, dev, budget_s=12.0):
                 seconds=spent)
 
 
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "compress_onepass_bert_large.md")
+ONEPASS_SOURCE = os.path.join(ROOT, "error_compensated_bit_amd", "csrc", "compress.hip")
+CALIBRATION_FLOATS = 1 << 28          # 1 GiB copied by the profile mode
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "error_compensated_bit_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profile_mode(steps):
+    """Work for rocprofv3: the headline step `steps` times, then a plain 1 GiB copy."""
+    import torch
+    ensure_built()
+    from error_compensated_bit_amd import workloads as W
+    dev = "cuda:0"
+    wl = W.bert_like()
+    plan, step, ws = compress_setup(wl, dev)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    src = torch.ones(CALIBRATION_FLOATS, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)        # plain streaming copy: 16-byte vector loads and stores
+    torch.cuda.synchronize()
+    log(f"[profile] {steps} steps of {wl.name} and one {CALIBRATION_FLOATS * 4} B copy done")
+
+
+def _rows(dirname, suffix):
+    files = glob.glob(os.path.join(dirname, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {dirname}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def summarize_profile(kt_dir, fetch_dir, write_dir):
+    """Summary text from rocprofv3 output (kernel trace + stats, FETCH_SIZE, WRITE_SIZE runs)."""
+    import numpy as np
+    stats = _rows(kt_dir, "kernel_stats.csv")
+    out = ["# k_compress_onepass on the BERT-Large-shaped vector (335,143,938 fp32 params)", ""]
+    out.append("Commands (from the repository root, on one MI355X):")
+    out.append("```")
+    for d, extra in ((kt_dir, "--kernel-trace --stats"), (fetch_dir, "--pmc FETCH_SIZE"), (write_dir, "--pmc WRITE_SIZE")):
+        out.append(f"rocprofv3 {extra} --output-format csv -d {d} -o bench -- python3 bench.py --profile")
+    out.append(f"python bench.py --summarize-profile {kt_dir} {fetch_dir} {write_dir}")
+    out.append("```")
+    out.append(f"Library source digest: {source_digest()}")
+    out.append("")
+    out.append("## Kernel time (rocprofv3 --kernel-trace --stats)")
+    out.append("")
+    out.append("| kernel | calls | average ns | min ns | max ns |")
+    out.append("|---|---|---|---|---|")
+    for r in stats:
+        if "onebit" in r["Name"] or "neg_kernel" in r["Name"]:
+            out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    res = {}
+    for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _rows(d, "counter_collection.csv")
+        per = {}
+        for r in rows:
+            if r.get("Counter_Name") != key:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        res[key] = per
+    def pick(per, pred, how=np.median):
+        vals = [v for k, vs in per.items() if pred(k) for v in vs]
+        return float(how(vals)) if vals else None
+    onepass = lambda k: "k_compress_onepass" in k  # noqa: E731
+    copy = lambda k: "neg_kernel" in k  # noqa: E731
+    f_one, w_one = pick(res["FETCH_SIZE"], onepass), pick(res["WRITE_SIZE"], onepass)
+    # the calibration copy is the largest copy dispatch of the run
+    f_cp, w_cp = pick(res["FETCH_SIZE"], copy, np.max), pick(res["WRITE_SIZE"], copy, np.max)
+    cal_bytes = CALIBRATION_FLOATS * 4
+    f_scale = cal_bytes / (f_cp * 1024.0) if f_cp else None
+    w_scale = cal_bytes / (w_cp * 1024.0) if w_cp else None
+    out.append("")
+    out.append("## HBM traffic per launch (rocprofv3 --pmc, KiB per dispatch, median over dispatches)")
+    out.append("")
+    out.append(f"- calibration copy of {cal_bytes} B: FETCH_SIZE {f_cp} KiB, WRITE_SIZE {w_cp} KiB "
+               f"-> scale {f_scale:.4f} (fetch), {w_scale:.4f} (write) bytes per counted byte")
+    out.append(f"- k_compress_onepass: FETCH_SIZE {f_one} KiB, WRITE_SIZE {w_one} KiB")
+    t_read = f_one * 1024.0 * f_scale
+    t_write = w_one * 1024.0 * w_scale
+    out.append(f"- traffic_read_bytes: {t_read:.0f}")
+    out.append(f"- traffic_write_bytes: {t_write:.0f}")
+    out.append(f"- traffic_bytes_per_launch: {t_read + t_write:.0f}")
+    return "\n".join(out) + "\n"
+
+
+def profile_traffic():
+    """Traffic per launch of the one-pass kernel from the committed summary, if the sources still match."""
+    try:
+        text = open(PROFILE_SUMMARY).read()
+    except OSError:
+        return None
+    if f"Library source digest: {source_digest()}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("- traffic_bytes_per_launch:"):
+            return float(line.split(":")[1])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,7 +287,15 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="bert_large", choices=["bert_large", "gpt2_xl"])
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_profile:
+        sys.stdout.write(summarize_profile(*args.summarize_profile))
+        return
+    if args.profile:
+        profile_mode(max(1, min(args.steps, 5)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path: the compressed all-reduce is simulated inside one GPU's memory)", file=sys.stderr)
@@ -217,7 +349,7 @@ def main():
                    "params": wl.n, "chunks": wl.n_chunks, "grad_dtype": "bf16" if wl.grad_bf16 else "f32",
                    "bytes_per_param": bpe, "plan": head["plan"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": (achieved / PEAK_HBM_GBPS) if achieved else None, "traffic": None,
+                     "frac": (achieved / PEAK_HBM_GBPS) if achieved else None, "traffic": profile_traffic(),
                      "kernel": "k_compress_onepass", "bytes_per_launch": bpe * head["onepass_elements"],
                      "mean_launch_ms": k_ms},
         "cpu_baseline": ({k: base[k] for k in ("value", "unit", "cores", "kind", "sample")} if base else None),
