@@ -402,6 +402,37 @@ def secondary_rows(dev, args):
     torch.cuda.empty_cache()
     log(f"[bench] qsdp {[(k, v) for k, v in rows.items() if 'qsdp' in k]}")
 
+    # simulated compressed all-reduce: 16 workers x 64M fp32, 16 chunks of 4M
+    a = W.AllreduceWorkload()
+    plan = ob.onebit_plan_create(a.chunk_off)
+    words, nch = ob.onebit_plan_words(plan), ob.onebit_plan_chunks(plan)
+    m = torch.zeros(a.n, device=dev)
+    e = torch.zeros((a.W, a.n), device=dev)
+    es = torch.zeros(a.n, device=dev)
+    grads = torch.randn((a.W, a.n), device=dev) * a.grad_std
+    wbits = torch.zeros((a.W, words), dtype=torch.int32, device=dev)
+    wsc = torch.zeros((a.W, nch), device=dev)
+    sbits = torch.zeros(words, dtype=torch.int32, device=dev)
+    ssc = torch.zeros(nch, device=dev)
+    wsp = torch.zeros(ob.onebit_plan_workspace_bytes(plan) // 8, dtype=torch.int64, device=dev)
+
+    def allreduce_step():
+        for w in range(a.W):
+            ob.onebit_compress_update(plan, grads[w], m, e[w], None, None, None, wbits[w], wsc[w], lr=0.0,
+                                      beta1=0.9, eps=1e-8, weight_decay=0.0, workspace=wsp)
+        ob.onebit_server_reduce(plan, wbits, wsc, es, sbits, ssc, m, wsp)
+    t, kt = timed(allreduce_step, steps, 1)
+    w_ms = kt.mean_ms("compress_onepass")
+    s_ms = kt.mean_ms("server_onepass")
+    step_bytes = (B_WORKER * a.W + 14.125) * a.n
+    rows["allreduce_16x64M"] = dict(ms_per_step=t * 1e3, gbps=step_bytes / t / 1e9,
+                                    worker_kernel_gbps=B_WORKER * a.n / (w_ms * 1e-3) / 1e9,
+                                    server_kernel_gbps=14.125 * a.n / (s_ms * 1e-3) / 1e9,
+                                    server_kernel_ms=s_ms, worker_kernel_ms=w_ms)
+    del m, e, es, grads, wbits, wsc, sbits, ssc, wsp, plan
+    torch.cuda.empty_cache()
+    log(f"[bench] allreduce {rows['allreduce_16x64M']}")
+
     # GPT-2-XL-shaped vector, bf16 gradients, bf16 copy of x
     wl = W.gpt2_like()
     r = bench_compress(wl, steps, 1, dev, B_COMPRESS_BF16_COPY)

@@ -50,6 +50,7 @@ struct CompressArgs {
     int32_t W;
     int64_t plan_words;
     int64_t n_chunks;
+    double w_pow2_scale;  // 1/W when W is a power of two, else 0
     float *m_out;
     // outputs
     uint32_t *bits;
@@ -102,9 +103,72 @@ __device__ __forceinline__ void load4(const float *base, uint32_t k0, float (&v)
     v[0] = h.x; v[1] = h.y; v[2] = h.z; v[3] = h.w;
 }
 
+// Server tiles: average of the W workers' decompressed values, summed in fp64 in
+// worker order 0..W-1.  Workers are taken kWBatch at a time: their scales for the
+// chunk and the tile's packed words are staged in LDS (each worker's words load as
+// one 256-byte run), then every thread adds +-s for its elements, forming -s by
+// flipping the sign bit of s.
+constexpr int kWBatch = 16;
+constexpr int kTileWords = kTile / 32;
+
+__device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileDesc &t, float (&c)[kPerThread],
+                                              double *s_wscale_d, uint32_t *s_words) {
+    const bool full = tile_full(a, t);
+    const int nwords = (t.len + 31) / 32;
+    double acc[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) acc[j] = 0.0;
+    for (int w0 = 0; w0 < a.W; w0 += kWBatch) {
+        const int wn = min(kWBatch, a.W - w0);
+        __syncthreads();  // previous batch fully consumed
+        for (int w = threadIdx.x; w < wn; w += kBlock)
+            s_wscale_d[w] = (double)a.wscales[(int64_t)(w0 + w) * a.n_chunks + t.chunk];
+        for (int k = threadIdx.x; k < wn * kTileWords; k += kBlock) {
+            const int w = k / kTileWords, i = k % kTileWords;
+            s_words[k] = i < nwords ? a.wbits[(int64_t)(w0 + w) * a.plan_words + t.word + i] : 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kGroups; ++r) {
+            const uint32_t k0 = lane_k0(r);
+            const uint32_t wi = k0 >> 5;
+            const uint32_t sh = k0 & 31u;
+            for (int w = 0; w < wn; ++w) {
+                const uint32_t bw = s_words[w * kTileWords + wi] >> sh;
+                const long long sb = __double_as_longlong(s_wscale_d[w]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const long long flip = (long long)((bw >> q) & 1u) << 63;
+                    acc[4 * r + q] = __dadd_rn(acc[4 * r + q], __longlong_as_double(sb ^ flip));
+                }
+            }
+        }
+    }
+    const float *eb = a.e + t.start;
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+        const uint32_t k0 = lane_k0(r);
+        float es[4];
+        if (full) {
+            load4(eb, k0, es);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) es[q] = (k0 + q < (uint32_t)t.len) ? eb[k0 + q] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // a power-of-two W divides exactly by scaling
+            const double x = acc[4 * r + q];
+            const double mean = a.w_pow2_scale != 0.0 ? __dmul_rn(x, a.w_pow2_scale) : __ddiv_rn(x, (double)a.W);
+            c[4 * r + q] = (full || k0 + q < (uint32_t)t.len) ? add_rn((float)mean, es[q]) : 0.0f;
+        }
+    }
+}
+
 template <int MODE, bool GBF16>
 __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const TileDesc &t,
-                                               float (&c)[kPerThread], const float *s_wscale) {
+                                               float (&c)[kPerThread], double *s_wscale_d,
+                                               uint32_t *s_words) {
     const bool full = tile_full(a, t);
     if (MODE != kServer) {
         const float *mb = a.m + t.start;
@@ -137,36 +201,7 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
             }
         }
     } else {
-        // server: average of the W workers' decompressed values, fp64 in worker order
-        const float *eb = a.e + t.start;
-        const double dW = (double)a.W;
-#pragma unroll
-        for (int r = 0; r < kGroups; ++r) {
-            const uint32_t k0 = lane_k0(r);
-            double acc[4] = {0.0, 0.0, 0.0, 0.0};
-            if (full || k0 < (uint32_t)t.len) {
-                const uint32_t *wb = a.wbits + t.word + (k0 >> 5);
-                const uint32_t sh = k0 & 31u;
-                for (int w = 0; w < a.W; ++w) {
-                    const uint32_t bw = wb[(int64_t)w * a.plan_words] >> sh;
-                    const double sw = (double)s_wscale[w];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = __dadd_rn(acc[q], ((bw >> q) & 1u) ? -sw : sw);
-                }
-            }
-            float es[4];
-            if (full) {
-                load4(eb, k0, es);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) es[q] = (k0 + q < (uint32_t)t.len) ? eb[k0 + q] : 0.0f;
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float avg = (float)__ddiv_rn(acc[q], dW);
-                c[4 * r + q] = (full || k0 + q < (uint32_t)t.len) ? add_rn(avg, es[q]) : 0.0f;
-            }
-        }
+        server_tile_c(a, t, c, s_wscale_d, s_words);
     }
 }
 
@@ -428,11 +463,6 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
     }
 }
 
-__device__ __forceinline__ void load_worker_scales(const CompressArgs &a, int chunk, float *s_wscale) {
-    for (int w = threadIdx.x; w < a.W; w += kBlock) s_wscale[w] = a.wscales[(int64_t)w * a.n_chunks + chunk];
-    __syncthreads();
-}
-
 // Pass-1 stores c where e was (e is fully rewritten by pass 2).
 __device__ __forceinline__ void tile_store_c(const CompressArgs &a, const TileDesc &t, const float (&c)[kPerThread]) {
     const bool full = tile_full(a, t);
@@ -466,8 +496,8 @@ __device__ __forceinline__ void tile_load_c(const CompressArgs &a, const TileDes
     }
 }
 
-constexpr int kMaxW = 1024;
 constexpr int kOnepassWavesPerSimd = 6;
+constexpr int kMaxW = 1024;
 
 // c of a posted tile waits in LDS (each thread reads back only what it wrote).
 __device__ __forceinline__ void park_c(float4 *s, const float (&c)[kPerThread]) {
@@ -499,10 +529,10 @@ constexpr int kDepth = 3;
 
 template <int MODE, bool GBF16>
 __device__ __forceinline__ Posted produce(const CompressArgs &a, int tile_id, const TileDesc &t, float4 *slot_c,
-                                          float *s_wscale, DD *s_red, uint32_t *s_u32, double *s_total) {
-    if (MODE == kServer) load_worker_scales(a, t.chunk, s_wscale);
+                                          double *s_wscale_d, uint32_t *s_words, DD *s_red, uint32_t *s_u32,
+                                          double *s_total) {
     float c[kPerThread];
-    tile_compute_c<MODE, GBF16>(a, t, c, s_wscale);
+    tile_compute_c<MODE, GBF16>(a, t, c, s_wscale_d, s_words);
     tile_store_bits(a, t, c);
     park_c(slot_c, c);
     return post_tile<true>(a, tile_id, t.chunk, tile_sum_squares(c, s_red), s_red, s_u32, s_total);
@@ -516,7 +546,8 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
     __shared__ DD s_red[kWaves];
     __shared__ uint32_t s_u32[2];
     __shared__ double s_total;
-    __shared__ float s_wscale[MODE == kServer ? kMaxW : 1];
+    __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
+    __shared__ uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int G = (int)gridDim.x;
     const int b = (int)blockIdx.x;
     const int mine = a.list_len > b ? (a.list_len - b + G - 1) / G : 0;  // tiles of this workgroup
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
     for (int i = 0; i < kDepth - 1 && i < mine; ++i) {
         const int id = a.list[b + i * G];
         const TileDesc t = a.tiles[id];
-        const Posted r = produce<MODE, GBF16>(a, id, t, s_c[i], s_wscale, s_red, s_u32, &s_total);
+        const Posted r = produce<MODE, GBF16>(a, id, t, s_c[i], s_wscale_d, s_words, s_red, s_u32, &s_total);
         if (threadIdx.x == 0) {
             s_tile[i] = t;
             s_post[i] = r;
@@ -536,7 +567,7 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
             const int id = a.list[b + ahead * G];
             const TileDesc t = a.tiles[id];
             const int sl = ahead % kDepth;
-            const Posted r = produce<MODE, GBF16>(a, id, t, s_c[sl], s_wscale, s_red, s_u32, &s_total);
+            const Posted r = produce<MODE, GBF16>(a, id, t, s_c[sl], s_wscale_d, s_words, s_red, s_u32, &s_total);
             if (threadIdx.x == 0) {
                 s_tile[sl] = t;
                 s_post[sl] = r;
@@ -561,12 +592,12 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     __shared__ DD s_red[kWaves];
     __shared__ uint32_t s_u32[2];
     __shared__ double s_total;
-    __shared__ float s_wscale[MODE == kServer ? kMaxW : 1];
+    __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
+    __shared__ uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int tile_id = a.list[blockIdx.x];
     const TileDesc t = a.tiles[tile_id];
-    if (MODE == kServer) load_worker_scales(a, t.chunk, s_wscale);
     float c[kPerThread];
-    tile_compute_c<MODE, GBF16>(a, t, c, s_wscale);
+    tile_compute_c<MODE, GBF16>(a, t, c, s_wscale_d, s_words);
     tile_store_bits(a, t, c);
     tile_store_c(a, t, c);
     const double part = tile_sum_squares(c, s_red);
@@ -765,6 +796,7 @@ extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const
     a.wbits = worker_bits;
     a.wscales = worker_scales;
     a.W = W;
+    a.w_pow2_scale = (W & (W - 1)) == 0 ? 1.0 / (double)W : 0.0;
     a.plan_words = plan->words;
     a.n_chunks = plan->n_chunks;
     a.m_out = m_out;

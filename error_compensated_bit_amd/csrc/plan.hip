@@ -116,11 +116,22 @@ extern "C" void onebit_plan_destroy(onebit_plan_t p) {
     delete p;
 }
 
-extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int64_t n_chunks,
-                                              const int64_t *tensor_offsets, const uint8_t *tensor_keep,
-                                              int64_t n_tensors, onebit_plan_t *out) {
-    if (!out) return ONEBIT_ERR_INVALID;
-    *out = nullptr;
+namespace onebit {
+
+// Host tables of a plan: merged masked intervals, per-chunk and per-tile
+// descriptors.  Pure host code (no device is touched).
+struct HostTables {
+    std::vector<int64_t> iv;  // [a, b) pairs of masked elements, sorted, disjoint, non-adjacent
+    std::vector<TileDesc> tiles;
+    std::vector<ChunkDesc> chunks;
+    int64_t n = 0;
+    int64_t words = 0;
+    int32_t max_chunk_tiles = 0;
+    bool aligned = true;
+};
+
+static onebit_status_t build_tables(const int64_t *chunk_offsets, int64_t n_chunks, const int64_t *tensor_offsets,
+                                    const uint8_t *tensor_keep, int64_t n_tensors, HostTables &T) {
     if (!offsets_ok(chunk_offsets, n_chunks)) return ONEBIT_ERR_INVALID;
     const int64_t n = chunk_offsets[n_chunks];
     if (tensor_offsets) {
@@ -129,6 +140,96 @@ extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int6
         return ONEBIT_ERR_INVALID;
     }
     if (n_chunks > (1ll << 30)) return ONEBIT_ERR_UNSUPPORTED;
+    T.n = n;
+
+    // masked intervals: runs of consecutive masked, non-empty tensors
+    if (tensor_offsets && tensor_keep) {
+        for (int64_t t = 0; t < n_tensors; ++t) {
+            const int64_t a = tensor_offsets[t], b = tensor_offsets[t + 1];
+            if (tensor_keep[t] || a == b) continue;
+            if (!T.iv.empty() && T.iv.back() == a)
+                T.iv.back() = b;
+            else {
+                T.iv.push_back(a);
+                T.iv.push_back(b);
+            }
+        }
+    }
+    const size_t n_iv = T.iv.size() / 2;
+
+    T.chunks.resize((size_t)n_chunks);
+    int64_t word = 0;
+    size_t ivp = 0;  // first interval that may still touch the current tile
+    for (int64_t j = 0; j < n_chunks; ++j) {
+        const int64_t o = chunk_offsets[j], len = chunk_offsets[j + 1] - o;
+        if (o % 4 != 0) T.aligned = false;
+        const int64_t nt = len > 0 ? (len + kTile - 1) / kTile : 1;
+        if ((int64_t)T.tiles.size() + nt > (1ll << 31) - 1) return ONEBIT_ERR_UNSUPPORTED;
+        T.chunks[j] = ChunkDesc{len, (int32_t)T.tiles.size(), (int32_t)nt};
+        if (nt > T.max_chunk_tiles) T.max_chunk_tiles = (int32_t)nt;
+        for (int64_t k = 0; k < nt; ++k) {
+            TileDesc t{};
+            t.start = o + k * kTile;
+            t.len = (int32_t)std::max<int64_t>(0, std::min<int64_t>(kTile, len - k * kTile));
+            t.word = word + k * (kTile / 32);
+            t.chunk = (int32_t)j;
+            const int64_t lo = t.start, hi = t.start + t.len;
+            while (ivp < n_iv && T.iv[2 * ivp + 1] <= lo) ++ivp;
+            size_t q = ivp;
+            while (q < n_iv && T.iv[2 * q] < hi) ++q;
+            t.mask_lo = (int32_t)ivp;
+            t.mask_hi = (int32_t)q;
+            if (t.len == 0) {
+                t.mask_lo = t.mask_hi = 0;
+            } else if (q == ivp + 1 && T.iv[2 * ivp] <= lo && T.iv[2 * ivp + 1] >= hi) {
+                t.mask_lo = -1;  // one interval covers the whole tile
+                t.mask_hi = 0;
+            }
+            T.tiles.push_back(t);
+        }
+        word += (len + 31) / 32;
+    }
+    T.words = word;
+    return ONEBIT_OK;
+}
+
+}  // namespace onebit
+
+extern "C" onebit_status_t onebit_plan_host_tables(const int64_t *chunk_offsets, int64_t n_chunks,
+                                                   const int64_t *tensor_offsets, const uint8_t *tensor_keep,
+                                                   int64_t n_tensors, int64_t *n_tiles, int64_t *n_words,
+                                                   int64_t *out_tiles, int64_t *n_mask_iv, int64_t *out_mask_iv) {
+    HostTables T;
+    const onebit_status_t st = build_tables(chunk_offsets, n_chunks, tensor_offsets, tensor_keep, n_tensors, T);
+    if (st != ONEBIT_OK) return st;
+    if (n_tiles) *n_tiles = (int64_t)T.tiles.size();
+    if (n_words) *n_words = T.words;
+    if (n_mask_iv) *n_mask_iv = (int64_t)T.iv.size() / 2;
+    if (out_tiles) {
+        for (size_t i = 0; i < T.tiles.size(); ++i) {
+            const TileDesc &t = T.tiles[i];
+            int64_t *r = out_tiles + 6 * i;
+            r[0] = t.start;
+            r[1] = t.word;
+            r[2] = t.len;
+            r[3] = t.chunk;
+            r[4] = t.mask_lo;
+            r[5] = t.mask_hi;
+        }
+    }
+    if (out_mask_iv)
+        for (size_t i = 0; i < T.iv.size(); ++i) out_mask_iv[i] = T.iv[i];
+    return ONEBIT_OK;
+}
+
+extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int64_t n_chunks,
+                                              const int64_t *tensor_offsets, const uint8_t *tensor_keep,
+                                              int64_t n_tensors, onebit_plan_t *out) {
+    if (!out) return ONEBIT_ERR_INVALID;
+    *out = nullptr;
+    HostTables T;
+    const onebit_status_t st = build_tables(chunk_offsets, n_chunks, tensor_offsets, tensor_keep, n_tensors, T);
+    if (st != ONEBIT_OK) return st;
 
     onebit_plan_s *p = new (std::nothrow) onebit_plan_s();
     if (!p) return ONEBIT_ERR_NOMEM;
@@ -136,63 +237,13 @@ extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int6
         delete p;
         return ONEBIT_ERR_HIP;
     }
-    p->n = n;
+    p->n = T.n;
     p->n_chunks = n_chunks;
-
-    // masked intervals: runs of consecutive masked, non-empty tensors
-    std::vector<int64_t> iv;
-    if (tensor_offsets && tensor_keep) {
-        for (int64_t t = 0; t < n_tensors; ++t) {
-            const int64_t a = tensor_offsets[t], b = tensor_offsets[t + 1];
-            if (tensor_keep[t] || a == b) continue;
-            if (!iv.empty() && iv.back() == a)
-                iv.back() = b;
-            else {
-                iv.push_back(a);
-                iv.push_back(b);
-            }
-        }
-    }
-    p->n_mask_iv = (int64_t)iv.size() / 2;
-
-    std::vector<TileDesc> tiles;
-    std::vector<ChunkDesc> chunks((size_t)n_chunks);
-    int64_t word = 0;
-    size_t ivp = 0;  // first interval that may still touch the current tile
-    for (int64_t j = 0; j < n_chunks; ++j) {
-        const int64_t o = chunk_offsets[j], len = chunk_offsets[j + 1] - o;
-        if (o % 4 != 0) p->aligned = false;
-        const int64_t nt = len > 0 ? (len + kTile - 1) / kTile : 1;
-        if ((int64_t)tiles.size() + nt > (1ll << 31) - 1) {
-            delete p;
-            return ONEBIT_ERR_UNSUPPORTED;
-        }
-        chunks[j] = ChunkDesc{len, (int32_t)tiles.size(), (int32_t)nt};
-        if (nt > p->max_chunk_tiles) p->max_chunk_tiles = (int32_t)nt;
-        for (int64_t k = 0; k < nt; ++k) {
-            TileDesc t{};
-            t.start = o + k * kTile;
-            t.len = (int32_t)std::min<int64_t>(kTile, len - k * kTile);
-            if (t.len < 0) t.len = 0;
-            t.word = word + k * (kTile / 32);
-            t.chunk = (int32_t)j;
-            const int64_t lo = t.start, hi = t.start + t.len;
-            while (ivp < iv.size() / 2 && iv[2 * ivp + 1] <= lo) ++ivp;
-            size_t q = ivp;
-            while (q < iv.size() / 2 && iv[2 * q] < hi) ++q;
-            t.mask_lo = (int32_t)ivp;
-            t.mask_hi = (int32_t)q;
-            if (q == ivp + 1 && iv[2 * ivp] <= lo && iv[2 * ivp + 1] >= hi && t.len > 0) {
-                t.mask_lo = -1;  // one interval covers the whole tile
-                t.mask_hi = 0;
-            }
-            if (t.len == 0) t.mask_lo = t.mask_hi = 0;
-            tiles.push_back(t);
-        }
-        word += (len + 31) / 32;
-    }
-    p->n_tiles = (int64_t)tiles.size();
-    p->words = word;
+    p->n_mask_iv = (int64_t)T.iv.size() / 2;
+    p->n_tiles = (int64_t)T.tiles.size();
+    p->words = T.words;
+    p->aligned = T.aligned;
+    p->max_chunk_tiles = T.max_chunk_tiles;
 
     // one-pass chunks (at most coop_depth() times the resident workgroups: the
     // one-pass kernel keeps that many tiles in flight per workgroup) and two-pass
@@ -200,7 +251,7 @@ extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int6
     p->coop_capacity = coop_capacity(p->device);
     std::vector<int32_t> coop, big, big_chunks;
     for (int64_t j = 0; j < n_chunks; ++j) {
-        const ChunkDesc &c = chunks[j];
+        const ChunkDesc &c = T.chunks[j];
         const bool one_pass = (int64_t)c.ntiles <= (int64_t)coop_depth() * (int64_t)p->coop_capacity;
         std::vector<int32_t> &dst = one_pass ? coop : big;
         for (int32_t k = 0; k < c.ntiles; ++k) dst.push_back(c.first_tile + k);
@@ -210,9 +261,9 @@ extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int6
     p->n_big = (int32_t)big.size();
     p->n_big_chunks = (int32_t)big_chunks.size();
 
-    hipError_t e = upload(&p->d_tiles, tiles);
-    if (e == hipSuccess) e = upload(&p->d_chunks, chunks);
-    if (e == hipSuccess) e = upload(&p->d_mask_iv, iv);
+    hipError_t e = upload(&p->d_tiles, T.tiles);
+    if (e == hipSuccess) e = upload(&p->d_chunks, T.chunks);
+    if (e == hipSuccess) e = upload(&p->d_mask_iv, T.iv);
     if (e == hipSuccess) e = upload(&p->d_coop_list, coop);
     if (e == hipSuccess) e = upload(&p->d_big_list, big);
     if (e == hipSuccess) e = upload(&p->d_big_chunks, big_chunks);

@@ -143,6 +143,175 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize(QArgs a) {
     }
 }
 
+// Buckets of exactly 1024 elements (the common configuration): one wave per
+// bucket, lane l owns the 16 consecutive elements 16l..16l+15, loaded as two
+// 16-byte vectors and kept in registers across the min/max and code passes;
+// four Philox calls per lane; codes leave as one 8- or 16-byte store.
+__device__ __forceinline__ void unpack8(uint4 h, float (&f)[8]) {
+    f[0] = bf16_bits_to_float(h.x & 0xffffu); f[1] = bf16_bits_to_float(h.x >> 16);
+    f[2] = bf16_bits_to_float(h.y & 0xffffu); f[3] = bf16_bits_to_float(h.y >> 16);
+    f[4] = bf16_bits_to_float(h.z & 0xffffu); f[5] = bf16_bits_to_float(h.z >> 16);
+    f[6] = bf16_bits_to_float(h.w & 0xffffu); f[7] = bf16_bits_to_float(h.w >> 16);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    constexpr float L = (float)((1 << BITS) - 1);
+    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+        const int64_t base = b * 1024;
+        const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
+        const int k0 = 16 * lane;
+        float f[16];
+        if (k0 + 15 < len) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + base + k0);
+            float lo[8], hi[8];
+            unpack8(src[0], lo);
+            unpack8(src[1], hi);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                f[q] = lo[q];
+                f[8 + q] = hi[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) f[q] = (k0 + q < len) ? bf16_bits_to_float(a.x[base + k0 + q]) : 0.0f;
+        }
+        int32_t kmin = 0x7fffffff, kmax = (int32_t)0x80000000;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            if (k0 + q < len) {
+                kmin = min(kmin, order_key(f[q]));
+                kmax = max(kmax, order_key(f[q]));
+            }
+        }
+        kmin = wave_min_i(kmin);
+        kmax = wave_max_i(kmax);
+        const float mn = key_to_float(kmin), mx = key_to_float(kmax);
+        const float delta = __fdiv_rn(sub_rn(mx, mn), L);
+        if (lane == 0) {
+            a.bmin[b] = mn;
+            a.bmax[b] = mx;
+        }
+        uint32_t code[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint64_t blk = (uint64_t)(base + k0 + 4 * g) >> 2;
+            const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
+            code[4 * g + 0] = sr_code<BITS>(f[4 * g + 0], mn, delta, r.a);
+            code[4 * g + 1] = sr_code<BITS>(f[4 * g + 1], mn, delta, r.b);
+            code[4 * g + 2] = sr_code<BITS>(f[4 * g + 2], mn, delta, r.c);
+            code[4 * g + 3] = sr_code<BITS>(f[4 * g + 3], mn, delta, r.d);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (k0 + q >= len) code[q] = 0;
+        if (BITS == 4) {
+            uint2 pk;
+            pk.x = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12) | (code[4] << 16) | (code[5] << 20) |
+                   (code[6] << 24) | (code[7] << 28);
+            pk.y = code[8] | (code[9] << 4) | (code[10] << 8) | (code[11] << 12) | (code[12] << 16) |
+                   (code[13] << 20) | (code[14] << 24) | (code[15] << 28);
+            uint8_t *dst = a.codes + ((base + k0) >> 1);
+            if (k0 + 15 < len) {
+                *reinterpret_cast<uint2 *>(dst) = pk;
+            } else {
+                for (int q = 0; 2 * q < len - k0; ++q) dst[q] = (uint8_t)(((q < 4 ? pk.x : pk.y) >> (8 * (q & 3))) & 0xffu);
+            }
+        } else {
+            uint4 pk;
+            pk.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            pk.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+            pk.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
+            pk.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
+            uint8_t *dst = a.codes + base + k0;
+            if (k0 + 15 < len) {
+                *reinterpret_cast<uint4 *>(dst) = pk;
+            } else {
+                for (int q = 0; q < len - k0; ++q) dst[q] = (uint8_t)code[q];
+            }
+        }
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_qsdp_dequantize_1024(QArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    constexpr float L = (float)((1 << BITS) - 1);
+    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+        const int64_t base = b * 1024;
+        const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
+        const int k0 = 16 * lane;
+        if (k0 >= len) continue;
+        const float mn = a.in_min[b];
+        const float delta = __fdiv_rn(sub_rn(a.in_max[b], mn), L);
+        uint32_t code[16];
+        const bool full = k0 + 15 < len;
+        if (BITS == 4) {
+            uint2 w = make_uint2(0u, 0u);
+            const uint8_t *src = a.in_codes + ((base + k0) >> 1);
+            if (full) {
+                w = *reinterpret_cast<const uint2 *>(src);
+            } else {
+                for (int q = 0; 2 * q < len - k0; ++q) {
+                    const uint32_t byte = src[q];
+                    if (q < 4) w.x |= byte << (8 * q); else w.y |= byte << (8 * (q - 4));
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                code[q] = (w.x >> (4 * q)) & 15u;
+                code[8 + q] = (w.y >> (4 * q)) & 15u;
+            }
+        } else {
+            uint4 w = make_uint4(0u, 0u, 0u, 0u);
+            const uint8_t *src = a.in_codes + base + k0;
+            if (full) {
+                w = *reinterpret_cast<const uint4 *>(src);
+            } else {
+                uint32_t t[4] = {0u, 0u, 0u, 0u};
+                for (int q = 0; q < len - k0; ++q) t[q >> 2] |= (uint32_t)src[q] << (8 * (q & 3));
+                w = make_uint4(t[0], t[1], t[2], t[3]);
+            }
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int q = 0; q < 16; ++q) code[q] = (ws[q >> 2] >> (8 * (q & 3))) & 255u;
+        }
+        float y[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) y[q] = add_rn(mn, mul_rn((float)code[q], delta));
+        const int64_t i0 = base + k0;
+        if (full) {
+            if (a.out_f32) {
+                float4 *o = reinterpret_cast<float4 *>(a.out_f32 + i0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) o[g] = make_float4(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]);
+            }
+            if (a.out_bf16) {
+                uint4 *o = reinterpret_cast<uint4 *>(a.out_bf16 + i0);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    uint4 pk;
+                    pk.x = float_to_bf16_bits(y[8 * g + 0]) | (float_to_bf16_bits(y[8 * g + 1]) << 16);
+                    pk.y = float_to_bf16_bits(y[8 * g + 2]) | (float_to_bf16_bits(y[8 * g + 3]) << 16);
+                    pk.z = float_to_bf16_bits(y[8 * g + 4]) | (float_to_bf16_bits(y[8 * g + 5]) << 16);
+                    pk.w = float_to_bf16_bits(y[8 * g + 6]) | (float_to_bf16_bits(y[8 * g + 7]) << 16);
+                    o[g] = pk;
+                }
+            }
+        } else {
+            for (int q = 0; q < len - k0; ++q) {
+                if (a.out_f32) a.out_f32[i0 + q] = y[q];
+                if (a.out_bf16) a.out_bf16[i0 + q] = (uint16_t)float_to_bf16_bits(y[q]);
+            }
+        }
+    }
+}
+
 // Generic bucket size (not a multiple of 4): one Philox call per element.
 template <int BITS>
 __global__ __launch_bounds__(256) void k_qsdp_quantize_generic(QArgs a) {
@@ -315,7 +484,7 @@ extern "C" onebit_status_t qsdp_quantize(const uint16_t *x_bf16, int64_t n, int 
     if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
     if (n == 0) return ONEBIT_OK;
     if (!x_bf16 || !codes || !bucket_min || !bucket_max) return ONEBIT_ERR_INVALID;
-    if (!aligned16(x_bf16) || !aligned_to(codes, 4) || !aligned_to(bucket_min, 4) || !aligned_to(bucket_max, 4))
+    if (!aligned16(x_bf16) || !aligned16(codes) || !aligned_to(bucket_min, 4) || !aligned_to(bucket_max, 4))
         return ONEBIT_ERR_ALIGN;
     QArgs a{};
     a.x = x_bf16;
@@ -332,7 +501,11 @@ extern "C" onebit_status_t qsdp_quantize(const uint16_t *x_bf16, int64_t n, int 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool fast = (bucket & 3) == 0;
     prof_before(kProfQuantize, s);
-    if (bits == 4 && fast)
+    if (bucket == 1024 && bits == 4)
+        hipLaunchKernelGGL(k_qsdp_quantize_1024<4>, dim3(grid), dim3(256), 0, s, a);
+    else if (bucket == 1024)
+        hipLaunchKernelGGL(k_qsdp_quantize_1024<8>, dim3(grid), dim3(256), 0, s, a);
+    else if (bits == 4 && fast)
         hipLaunchKernelGGL(k_qsdp_quantize<4>, dim3(grid), dim3(256), 0, s, a);
     else if (bits == 4)
         hipLaunchKernelGGL(k_qsdp_quantize_generic<4>, dim3(grid), dim3(256), 0, s, a);
@@ -351,7 +524,7 @@ extern "C" onebit_status_t qsdp_dequantize(const uint8_t *codes, const float *bu
     if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
     if (n == 0) return ONEBIT_OK;
     if (!codes || !bucket_min || !bucket_max) return ONEBIT_ERR_INVALID;
-    if (!aligned_to(codes, 4) || !aligned_to(bucket_min, 4) || !aligned_to(bucket_max, 4)) return ONEBIT_ERR_ALIGN;
+    if (!aligned16(codes) || !aligned_to(bucket_min, 4) || !aligned_to(bucket_max, 4)) return ONEBIT_ERR_ALIGN;
     if ((out_bf16 && !aligned16(out_bf16)) || (out_f32 && !aligned16(out_f32))) return ONEBIT_ERR_ALIGN;
     QArgs a{};
     a.n = n;
@@ -366,7 +539,11 @@ extern "C" onebit_status_t qsdp_dequantize(const uint8_t *codes, const float *bu
     const unsigned grid = grid_for(a.n_buckets);
     hipStream_t s = static_cast<hipStream_t>(stream);
     prof_before(kProfDequantize, s);
-    if (bits == 4)
+    if (bucket == 1024 && bits == 4)
+        hipLaunchKernelGGL(k_qsdp_dequantize_1024<4>, dim3(grid), dim3(256), 0, s, a);
+    else if (bucket == 1024)
+        hipLaunchKernelGGL(k_qsdp_dequantize_1024<8>, dim3(grid), dim3(256), 0, s, a);
+    else if (bits == 4)
         hipLaunchKernelGGL(k_qsdp_dequantize<4>, dim3(grid), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(k_qsdp_dequantize<8>, dim3(grid), dim3(256), 0, s, a);

@@ -29,32 +29,54 @@ __device__ __forceinline__ void warm_one(const WarmupArgs &a, float g, float &x,
 }
 
 template <bool GBF16>
+__device__ __forceinline__ void load_g4w(const void *g, int64_t i, float (&gg)[4]) {
+    if (GBF16) {
+        const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + i);
+        gg[0] = bf16_bits_to_float(h.x & 0xffffu);
+        gg[1] = bf16_bits_to_float(h.x >> 16);
+        gg[2] = bf16_bits_to_float(h.y & 0xffffu);
+        gg[3] = bf16_bits_to_float(h.y >> 16);
+    } else {
+        const float4 h = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + i);
+        gg[0] = h.x; gg[1] = h.y; gg[2] = h.z; gg[3] = h.w;
+    }
+}
+
+// Each thread takes kWU groups of four elements per iteration (all loads of an
+// iteration in flight together), grid-stride over the vector.
+constexpr int kWU = 2;
+
+template <bool GBF16>
 __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
     const int64_t groups = a.n / 4;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < groups; q += stride) {
-        const int64_t i = 4 * q;
-        float gg[4];
-        if (GBF16) {
-            const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.g) + i);
-            gg[0] = bf16_bits_to_float(h.x & 0xffffu);
-            gg[1] = bf16_bits_to_float(h.x >> 16);
-            gg[2] = bf16_bits_to_float(h.y & 0xffffu);
-            gg[3] = bf16_bits_to_float(h.y >> 16);
-        } else {
-            const float4 h = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + i);
-            gg[0] = h.x; gg[1] = h.y; gg[2] = h.z; gg[3] = h.w;
+    const int64_t span = (int64_t)blockDim.x * kWU;
+    for (int64_t base = blockIdx.x * span; base < groups; base += (int64_t)gridDim.x * span) {
+        float gg[kWU][4];
+        float4 xx[kWU], mm[kWU], vv[kWU];
+        bool in[kWU];
+#pragma unroll
+        for (int u = 0; u < kWU; ++u) {
+            const int64_t q = base + u * (int64_t)blockDim.x + threadIdx.x;
+            in[u] = q < groups;
+            if (in[u]) {
+                load_g4w<GBF16>(a.g, 4 * q, gg[u]);
+                xx[u] = *reinterpret_cast<const float4 *>(a.x + 4 * q);
+                mm[u] = *reinterpret_cast<const float4 *>(a.m + 4 * q);
+                vv[u] = *reinterpret_cast<const float4 *>(a.v + 4 * q);
+            }
         }
-        float4 xx = *reinterpret_cast<const float4 *>(a.x + i);
-        float4 mm = *reinterpret_cast<const float4 *>(a.m + i);
-        float4 vv = *reinterpret_cast<const float4 *>(a.v + i);
-        warm_one<GBF16>(a, gg[0], xx.x, mm.x, vv.x);
-        warm_one<GBF16>(a, gg[1], xx.y, mm.y, vv.y);
-        warm_one<GBF16>(a, gg[2], xx.z, mm.z, vv.z);
-        warm_one<GBF16>(a, gg[3], xx.w, mm.w, vv.w);
-        *reinterpret_cast<float4 *>(a.x + i) = xx;
-        *reinterpret_cast<float4 *>(a.m + i) = mm;
-        *reinterpret_cast<float4 *>(a.v + i) = vv;
+#pragma unroll
+        for (int u = 0; u < kWU; ++u) {
+            if (!in[u]) continue;
+            const int64_t q = base + u * (int64_t)blockDim.x + threadIdx.x;
+            warm_one<GBF16>(a, gg[u][0], xx[u].x, mm[u].x, vv[u].x);
+            warm_one<GBF16>(a, gg[u][1], xx[u].y, mm[u].y, vv[u].y);
+            warm_one<GBF16>(a, gg[u][2], xx[u].z, mm[u].z, vv[u].z);
+            warm_one<GBF16>(a, gg[u][3], xx[u].w, mm[u].w, vv[u].w);
+            *reinterpret_cast<float4 *>(a.x + 4 * q) = xx[u];
+            *reinterpret_cast<float4 *>(a.m + 4 * q) = mm[u];
+            *reinterpret_cast<float4 *>(a.v + 4 * q) = vv[u];
+        }
     }
     // ragged tail (n % 4 elements), one thread each
     const int64_t tail = a.n - 4 * groups;
@@ -106,8 +128,8 @@ extern "C" onebit_status_t onebit_adam_warmup_step(float *x, float *m, float *v,
             cus = v_cus;
     }
     const int64_t groups = n / 4;
-    int64_t blocks = (groups + 255) / 256;
-    const int64_t cap = (int64_t)cus * 16;  // enough resident waves to cover HBM latency
+    int64_t blocks = (groups + 256 * kWU - 1) / (256 * kWU);
+    const int64_t cap = (int64_t)cus * 8;  // resident waves enough to cover HBM latency
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -25,6 +25,7 @@ _SIGS = {
     "onebit_status_string": (C.c_char_p, [_I]),
     "onebit_plan_create": (_I, [_P, _I64, _P, _P, _I64, C.POINTER(_P)]),
     "onebit_plan_destroy": (None, [_P]),
+    "onebit_plan_host_tables": (_I, [_P, _I64, _P, _P, _I64, _P, _P, _P, _P, _P]),
     "onebit_plan_elements": (_I64, [_P]),
     "onebit_plan_chunks": (_I64, [_P]),
     "onebit_plan_words": (_I64, [_P]),
@@ -139,6 +140,25 @@ def onebit_plan_create(chunk_offsets, tensor_offsets=None, tensor_keep=None) -> 
                                   None if tk is None else tk.ctypes.data, n_tensors, C.byref(out)),
            "onebit_plan_create")
     return Plan(out.value)
+
+
+def onebit_plan_host_tables(chunk_offsets, tensor_offsets=None, tensor_keep=None):
+    """Host-only plan tables: (tiles int64[n_tiles, 6], words, masked intervals int64[k, 2])."""
+    lib = load()
+    co = np.ascontiguousarray(chunk_offsets, dtype=np.int64)
+    to = None if tensor_offsets is None else np.ascontiguousarray(tensor_offsets, dtype=np.int64)
+    tk = None if tensor_keep is None else np.ascontiguousarray(tensor_keep, dtype=np.uint8)
+    n_t = 0 if to is None else to.size - 1
+    nt, nw, ni = C.c_int64(), C.c_int64(), C.c_int64()
+    args = (co.ctypes.data, co.size - 1, None if to is None else to.ctypes.data,
+            None if tk is None else tk.ctypes.data, n_t)
+    _check(lib.onebit_plan_host_tables(*args, C.byref(nt), C.byref(nw), None, C.byref(ni), None),
+           "onebit_plan_host_tables")
+    tiles = np.zeros((nt.value, 6), dtype=np.int64)
+    iv = np.zeros((ni.value, 2), dtype=np.int64)
+    _check(lib.onebit_plan_host_tables(*args, None, None, tiles.ctypes.data, None, iv.ctypes.data),
+           "onebit_plan_host_tables")
+    return tiles, int(nw.value), iv
 
 
 def onebit_plan_destroy(plan: Plan):

@@ -21,8 +21,8 @@
  * Conventions for every call:
  *  - Every data pointer is a DEVICE pointer owned by the caller unless marked
  *    (host).  Per-element arrays (x, m, v, e, g, x_bf16, server_error, m_out and
- *    the QSDP weights and outputs) must be 16-byte aligned; packed words, scales,
- *    codes and bucket min/max 4-byte aligned; the workspace 8-byte aligned
+ *    the QSDP weights, codes and outputs) must be 16-byte aligned; packed words,
+ *    scales and bucket min/max 4-byte aligned; the workspace 8-byte aligned
  *    (ONEBIT_ERR_ALIGN otherwise).  Chunk offsets inside the arrays may be
  *    arbitrary.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
@@ -81,6 +81,19 @@ onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int64_t n_chunk
                                    const int64_t *tensor_offsets, const uint8_t *tensor_keep,
                                    int64_t n_tensors, onebit_plan_t *out);
 void onebit_plan_destroy(onebit_plan_t plan);
+
+/* Host only (touches no device): the tables onebit_plan_create would build, for
+ * inspection and host-side tests.  Same validation and status codes.  Outputs are
+ * host arrays and nullable: *n_tiles, *n_words, *n_mask_iv; out_tiles
+ * [n_tiles][6] = {first element, first packed word, length (0..2048), chunk,
+ * mask_lo, mask_hi}, where masked intervals [mask_lo, mask_hi) touch the tile and
+ * mask_lo = -1 means one masked interval covers it; out_mask_iv [n_mask_iv][2] =
+ * merged masked element ranges [a, b).  Tiles are 2048 elements, each chunk cut
+ * from its start (an empty chunk gets one empty tile). */
+onebit_status_t onebit_plan_host_tables(const int64_t *chunk_offsets, int64_t n_chunks,
+                                        const int64_t *tensor_offsets, const uint8_t *tensor_keep,
+                                        int64_t n_tensors, int64_t *n_tiles, int64_t *n_words,
+                                        int64_t *out_tiles, int64_t *n_mask_iv, int64_t *out_mask_iv);
 int64_t onebit_plan_elements(onebit_plan_t plan); /* n */
 int64_t onebit_plan_chunks(onebit_plan_t plan);   /* n_chunks */
 int64_t onebit_plan_words(onebit_plan_t plan);    /* sum_j ceil(n_j / 32) */
