@@ -42,6 +42,8 @@ B_COMPRESS_F32 = 32.125      # read g,m,e,v,x (20 B); write m,e,x (12 B); bits (
 B_COMPRESS_BF16_COPY = 32.125  # read g bf16 (2),m,e,v,x (16); write m,e,x (12), x_bf16 (2); bits
 B_WARMUP = 28.0              # read g,m,v,x; write m,v,x
 B_WORKER = 16.125            # read g,m,e; write e; bits
+B_WORKER_F16 = 14.125        # read g fp16 (2), m, e; write e; bits
+B_FINISH_MASK = 21.0         # read m, mask (1), v, x; write m, x
 B_QSDP4, B_QSDP8 = 2.0 + 0.5 + 8.0 / 1024, 2.0 + 1.0 + 8.0 / 1024
 
 
@@ -134,37 +136,40 @@ def bench_compress(wl, steps, warmup, dev, bpe):
 
 
 def cpu_baseline(wl, dev, budget_s=12.0):
-    """Time the CPU oracle on whole chunks of the workload until about budget_s of work."""
+    """Time the CPU oracle on whole chunks of the workload (successive compressed
+    steps over the vector, chunk by chunk) until about budget_s of CPU work."""
     import numpy as np
     import oracle
     from error_compensated_bit_amd import workloads as W
-    state = W.init_state(wl, device=dev)
-    gd = W.gradient(wl, 1, device=dev)
-    gd = gd.float() if wl.grad_bf16 else gd
+    state = [t.cpu().numpy() for t in W.init_state(wl, device=dev)]       # x, m, e, v
+    g = W.gradient(wl, 1, device=dev)
+    g = (g.float() if wl.grad_bf16 else g).cpu().numpy()
     done = 0
     spent = 0.0
-    chunks = []
-    order = np.random.default_rng(0).permutation(wl.n_chunks)
-    for j in order:
-        lo, hi = int(wl.chunk_off[j]), int(wl.chunk_off[j + 1])
-        off = np.array([0, hi - lo], np.int64)
-        keep_el = None
-        if wl.tensor_keep is not None:
-            t = int(np.searchsorted(wl.tensor_off, lo, side="right") - 1)
-            keep_el = (np.array([0, hi - lo], np.int64), wl.tensor_keep[t:t + 1])
-        x, m, e, v = (t[lo:hi].cpu().numpy() for t in state)
-        args = [gd[lo:hi].cpu().numpy(), m, e, v, x]
-        t0 = time.perf_counter()
-        oracle.compress_update(off, *args, tensor_off=keep_el[0] if keep_el else None,
-                               tensor_keep=keep_el[1] if keep_el else None, lr=1e-3, beta1=0.9, eps=1e-8)
-        spent += time.perf_counter() - t0
-        done += hi - lo
-        chunks.append(int(j))
-        if spent >= budget_s:
-            break
+    calls = 0
+    steps = 0
+    while spent < budget_s:
+        steps += 1
+        for j in range(wl.n_chunks):
+            lo, hi = int(wl.chunk_off[j]), int(wl.chunk_off[j + 1])
+            off = np.array([0, hi - lo], np.int64)
+            t_off = t_keep = None
+            if wl.tensor_keep is not None:
+                t = int(np.searchsorted(wl.tensor_off, lo, side="right") - 1)
+                t_off, t_keep = np.array([0, hi - lo], np.int64), wl.tensor_keep[t:t + 1]
+            x, m, e, v = (a[lo:hi] for a in state)
+            gj = g[lo:hi]
+            t0 = time.perf_counter()
+            oracle.compress_update(off, gj, m, e, v, x, tensor_off=t_off, tensor_keep=t_keep, lr=1e-3, beta1=0.9,
+                                   eps=1e-8)
+            spent += time.perf_counter() - t0
+            done += hi - lo
+            calls += 1
+            if spent >= budget_s:
+                break
     return dict(value=done / spent, unit="params/s", cores=1, kind="oracle",
-                sample=f"{len(chunks)} whole chunks ({done} params, {100.0 * done / wl.n:.1f}% of the vector) "
-                       f"of the same workload, one compressed step each, single-threaded C oracle",
+                sample=f"{calls} whole-chunk calls over {steps} compressed step(s) of the same workload "
+                       f"({done} params), single-threaded C oracle, in place on host copies",
                 seconds=spent)
 
 
@@ -429,9 +434,31 @@ def secondary_rows(dev, args):
                                     worker_kernel_gbps=B_WORKER * a.n / (w_ms * 1e-3) / 1e9,
                                     server_kernel_gbps=14.125 * a.n / (s_ms * 1e-3) / 1e9,
                                     server_kernel_ms=s_ms, worker_kernel_ms=w_ms)
-    del m, e, es, grads, wbits, wsc, sbits, ssc, wsp, plan
+    # the same exchange as a full step: fp16 gradients, the server's result masked
+    # per element into the momentum, frozen-v update of x
+    g16 = grads.to(torch.float16)
+    del grads
+    v = torch.rand(a.n, device=dev) * 1e-6 + 1e-7
+    x = torch.randn(a.n, device=dev) * 0.02
+    mask = (torch.rand(a.n, device=dev) < 0.98).to(torch.uint8)
+
+    def full_step():
+        for w in range(a.W):
+            ob.onebit_compress_update(plan, g16[w], m, e[w], None, None, None, wbits[w], wsc[w], lr=0.0,
+                                      beta1=0.9, eps=1e-8, weight_decay=0.0, workspace=wsp)
+        ob.onebit_server_reduce(plan, wbits, wsc, es, sbits, ssc, m, wsp)
+        ob.onebit_momentum_update(m, mask, v, x, None, lr=1e-3, eps=1e-8, weight_decay=0.01)
+    t, kt = timed(full_step, steps, 1)
+    f_ms = kt.mean_ms("momentum_update")
+    step_bytes = (B_WORKER_F16 * a.W + 14.125 + B_FINISH_MASK) * a.n
+    rows["full_step_16x64M_f16_mask"] = dict(ms_per_step=t * 1e3, gbps=step_bytes / t / 1e9,
+                                             worker_kernel_gbps=B_WORKER_F16 * a.n /
+                                             (kt.mean_ms("compress_onepass") * 1e-3) / 1e9,
+                                             finish_kernel_gbps=B_FINISH_MASK * a.n / (f_ms * 1e-3) / 1e9,
+                                             finish_kernel_ms=f_ms)
+    del m, e, es, g16, v, x, mask, wbits, wsc, sbits, ssc, wsp, plan
     torch.cuda.empty_cache()
-    log(f"[bench] allreduce {rows['allreduce_16x64M']}")
+    log(f"[bench] allreduce {rows['allreduce_16x64M']} full step {rows['full_step_16x64M_f16_mask']}")
 
     # GPT-2-XL-shaped vector, bf16 gradients, bf16 copy of x
     wl = W.gpt2_like()

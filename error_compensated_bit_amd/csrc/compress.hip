@@ -84,14 +84,14 @@ __device__ __forceinline__ bool tile_full(const CompressArgs &a, const TileDesc 
 }
 __device__ __forceinline__ uint32_t lane_k0(int r) { return 4u * (threadIdx.x + kBlock * r); }
 
-template <bool GBF16>
+template <int GT>
 __device__ __forceinline__ void load_g4(const void *g, int64_t start, uint32_t k0, float (&g4)[4]) {
-    if (GBF16) {
+    if (GT != kGradF32) {
         const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + start + k0);
-        g4[0] = bf16_bits_to_float(h.x & 0xffffu);
-        g4[1] = bf16_bits_to_float(h.x >> 16);
-        g4[2] = bf16_bits_to_float(h.y & 0xffffu);
-        g4[3] = bf16_bits_to_float(h.y >> 16);
+        g4[0] = half_bits_to_float<GT>(h.x & 0xffffu);
+        g4[1] = half_bits_to_float<GT>(h.x >> 16);
+        g4[2] = half_bits_to_float<GT>(h.y & 0xffffu);
+        g4[3] = half_bits_to_float<GT>(h.y >> 16);
     } else {
         const float4 h = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + start + k0);
         g4[0] = h.x; g4[1] = h.y; g4[2] = h.z; g4[3] = h.w;
@@ -165,7 +165,7 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
     }
 }
 
-template <int MODE, bool GBF16>
+template <int MODE, int GT>
 __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const TileDesc &t,
                                                float (&c)[kPerThread], double *s_wscale_d,
                                                uint32_t *s_words) {
@@ -178,7 +178,7 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
             const uint32_t k0 = lane_k0(r);
             float g4[4], m4[4], e4[4];
             if (full) {
-                load_g4<GBF16>(a.g, t.start, k0, g4);
+                load_g4<GT>(a.g, t.start, k0, g4);
                 load4(mb, k0, m4);
                 load4(eb, k0, e4);
             } else {
@@ -186,8 +186,8 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
                 for (int q = 0; q < 4; ++q) {
                     const uint32_t k = k0 + q;
                     const bool in = k < (uint32_t)t.len;
-                    g4[q] = in ? (GBF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.g)[t.start + k])
-                                        : static_cast<const float *>(a.g)[t.start + k])
+                    g4[q] = in ? (GT != kGradF32 ? half_bits_to_float<GT>(static_cast<const uint16_t *>(a.g)[t.start + k])
+                                                 : static_cast<const float *>(a.g)[t.start + k])
                                : 0.0f;
                     m4[q] = in ? mb[k] : 0.0f;
                     e4[q] = in ? eb[k] : 0.0f;
@@ -527,18 +527,18 @@ __device__ __forceinline__ void unpark_c(const float4 *s, float (&c)[kPerThread]
 // so the lowest unfinished chunk always completes.
 constexpr int kDepth = 3;
 
-template <int MODE, bool GBF16>
+template <int MODE, int GT>
 __device__ __forceinline__ Posted produce(const CompressArgs &a, int tile_id, const TileDesc &t, float4 *slot_c,
                                           double *s_wscale_d, uint32_t *s_words, DD *s_red, uint32_t *s_u32,
                                           double *s_total) {
     float c[kPerThread];
-    tile_compute_c<MODE, GBF16>(a, t, c, s_wscale_d, s_words);
+    tile_compute_c<MODE, GT>(a, t, c, s_wscale_d, s_words);
     tile_store_bits(a, t, c);
     park_c(slot_c, c);
     return post_tile<true>(a, tile_id, t.chunk, tile_sum_squares(c, s_red), s_red, s_u32, s_total);
 }
 
-template <int MODE, bool GBF16, bool XB>
+template <int MODE, int GT, bool XB>
 __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepass(CompressArgs a) {
     __shared__ float4 s_c[kDepth][kGroups * kBlock];
     __shared__ TileDesc s_tile[kDepth];
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
     for (int i = 0; i < kDepth - 1 && i < mine; ++i) {
         const int id = a.list[b + i * G];
         const TileDesc t = a.tiles[id];
-        const Posted r = produce<MODE, GBF16>(a, id, t, s_c[i], s_wscale_d, s_words, s_red, s_u32, &s_total);
+        const Posted r = produce<MODE, GT>(a, id, t, s_c[i], s_wscale_d, s_words, s_red, s_u32, &s_total);
         if (threadIdx.x == 0) {
             s_tile[i] = t;
             s_post[i] = r;
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
             const int id = a.list[b + ahead * G];
             const TileDesc t = a.tiles[id];
             const int sl = ahead % kDepth;
-            const Posted r = produce<MODE, GBF16>(a, id, t, s_c[sl], s_wscale_d, s_words, s_red, s_u32, &s_total);
+            const Posted r = produce<MODE, GT>(a, id, t, s_c[sl], s_wscale_d, s_words, s_red, s_u32, &s_total);
             if (threadIdx.x == 0) {
                 s_tile[sl] = t;
                 s_post[sl] = r;
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
 // Two passes for chunks too large for the one-pass kernel: pass 1 stores c in
 // place of e, its sign words and its partial; a per-chunk kernel sums the
 // partials; pass 2 finishes from c, v and x.
-template <int MODE, bool GBF16>
+template <int MODE, int GT>
 __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     __shared__ DD s_red[kWaves];
     __shared__ uint32_t s_u32[2];
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     const int tile_id = a.list[blockIdx.x];
     const TileDesc t = a.tiles[tile_id];
     float c[kPerThread];
-    tile_compute_c<MODE, GBF16>(a, t, c, s_wscale_d, s_words);
+    tile_compute_c<MODE, GT>(a, t, c, s_wscale_d, s_words);
     tile_store_bits(a, t, c);
     tile_store_c(a, t, c);
     const double part = tile_sum_squares(c, s_red);
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass2(CompressArgs a) {
 }
 
 // ---------------------------------------------------------- host side
-template <int MODE, bool GBF16, bool XB>
+template <int MODE, int GT, bool XB>
 static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_t stream) {
     const int base = MODE == kServer ? kProfServerPass1 : kProfPass1;
     // Two-pass chunks first, pass 2 right after pass 1 so that the c it re-reads
@@ -635,7 +635,7 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
         a.list = p->d_big_list;
         a.list_len = p->n_big;
         prof_before(base + 0, stream);
-        hipLaunchKernelGGL((k_compress_pass1<MODE, GBF16>), dim3(p->n_big), dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL((k_compress_pass1<MODE, GT>), dim3(p->n_big), dim3(kBlock), 0, stream, a);
         prof_after(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e);
@@ -663,7 +663,7 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
         if (cap <= 0) {
             int per_cu = 0, cus = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, reinterpret_cast<const void *>(&k_compress_onepass<MODE, GBF16, XB>), kBlock, 0) != hipSuccess ||
+                    &per_cu, reinterpret_cast<const void *>(&k_compress_onepass<MODE, GT, XB>), kBlock, 0) != hipSuccess ||
                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
                 return ONEBIT_ERR_HIP;
             cap = per_cu * cus;
@@ -673,7 +673,7 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
         const int grid = p->n_coop < cap ? p->n_coop : cap;
         void *args[] = {&a};
         prof_before(base + 1, stream);
-        hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_compress_onepass<MODE, GBF16, XB>),
+        hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_compress_onepass<MODE, GT, XB>),
                                                   dim3(grid), dim3(kBlock), args, 0, stream);
         prof_after(stream);
         if (e != hipSuccess) {
@@ -699,13 +699,16 @@ int32_t coop_capacity(int device) {
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
     if (!prop.cooperativeLaunch) return 0;
     const void *fns[] = {
-        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, false, false>),
-        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, false, true>),
-        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, true, false>),
-        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, true, true>),
-        reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, false, false>),
-        reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, true, false>),
-        reinterpret_cast<const void *>(&k_compress_onepass<kServer, false, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradF32, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradF32, true>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradBF16, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradBF16, true>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradF16, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradF16, true>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, kGradF32, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, kGradBF16, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, kGradF16, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kServer, kGradF32, false>),
     };
     int per_cu = 1 << 30;
     for (const void *f : fns) {
@@ -727,7 +730,7 @@ extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void
                                                   double beta1, double eps, double weight_decay,
                                                   void *workspace, void *stream) {
     if (!plan) return ONEBIT_ERR_INVALID;
-    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16) return ONEBIT_ERR_INVALID;
+    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
     const bool update = (v != nullptr) || (x != nullptr);
     if (update && (!v || !x)) return ONEBIT_ERR_INVALID;
     if (!update && x_bf16) return ONEBIT_ERR_INVALID;
@@ -765,10 +768,17 @@ extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void
     a.slots = ws.slots;
     a.spin_limit = kSpinLimit;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool bf = g_dtype == ONEBIT_BF16;
-    if (!update) return bf ? launch<kCompressOnly, true, false>(plan, a, s) : launch<kCompressOnly, false, false>(plan, a, s);
-    if (x_bf16) return bf ? launch<kUpdate, true, true>(plan, a, s) : launch<kUpdate, false, true>(plan, a, s);
-    return bf ? launch<kUpdate, true, false>(plan, a, s) : launch<kUpdate, false, false>(plan, a, s);
+    switch (g_dtype) {
+        case ONEBIT_BF16:
+            if (!update) return launch<kCompressOnly, kGradBF16, false>(plan, a, s);
+            return x_bf16 ? launch<kUpdate, kGradBF16, true>(plan, a, s) : launch<kUpdate, kGradBF16, false>(plan, a, s);
+        case ONEBIT_F16:
+            if (!update) return launch<kCompressOnly, kGradF16, false>(plan, a, s);
+            return x_bf16 ? launch<kUpdate, kGradF16, true>(plan, a, s) : launch<kUpdate, kGradF16, false>(plan, a, s);
+        default:
+            if (!update) return launch<kCompressOnly, kGradF32, false>(plan, a, s);
+            return x_bf16 ? launch<kUpdate, kGradF32, true>(plan, a, s) : launch<kUpdate, kGradF32, false>(plan, a, s);
+    }
 }
 
 extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *worker_bits,
@@ -807,5 +817,5 @@ extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const
     a.publish = ws.publish;
     a.slots = ws.slots;
     a.spin_limit = kSpinLimit;
-    return launch<kServer, false, false>(plan, a, static_cast<hipStream_t>(stream));
+    return launch<kServer, kGradF32, false>(plan, a, static_cast<hipStream_t>(stream));
 }

@@ -23,6 +23,16 @@ __device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, 
 __device__ __forceinline__ float sub_rn(float a, float b) { return __fsub_rn(a, b); }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h16) { return __uint_as_float(h16 << 16); }
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);  // exact widening
+}
+
+// Gradient element types: fp32, bf16, fp16 (the 16-bit ones widen exactly).
+enum GradType { kGradF32 = 0, kGradBF16 = 1, kGradF16 = 2 };
+template <int GT>
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+    return GT == kGradBF16 ? bf16_bits_to_float(h16) : f16_bits_to_float(h16);
+}
 
 // binary32 -> bfloat16 bits, nearest-even; NaN kept quiet.
 __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {

@@ -85,7 +85,8 @@ enum ProfClass {
     kProfServerOnepass = 7,
     kProfServerPass2 = 8,
     kProfFinalize = 9,
-    kProfClasses = 10
+    kProfMomentumUpdate = 10,
+    kProfClasses = 11
 };
 void prof_before(int cls, hipStream_t s);
 void prof_after(hipStream_t s);

@@ -1,0 +1,129 @@
+// update.hip -- the worker's finish after the compressed all-reduce (DeepSpeed
+// 1-bit Adam guide, sec. 3.5 and sec. 4, phase two): the all-reduced momentum is
+// multiplied by the per-element exp_avg_mask, then the parameters take the
+// frozen-variance step x -= lr * (m / (sqrt(v) + eps) + weight_decay * x).
+// Streaming; per element 12 bytes read and 4 written (x) without a mask, 13 read
+// and 8 written with one (the masked momentum is stored back), plus 2 written for
+// the optional bf16 copy of x.  Eight elements per thread and iteration: two
+// 128-bit accesses for each fp32 array, one 64-bit mask load, one 128-bit bf16 store.
+#include "device_common.h"
+#include "internal.h"
+
+namespace onebit {
+
+struct UpdateArgs {
+    float *m;
+    const uint8_t *mask;
+    const float *v;
+    float *x;
+    uint16_t *xb;
+    int64_t n;
+    float lr, eps, wd;
+};
+
+__device__ __forceinline__ float finish_one(const UpdateArgs &a, float &m, uint32_t keep, float v, float x) {
+    if (a.mask) m = mul_rn(m, keep ? 1.0f : 0.0f);
+    const float upd = add_rn(m / (sqrtf(v) + a.eps), mul_rn(a.wd, x));
+    return sub_rn(x, mul_rn(a.lr, upd));
+}
+
+template <bool MASK, bool XB>
+__global__ __launch_bounds__(256) void k_momentum_update(UpdateArgs a) {
+    const int64_t groups = a.n / 8;
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < groups;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = 8 * q;
+        float4 m4[2], v4[2], x4[2];
+        uint2 mk = make_uint2(0xffffffffu, 0xffffffffu);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            m4[h] = *reinterpret_cast<const float4 *>(a.m + i + 4 * h);
+            v4[h] = *reinterpret_cast<const float4 *>(a.v + i + 4 * h);
+            x4[h] = *reinterpret_cast<const float4 *>(a.x + i + 4 * h);
+        }
+        if (MASK) mk = *reinterpret_cast<const uint2 *>(a.mask + i);
+        float xn[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t w = h ? mk.y : mk.x;
+            xn[4 * h + 0] = finish_one(a, m4[h].x, w & 0xffu, v4[h].x, x4[h].x);
+            xn[4 * h + 1] = finish_one(a, m4[h].y, (w >> 8) & 0xffu, v4[h].y, x4[h].y);
+            xn[4 * h + 2] = finish_one(a, m4[h].z, (w >> 16) & 0xffu, v4[h].z, x4[h].z);
+            xn[4 * h + 3] = finish_one(a, m4[h].w, w >> 24, v4[h].w, x4[h].w);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (MASK) *reinterpret_cast<float4 *>(a.m + i + 4 * h) = m4[h];
+            *reinterpret_cast<float4 *>(a.x + i + 4 * h) =
+                make_float4(xn[4 * h], xn[4 * h + 1], xn[4 * h + 2], xn[4 * h + 3]);
+        }
+        if (XB) {
+            uint4 pk;
+            pk.x = float_to_bf16_bits(xn[0]) | (float_to_bf16_bits(xn[1]) << 16);
+            pk.y = float_to_bf16_bits(xn[2]) | (float_to_bf16_bits(xn[3]) << 16);
+            pk.z = float_to_bf16_bits(xn[4]) | (float_to_bf16_bits(xn[5]) << 16);
+            pk.w = float_to_bf16_bits(xn[6]) | (float_to_bf16_bits(xn[7]) << 16);
+            *reinterpret_cast<uint4 *>(a.xb + i) = pk;
+        }
+    }
+    // ragged tail (n % 8 elements), one thread each
+    const int64_t tail = a.n - 8 * groups;
+    const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (gid < tail) {
+        const int64_t i = 8 * groups + gid;
+        float m = a.m[i];
+        const float xn = finish_one(a, m, MASK ? a.mask[i] : 1u, a.v[i], a.x[i]);
+        if (MASK) a.m[i] = m;
+        a.x[i] = xn;
+        if (XB) a.xb[i] = (uint16_t)float_to_bf16_bits(xn);
+    }
+}
+
+}  // namespace onebit
+
+using namespace onebit;
+
+extern "C" onebit_status_t onebit_momentum_update(float *m, const uint8_t *mask, const float *v, float *x,
+                                                  uint16_t *x_bf16, int64_t n, double lr, double eps,
+                                                  double weight_decay, void *stream) {
+    if (n < 0) return ONEBIT_ERR_INVALID;
+    if (n == 0) return ONEBIT_OK;
+    if (!m || !v || !x) return ONEBIT_ERR_INVALID;
+    if (!aligned16(m) || !aligned16(v) || !aligned16(x) || (mask && !aligned16(mask)) ||
+        (x_bf16 && !aligned16(x_bf16)))
+        return ONEBIT_ERR_ALIGN;
+    UpdateArgs a{};
+    a.m = m;
+    a.mask = mask;
+    a.v = v;
+    a.x = x;
+    a.xb = x_bf16;
+    a.n = n;
+    a.lr = (float)lr;
+    a.eps = (float)eps;
+    a.wd = (float)weight_decay;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v_cus = 0;
+        if (hipDeviceGetAttribute(&v_cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v_cus > 0)
+            cus = v_cus;
+    }
+    const int64_t groups = n / 8;
+    int64_t blocks = (groups + 255) / 256;
+    const int64_t cap = (int64_t)cus * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)blocks), block(256);
+    prof_before(kProfMomentumUpdate, s);
+    if (mask && x_bf16)
+        hipLaunchKernelGGL((k_momentum_update<true, true>), grid, block, 0, s, a);
+    else if (mask)
+        hipLaunchKernelGGL((k_momentum_update<true, false>), grid, block, 0, s, a);
+    else if (x_bf16)
+        hipLaunchKernelGGL((k_momentum_update<false, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_momentum_update<false, false>), grid, block, 0, s, a);
+    prof_after(s);
+    return hip_status(hipGetLastError());
+}

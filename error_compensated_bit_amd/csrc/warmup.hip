@@ -18,7 +18,7 @@ struct WarmupArgs {
     int bias;
 };
 
-template <bool GBF16>
+template <int GT>
 __device__ __forceinline__ void warm_one(const WarmupArgs &a, float g, float &x, float &m, float &v) {
     m = add_rn(mul_rn(a.b1, m), mul_rn(a.ob1, g));
     v = add_rn(mul_rn(a.b2, v), mul_rn(a.ob2, mul_rn(g, g)));
@@ -28,14 +28,14 @@ __device__ __forceinline__ void warm_one(const WarmupArgs &a, float g, float &x,
     x = x - a.lr * upd;
 }
 
-template <bool GBF16>
+template <int GT>
 __device__ __forceinline__ void load_g4w(const void *g, int64_t i, float (&gg)[4]) {
-    if (GBF16) {
+    if (GT != kGradF32) {
         const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + i);
-        gg[0] = bf16_bits_to_float(h.x & 0xffffu);
-        gg[1] = bf16_bits_to_float(h.x >> 16);
-        gg[2] = bf16_bits_to_float(h.y & 0xffffu);
-        gg[3] = bf16_bits_to_float(h.y >> 16);
+        gg[0] = half_bits_to_float<GT>(h.x & 0xffffu);
+        gg[1] = half_bits_to_float<GT>(h.x >> 16);
+        gg[2] = half_bits_to_float<GT>(h.y & 0xffffu);
+        gg[3] = half_bits_to_float<GT>(h.y >> 16);
     } else {
         const float4 h = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + i);
         gg[0] = h.x; gg[1] = h.y; gg[2] = h.z; gg[3] = h.w;
@@ -46,7 +46,7 @@ __device__ __forceinline__ void load_g4w(const void *g, int64_t i, float (&gg)[4
 // iteration in flight together), grid-stride over the vector.
 constexpr int kWU = 2;
 
-template <bool GBF16>
+template <int GT>
 __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
     const int64_t groups = a.n / 4;
     const int64_t span = (int64_t)blockDim.x * kWU;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
             const int64_t q = base + u * (int64_t)blockDim.x + threadIdx.x;
             in[u] = q < groups;
             if (in[u]) {
-                load_g4w<GBF16>(a.g, 4 * q, gg[u]);
+                load_g4w<GT>(a.g, 4 * q, gg[u]);
                 xx[u] = *reinterpret_cast<const float4 *>(a.x + 4 * q);
                 mm[u] = *reinterpret_cast<const float4 *>(a.m + 4 * q);
                 vv[u] = *reinterpret_cast<const float4 *>(a.v + 4 * q);
@@ -69,10 +69,10 @@ __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
         for (int u = 0; u < kWU; ++u) {
             if (!in[u]) continue;
             const int64_t q = base + u * (int64_t)blockDim.x + threadIdx.x;
-            warm_one<GBF16>(a, gg[u][0], xx[u].x, mm[u].x, vv[u].x);
-            warm_one<GBF16>(a, gg[u][1], xx[u].y, mm[u].y, vv[u].y);
-            warm_one<GBF16>(a, gg[u][2], xx[u].z, mm[u].z, vv[u].z);
-            warm_one<GBF16>(a, gg[u][3], xx[u].w, mm[u].w, vv[u].w);
+            warm_one<GT>(a, gg[u][0], xx[u].x, mm[u].x, vv[u].x);
+            warm_one<GT>(a, gg[u][1], xx[u].y, mm[u].y, vv[u].y);
+            warm_one<GT>(a, gg[u][2], xx[u].z, mm[u].z, vv[u].z);
+            warm_one<GT>(a, gg[u][3], xx[u].w, mm[u].w, vv[u].w);
             *reinterpret_cast<float4 *>(a.x + 4 * q) = xx[u];
             *reinterpret_cast<float4 *>(a.m + 4 * q) = mm[u];
             *reinterpret_cast<float4 *>(a.v + 4 * q) = vv[u];
@@ -83,9 +83,10 @@ __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
     const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (gid < tail) {
         const int64_t i = 4 * groups + gid;
-        const float g = GBF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.g)[i]) : static_cast<const float *>(a.g)[i];
+        const float g = GT != kGradF32 ? half_bits_to_float<GT>(static_cast<const uint16_t *>(a.g)[i])
+                                       : static_cast<const float *>(a.g)[i];
         float x = a.x[i], m = a.m[i], v = a.v[i];
-        warm_one<GBF16>(a, g, x, m, v);
+        warm_one<GT>(a, g, x, m, v);
         a.x[i] = x;
         a.m[i] = m;
         a.v[i] = v;
@@ -101,7 +102,7 @@ extern "C" onebit_status_t onebit_adam_warmup_step(float *x, float *m, float *v,
                                                    double beta2, double eps, double weight_decay,
                                                    int bias_correction, int64_t step, void *stream) {
     if (n < 0 || step < 1) return ONEBIT_ERR_INVALID;
-    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16) return ONEBIT_ERR_INVALID;
+    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
     if (n == 0) return ONEBIT_OK;
     if (!x || !m || !v || !g) return ONEBIT_ERR_INVALID;
     if (!aligned16(x) || !aligned16(m) || !aligned16(v) || !aligned16(g)) return ONEBIT_ERR_ALIGN;
@@ -135,9 +136,11 @@ extern "C" onebit_status_t onebit_adam_warmup_step(float *x, float *m, float *v,
     hipStream_t s = static_cast<hipStream_t>(stream);
     prof_before(kProfWarmup, s);
     if (g_dtype == ONEBIT_BF16)
-        hipLaunchKernelGGL(k_adam_warmup<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_adam_warmup<kGradBF16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else if (g_dtype == ONEBIT_F16)
+        hipLaunchKernelGGL(k_adam_warmup<kGradF16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(k_adam_warmup<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_adam_warmup<kGradF32>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     prof_after(s);
     return hip_status(hipGetLastError());
 }

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libonebit.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "onebit.h")
 
 ONEBIT_OK, ONEBIT_ERR_INVALID, ONEBIT_ERR_ALIGN, ONEBIT_ERR_HIP, ONEBIT_ERR_NOMEM, ONEBIT_ERR_UNSUPPORTED = range(6)
-ONEBIT_F32, ONEBIT_BF16 = 0, 1
+ONEBIT_F32, ONEBIT_BF16, ONEBIT_F16 = 0, 1, 2
 
 _P, _I64, _I, _D, _U64, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_double, C.c_uint64, C.c_size_t
 
@@ -40,6 +40,7 @@ _SIGS = {
     "onebit_adam_warmup_step": (_I, [_P, _P, _P, _P, _I, _I64, _D, _D, _D, _D, _D, _I, _I64, _P]),
     "onebit_compress_update": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
     "qsdp_quantize": (_I, [_P, _I64, _I, _I, _U64, _P, _P, _P, _P]),
     "qsdp_dequantize": (_I, [_P, _P, _P, _I64, _I, _I, _P, _P, _P]),
     "qsdp_error_stats": (_I, [_P, _P, _I64, _P, _P, _P, _P]),
@@ -104,7 +105,9 @@ def _dtype_code(t):
         return ONEBIT_F32
     if t.dtype in (torch.bfloat16, torch.int16):
         return ONEBIT_BF16
-    raise TypeError(f"gradient dtype {t.dtype} is not float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return ONEBIT_F16
+    raise TypeError(f"gradient dtype {t.dtype} is not float32, bfloat16 or float16")
 
 
 # ---------------------------------------------------------------- API
@@ -199,7 +202,8 @@ def onebit_onepass_max_elements() -> int:
 
 
 PROFILE_CLASSES = ("warmup", "compress_pass1", "compress_onepass", "compress_pass2", "qsdp_quantize",
-                   "qsdp_dequantize", "server_pass1", "server_onepass", "server_pass2", "finalize")
+                   "qsdp_dequantize", "server_pass1", "server_onepass", "server_pass2", "finalize",
+                   "momentum_update")
 
 
 def onebit_profile_begin():
@@ -245,6 +249,12 @@ def onebit_server_reduce(plan, worker_bits, worker_scales, server_error, server_
     _check(load().onebit_server_reduce(plan.handle, W, _ptr(worker_bits), _ptr(worker_scales), _ptr(server_error),
                                        _ptr(server_bits), _ptr(server_scales), _ptr(m_out), _ptr(workspace),
                                        _stream(stream)), "onebit_server_reduce")
+
+
+def onebit_momentum_update(m, mask, v, x, x_bf16, *, lr, eps, weight_decay, stream=None):
+    """mask: uint8 (or bool) tensor of n elements, or None."""
+    _check(load().onebit_momentum_update(_ptr(m), _ptr(mask), _ptr(v), _ptr(x), _ptr(x_bf16), x.numel(), lr, eps,
+                                         weight_decay, _stream(stream)), "onebit_momentum_update")
 
 
 def qsdp_quantize(x_bf16, bucket, bits, seed, codes, bucket_min, bucket_max, stream=None):

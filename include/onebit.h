@@ -57,7 +57,7 @@ typedef enum {
     ONEBIT_ERR_UNSUPPORTED = 5  /* valid request this build does not serve */
 } onebit_status_t;
 
-typedef enum { ONEBIT_F32 = 0, ONEBIT_BF16 = 1 } onebit_dtype_t;
+typedef enum { ONEBIT_F32 = 0, ONEBIT_BF16 = 1, ONEBIT_F16 = 2 } onebit_dtype_t;
 
 /* Opaque plan: device copies of the chunk, tile and mask tables for one flat
  * parameter vector.  Library-owned, immutable after creation, usable from any
@@ -129,8 +129,9 @@ int64_t onebit_onepass_max_elements(void);
  * the summed elapsed milliseconds and the launch count (host arrays of
  * ONEBIT_PROFILE_CLASSES entries, nullable).  Classes: 0 warmup, 1/2/3 worker
  * compression pass 1 / one-pass / pass 2, 4 quantize, 5 dequantize, 6/7/8 server
- * pass 1 / one-pass / pass 2, 9 chunk-norm finalization of two-pass chunks.  Not thread-safe; diagnostics only. */
-#define ONEBIT_PROFILE_CLASSES 10
+ * pass 1 / one-pass / pass 2, 9 chunk-norm finalization of two-pass chunks, 10
+ * momentum update.  Not thread-safe; diagnostics only. */
+#define ONEBIT_PROFILE_CLASSES 11
 void onebit_profile_begin(void);
 onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
 
@@ -138,7 +139,8 @@ onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
  * phase one; [1BA]):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
  *   x -= lr * ( mhat / (sqrt(vhat) + eps) + weight_decay * x ),
  * with mhat = m / (1-b1^t), vhat = v / (1-b2^t) when bias_correction != 0, else
- * mhat = m, vhat = v.  x, m, v: fp32 [n] in place.  g: [n] fp32 or bf16. */
+ * mhat = m, vhat = v.  x, m, v: fp32 [n] in place.  g: [n] fp32, bf16 or fp16
+ * (widened exactly). */
 onebit_status_t onebit_adam_warmup_step(float *x, float *m, float *v, const void *g,
                                         onebit_dtype_t g_dtype, int64_t n, double lr,
                                         double beta1, double beta2, double eps,
@@ -151,7 +153,8 @@ onebit_status_t onebit_adam_warmup_step(float *x, float *m, float *v, const void
  *   bit_i = (c_i < 0);  q_i = bit_i ? -scale_j : +scale_j;  e = c - q;  m = q
  *   masked tensors: m = 0, e = 0 (bits and scale still from c)
  *   x -= lr * ( m / (sqrt(v) + eps) + weight_decay * x );  x_bf16 = bf16(x)
- * g: [n] fp32 or bf16.  m, e, x: fp32 [n] in place; v: fp32 [n] read-only (frozen).
+ * g: [n] fp32, bf16 or fp16 (widened exactly).  m, e, x: fp32 [n] in place; v: fp32
+ * [n] read-only (frozen).
  * bits: uint32 [plan_words] out, least significant bit first, every chunk starting
  * on a word boundary, pad bits 0.  scales: fp32 [n_chunks] out.  x_bf16: uint16
  * [n] out, nullable.  Compress-only (the worker half of the compressed
@@ -175,6 +178,20 @@ onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *
                                      const float *worker_scales, float *server_error,
                                      uint32_t *server_bits, float *server_scales, float *m_out,
                                      void *workspace, void *stream);
+
+/* The worker's finish after the compressed all-reduce ([DSG] sec. 3.5, exp_avg_mask;
+ * sec. 4, phase two), elementwise over n elements, in binary32, unfused:
+ *   m = m * mask;  x -= lr * ( m / (sqrt(v) + eps) + weight_decay * x );  x_bf16 = bf16(x)
+ * m: fp32 [n] in place (the all-reduced momentum, e.g. m_out of the server stage
+ * or its broadcast copy); written only when a mask is given.  mask: uint8 [n],
+ * non-zero = keep, nullable (no mask).  v: fp32 [n] read-only (frozen).  x: fp32 [n]
+ * in place.  x_bf16: uint16 [n] out, nullable.  All arrays 16-byte aligned.  With
+ * no mask and the server's output as m, onebit_compress_update in compress-only
+ * mode -> onebit_server_reduce -> this call reproduces onebit_compress_update's
+ * own update for one worker bit for bit. */
+onebit_status_t onebit_momentum_update(float *m, const uint8_t *mask, const float *v, float *x,
+                                       uint16_t *x_bf16, int64_t n, double lr, double eps,
+                                       double weight_decay, void *stream);
 
 /* QSDP-style unbiased stochastic rounding of bf16 weights ([QSDP] "proposed
  * method"), per bucket of `bucket` elements (the last one may be short):

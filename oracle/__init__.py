@@ -37,6 +37,7 @@ def _load():
                                                _D, _D, _D, _D, _I]
         lib.oracle_server_reduce.argtypes = [_P, _I64, _I, _P, _P, _P, _P, _P, _P]
         lib.oracle_decompress.argtypes = [_P, _I64, _P, _P, _P]
+        lib.oracle_momentum_update.argtypes = [_P, _P, _P, _P, _P, _I64, _D, _D, _D]
         lib.oracle_philox4x32_10.argtypes = [_P, _P, _P]
         lib.oracle_philox4x32_10.restype = None
         lib.oracle_qsdp_uniform.argtypes = [C.c_uint64, _I64]
@@ -46,6 +47,7 @@ def _load():
         lib.oracle_f32_to_bf16.argtypes = [_F]
         lib.oracle_f32_to_bf16.restype = C.c_uint16
         for name in ("oracle_adam_warmup_step", "oracle_compress_update", "oracle_server_reduce",
+                     "oracle_momentum_update",
                      "oracle_decompress", "oracle_qsdp_quantize", "oracle_qsdp_dequantize"):
             getattr(lib, name).restype = C.c_int
         _lib = lib
@@ -91,6 +93,15 @@ def _f32(a):
     return np.ascontiguousarray(a, dtype=np.float32)
 
 
+def _widen(g):
+    """Exact widening of a gradient given as float32, bfloat16 bits (uint16) or float16."""
+    if g.dtype == np.uint16:
+        return bf16_bits_to_f32(g)
+    if g.dtype == np.float16:
+        return np.ascontiguousarray(g, dtype=np.float32)
+    return _f32(g)
+
+
 def bf16_bits_to_f32(u16: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns (uint16) to float32."""
     return (np.ascontiguousarray(u16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
@@ -111,9 +122,7 @@ def words_for_chunks(chunk_off: np.ndarray) -> int:
 def adam_warmup_step(x, m, v, g, *, lr, beta1, beta2, eps, weight_decay, bias_correction, step):
     """In place on float32 arrays x, m, v; g is float32 (or uint16 bf16 bits)."""
     lib = _load()
-    if g.dtype == np.uint16:
-        g = bf16_bits_to_f32(g)
-    g = _f32(g)
+    g = _widen(g)
     _check(lib.oracle_adam_warmup_step(_ptr(x), _ptr(m), _ptr(v), _ptr(g), x.size, lr, beta1, beta2,
                                        eps, weight_decay, int(bias_correction), int(step)), "warmup")
 
@@ -127,9 +136,7 @@ def compress_update(chunk_off, g, m, e, v=None, x=None, *, tensor_off=None, tens
     lib = _load()
     chunk_off = np.ascontiguousarray(chunk_off, dtype=np.int64)
     n_chunks = chunk_off.size - 1
-    if g.dtype == np.uint16:
-        g = bf16_bits_to_f32(g)
-    g = _f32(g)
+    g = _widen(g)
     bits = np.zeros(max(words_for_chunks(chunk_off), 1), dtype=np.uint32)
     scales = np.zeros(max(n_chunks, 1), dtype=np.float32)
     xb = np.zeros(x.size, dtype=np.uint16) if (want_bf16 and x is not None) else None
@@ -162,6 +169,16 @@ def server_reduce(chunk_off, worker_bits, worker_scales, server_error, *, want_m
     _check(lib.oracle_server_reduce(_ptr(chunk_off), n_chunks, W, _ptr(worker_bits), _ptr(worker_scales),
                                     _ptr(server_error), _ptr(bits), _ptr(scales), _ptr(m_out)), "server")
     return bits[:words_for_chunks(chunk_off)], scales[:n_chunks], m_out
+
+
+def momentum_update(m, v, x, *, mask=None, lr, eps, weight_decay, want_bf16=False):
+    """Worker finish after the all-reduce, in place on m and x.  Returns x_bf16 or None."""
+    lib = _load()
+    mask = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    xb = np.zeros(x.size, dtype=np.uint16) if want_bf16 else None
+    _check(lib.oracle_momentum_update(_ptr(m), _ptr(mask), _ptr(v), _ptr(x), _ptr(xb), x.size, lr, eps,
+                                      weight_decay), "momentum_update")
+    return xb
 
 
 def decompress(chunk_off, bits, scales):

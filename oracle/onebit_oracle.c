@@ -349,6 +349,30 @@ int oracle_server_reduce(const int64_t *chunk_off, int64_t n_chunks, int W, cons
     return ORACLE_OK;
 }
 
+/* ------------------------------------- worker finish after the all-reduce
+ * [DSG] sec. 3.5 and sec. 4: after the compressed all-reduce has written the
+ * decompressed momentum back, the momentum is multiplied by exp_avg_mask (a 0/1
+ * tensor of the parameter's shape; here one byte per element, non-zero = 1), then
+ * update = m / (sqrt(v) + eps) + wd * x and x -= lr * update.
+ * mask and x_bf16 are nullable (no mask = all ones).
+ */
+int oracle_momentum_update(float *m, const uint8_t *mask, const float *v, float *x, uint16_t *x_bf16, int64_t n,
+                           double lr_d, double eps_d, double weight_decay_d)
+{
+    if (n < 0 || (n > 0 && (!m || !v || !x)))
+        return ORACLE_ERR_INVALID;
+    const float lr = (float)lr_d, eps = (float)eps_d, weight_decay = (float)weight_decay_d;
+    for (int64_t i = 0; i < n; ++i) {
+        if (mask)
+            m[i] = m[i] * (mask[i] ? 1.0f : 0.0f);
+        const float update = m[i] / (sqrtf(v[i]) + eps) + weight_decay * x[i];
+        x[i] = x[i] - lr * update;
+        if (x_bf16)
+            x_bf16[i] = oracle_f32_to_bf16(x[i]);
+    }
+    return ORACLE_OK;
+}
+
 /* Decompress a packed stream (one worker's or the server's) into fp32. */
 int oracle_decompress(const int64_t *chunk_off, int64_t n_chunks, const uint32_t *bits,
                       const float *scales, float *out)

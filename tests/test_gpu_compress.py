@@ -140,8 +140,8 @@ def edge_state(lengths, rng):
 SIGNED_ZEROS = np.array([0, -0.0, 0, -0.0, 0, 0, -0.0], np.float32)   # c = -0 where m, g, e are all -0
 
 
-@pytest.mark.parametrize("bf16_grad,x_bf16", [(False, False), (True, True)])
-def test_edge_chunk_lengths(bf16_grad, x_bf16):
+@pytest.mark.parametrize("grad_dtype,x_bf16", [("f32", False), ("bf16", True), ("f16", False)])
+def test_edge_chunk_lengths(grad_dtype, x_bf16):
     rng = np.random.default_rng(21)
     off, init = edge_state(LENGTHS, rng)
     n = int(off[-1])
@@ -150,12 +150,14 @@ def test_edge_chunk_lengths(bf16_grad, x_bf16):
     def grads(s):
         g = (np.random.default_rng(100 + s).standard_normal(n) * 1e-3).astype(np.float32)
         g[zero_chunk] = SIGNED_ZEROS
-        if bf16_grad:
+        if grad_dtype == "bf16":
             return torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        if grad_dtype == "f16":
+            return g.astype(np.float16)
         return g
 
-    say(f"edge lengths bf16_grad={bf16_grad}")
-    run_steps(off, 3, init=init, grads=grads, x_bf16=x_bf16, bf16_grad=bf16_grad)
+    say(f"edge lengths grad_dtype={grad_dtype}")
+    run_steps(off, 3, init=init, grads=grads, x_bf16=x_bf16)
 
 
 def test_unaligned_chunk_starts_and_compress_only():
@@ -240,7 +242,7 @@ def test_repeat_is_bit_identical_and_workspace_shared_across_plans():
 
 def test_warmup_kernel_edge_sizes():
     for n in (1, 3, 4, 5, 4099, (1 << 20) + 3):
-        for gbf16 in (False, True):
+        for gdt in ("f32", "bf16", "f16"):
             for bias, wd in ((False, 0.0), (True, 0.01)):
                 rng = np.random.default_rng(n)
                 x, m, _, v = rand_state(n, rng)
@@ -248,9 +250,12 @@ def test_warmup_kernel_edge_sizes():
                 for t in range(1, 4):
                     g32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
                     gt = torch.from_numpy(g32).to(DEV)
-                    if gbf16:
+                    if gdt == "bf16":
                         gt = gt.to(torch.bfloat16)
                         g = host(gt)
+                    elif gdt == "f16":
+                        gt = gt.to(torch.float16)
+                        g = gt.cpu().numpy()
                     else:
                         g = g32
                     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd, bias_correction=bias, step=t)

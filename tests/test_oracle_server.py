@@ -99,3 +99,47 @@ def test_decompress_matches_unpackbits():
     y = oracle.decompress(off, bits, scales)
     per = np.repeat(scales, np.diff(off))
     np.testing.assert_array_equal(y, np.where(unpack(bits, off), -per, per))
+
+
+def test_worker_server_finish_composition_equals_fused_step():
+    """One worker, zero server error, no mask: compress-only -> server -> finish
+    reproduces the fused compress+update bit for bit (bits, scales, m, e, x)."""
+    rng = np.random.default_rng(123)
+    off = W.offsets_from_sizes(LENGTHS)
+    n = int(off[-1])
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    e = (rng.standard_normal(n) * 1e-5).astype(np.float32)
+    v = (rng.uniform(0.5, 2, n) * 1e-6).astype(np.float32)
+    x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    h = dict(lr=1e-3, eps=1e-8, weight_decay=0.01)
+    fm, fe, fx = m.copy(), e.copy(), x.copy()
+    fb, fs, fxb = oracle.compress_update(off, g, fm, fe, v, fx, beta1=0.9, want_bf16=True, **h)
+    wm, we, wx = m.copy(), e.copy(), x.copy()
+    wb, wsc, _ = oracle.compress_update(off, g, wm, we, beta1=0.9)
+    es = np.zeros(n, np.float32)
+    sb, ss, m_out = oracle.server_reduce(off, wb[None], wsc[None], es)
+    xb = oracle.momentum_update(m_out, v, wx, want_bf16=True, **h)
+    for a, b in ((wb, fb), (sb, fb), (wsc, fs), (ss, fs), (we, fe), (m_out, fm), (wx, fx), (xb, fxb)):
+        np.testing.assert_array_equal(a, b)
+    assert np.all(es == 0)
+
+
+def test_momentum_update_mask_and_closed_form():
+    """Mask zeros give m = 0 (sign of the product kept) and, with wd = 0, an unchanged x;
+    with weight decay only (m = 0 everywhere) x follows x (1 - lr wd) to one rounding."""
+    rng = np.random.default_rng(5)
+    n = 5000
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = (rng.uniform(0.5, 2, n) * 1e-6).astype(np.float32)
+    x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    mask = (rng.random(n) < 0.7).astype(np.uint8)
+    m2, x2 = m.copy(), x.copy()
+    oracle.momentum_update(m2, v, x2, mask=mask, lr=1e-3, eps=1e-8, weight_decay=0.0)
+    assert np.all(m2[mask == 0] == 0) and np.array_equal(np.signbit(m2[mask == 0]), np.signbit(m[mask == 0]))
+    np.testing.assert_array_equal(m2[mask == 1], m[mask == 1])
+    np.testing.assert_array_equal(x2[mask == 0], x[mask == 0])
+    z, x3 = np.zeros(n, np.float32), x.copy()
+    oracle.momentum_update(z, v, x3, lr=1e-3, eps=1e-8, weight_decay=0.01)
+    ref = x.astype(np.float64) * (1 - float(np.float32(1e-3)) * float(np.float32(0.01)))
+    assert np.all(np.abs(x3 - ref) <= 2 ** -22 * np.abs(ref))

@@ -105,3 +105,26 @@ def test_bf16_gradient_is_exact_widening():
     oracle.adam_warmup_step(*b, g_wide, weight_decay=0.0, bias_correction=False, step=1, **H)
     for u, w in zip(a, b):
         np.testing.assert_array_equal(u, w)
+
+
+def test_f16_gradient_is_exact_widening():
+    """fp16 gradients enter as their exact binary32 values, subnormals included:
+    2^-24 (the smallest fp16 subnormal), 65504 (the largest finite), -0."""
+    special = np.array([2.0 ** -24, 3 * 2.0 ** -24, 65504.0, -0.0, 2.0 ** -14, -1.5], np.float64)
+    g16 = np.concatenate([special.astype(np.float16),
+                          (np.random.default_rng(4).standard_normal(771) * 1e-4).astype(np.float16)])
+    g_wide = torch.from_numpy(g16).float().numpy()
+    np.testing.assert_array_equal(g_wide[:6], special.astype(np.float32))
+    n = g16.size
+    a = [np.zeros(n, np.float32) for _ in range(3)]
+    b = [np.zeros(n, np.float32) for _ in range(3)]
+    oracle.adam_warmup_step(*a, g16, weight_decay=0.0, bias_correction=False, step=1, **H)
+    oracle.adam_warmup_step(*b, g_wide, weight_decay=0.0, bias_correction=False, step=1, **H)
+    for u, w in zip(a, b):
+        np.testing.assert_array_equal(u, w)
+    off = np.array([0, 300, n], np.int64)
+    r16 = oracle.compress_update(off, g16, np.zeros(n, np.float32), np.zeros(n, np.float32), beta1=0.0)
+    r32 = oracle.compress_update(off, g_wide, np.zeros(n, np.float32), np.zeros(n, np.float32), beta1=0.0)
+    for u, w in zip(r16[:2], r32[:2]):
+        np.testing.assert_array_equal(u, w)
+    assert np.signbit(oracle.decompress(off, r16[0], r16[1])[3]) == 0   # sign(-0) = +1
