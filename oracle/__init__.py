@@ -37,6 +37,8 @@ def _load():
                                                _D, _D, _D, _D, _I]
         lib.oracle_server_reduce.argtypes = [_P, _I64, _I, _P, _P, _P, _P, _P, _P]
         lib.oracle_decompress.argtypes = [_P, _I64, _P, _P, _P]
+        lib.oracle_qsgd_quantize.argtypes = [_P, _I, _I64, _I, _I, C.c_uint64, _I64, _P, _P]
+        lib.oracle_qsgd_reduce.argtypes = [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P]
         lib.oracle_momentum_update.argtypes = [_P, _P, _P, _P, _P, _I64, _D, _D, _D]
         lib.oracle_philox4x32_10.argtypes = [_P, _P, _P]
         lib.oracle_philox4x32_10.restype = None
@@ -47,7 +49,7 @@ def _load():
         lib.oracle_f32_to_bf16.argtypes = [_F]
         lib.oracle_f32_to_bf16.restype = C.c_uint16
         for name in ("oracle_adam_warmup_step", "oracle_compress_update", "oracle_server_reduce",
-                     "oracle_momentum_update",
+                     "oracle_momentum_update", "oracle_qsgd_quantize", "oracle_qsgd_reduce",
                      "oracle_decompress", "oracle_qsdp_quantize", "oracle_qsdp_dequantize"):
             getattr(lib, name).restype = C.c_int
         _lib = lib
@@ -231,3 +233,37 @@ def qsdp_dequantize(codes, bmin, bmax, n, *, bucket, bits, want_f32=False):
     _check(lib.oracle_qsdp_dequantize(_ptr(codes), _ptr(bmin), _ptr(bmax), n, bucket, bits, _ptr(out), _ptr(y)),
            "qsdp_dequantize")
     return out[:n], (y[:n] if want_f32 else None)
+
+
+def qsgd_quantize(g, *, bucket, bits, seed, first_index=0):
+    """g: float32 values or bf16 bit patterns (uint16), global indices first_index...
+    Returns (codes, norms)."""
+    lib = _load()
+    if g.dtype == np.uint16:
+        dt = 1
+    else:
+        g = _f32(g)
+        dt = 0
+    g = np.ascontiguousarray(g)
+    n = g.size
+    nb = (n + bucket - 1) // bucket
+    nbytes = (n + 1) // 2 if bits == 4 else n
+    codes = np.zeros(max(nbytes, 1), dtype=np.uint8)
+    norms = np.zeros(max(nb, 1), dtype=np.float32)
+    _check(lib.oracle_qsgd_quantize(_ptr(g), dt, n, bucket, bits, seed, first_index, _ptr(codes), _ptr(norms)),
+           "qsgd_quantize")
+    return codes[:nbytes], norms[:nb]
+
+
+def qsgd_reduce(codes, norms, n, *, bucket, bits, want_bf16=False):
+    """codes: uint8 [W, code_bytes] (or 1-D for one worker); norms: float32 [W, n_buckets].
+    Returns (y_f32 [n], y_bf16 [n] or None)."""
+    lib = _load()
+    codes = np.ascontiguousarray(np.atleast_2d(codes), dtype=np.uint8)
+    norms = np.ascontiguousarray(np.atleast_2d(norms), dtype=np.float32)
+    W = codes.shape[0]
+    out = np.zeros(max(n, 1), dtype=np.float32)
+    ob = np.zeros(max(n, 1), dtype=np.uint16) if want_bf16 else None
+    _check(lib.oracle_qsgd_reduce(W, _ptr(codes), codes.shape[1], _ptr(norms), norms.shape[1], n, bucket, bits,
+                                  _ptr(out), _ptr(ob)), "qsgd_reduce")
+    return out[:n], (ob[:n] if want_bf16 else None)

@@ -27,6 +27,10 @@
  *  [QSDP] nubint.ai review "Quantized Distributed Training of Large Models with
  *         Convergence Guarantees", section "proposed method": weights quantized by
  *         unbiased stochastic rounding to the nearest quantization levels.
+ *  [QSGD] Alistarh, Grubic, Li, Tomioka, Vojnovic, "QSGD: Communication-Efficient
+ *         SGD via Gradient Quantization and Encoding", NeurIPS 2017, sec. 3.1 (the
+ *         stochastic quantizer Q_s) and its bucketed form; named by [QSDP] as the
+ *         standard unbiased compressor applied to gradients.
  *  [PHX]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
  *         SC'11, section 4 (the Philox-4x32 bijection, 10 rounds).
  *
@@ -48,7 +52,14 @@
  *    one rounding to fp32;
  *  - QSDP: 2^b evenly spaced levels over [min, max] of each bucket; Philox key =
  *    seed, counter = (element index >> 2, 0, 0), output word (index & 3);
- *    round up iff u < floor(p * 2^32).
+ *    round up iff u < floor(p * 2^32);
+ *  - QSGD: per bucket the L2 norm (same fp64 sum, sqrt in fp64, one rounding to
+ *    fp32); s = 2^(bits-1) - 1 levels of |g| / norm; code = sign bit (top bit of
+ *    the code, set iff g < 0) and the level below it; same Philox stream layout as
+ *    the weights (the caller picks a different seed); dequantized value
+ *    fl32(fl32(level * norm) / s), negated for a set sign bit; several workers'
+ *    values are averaged as the server stage does (fp64 sum in worker order, fp64
+ *    divide by W, one rounding).
  */
 #include <math.h>
 #include <stddef.h>
@@ -527,6 +538,105 @@ int oracle_qsdp_dequantize(const uint8_t *codes, const float *bucket_min, const 
         else
             code = (codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu;
         const float y = mn + (float)code * delta;
+        if (out_f32)
+            out_f32[i] = y;
+        if (out_bf16)
+            out_bf16[i] = oracle_f32_to_bf16(y);
+    }
+    return ORACLE_OK;
+}
+
+/* --------------------------------------------- O7: QSGD gradient quantizer
+ * [QSGD] sec. 3.1: with v a bucket of the gradient and l the integer such that
+ * |v_i| / ||v||_2 lies in [l/s, (l+1)/s], the value sent is ||v||_2 sgn(v_i) xi_i / s,
+ * where xi_i = l + 1 with probability |v_i| s / ||v||_2 - l and l otherwise, so
+ * that its expectation is v_i.  Here (binary32 steps, as on the device side):
+ *   t = fl32(|g| / norm);  u = fl32(t * s);  l = floor(u);  p = u - l (exact)
+ *   level = l + (uniform < floor(p * 2^32));  code = (g < 0) << (bits-1) | level.
+ * A bucket of zeros has norm 0 and all codes 0.  g: fp32 (dtype 0) or bf16 bits
+ * (dtype 1).  4-bit codes are packed two per byte, even element in the low nibble.
+ */
+static double bucket_sum_squares(const float *v, int64_t n)
+{
+    neumaier_t acc = {0.0, 0.0};
+    for (int64_t i = 0; i < n; ++i)
+        neumaier_add(&acc, (double)v[i] * (double)v[i]);
+    return neumaier_result(&acc);
+}
+
+int oracle_qsgd_quantize(const void *g, int g_dtype, int64_t n, int bucket, int nbits, uint64_t seed,
+                         int64_t first_index, uint8_t *codes, float *norms)
+{
+    if (n < 0 || bucket < 1 || (nbits != 4 && nbits != 8) || (g_dtype != 0 && g_dtype != 1) || first_index < 0 ||
+        first_index % bucket != 0 || (nbits == 4 && (bucket % 2 != 0 || first_index % 2 != 0)))
+        return ORACLE_ERR_INVALID;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!g || !codes || !norms)
+        return ORACLE_ERR_INVALID;
+    const uint32_t s = (1u << (nbits - 1)) - 1u;
+    float *v = (float *)malloc((size_t)bucket * sizeof(float));
+    if (!v)
+        return ORACLE_ERR_NOMEM;
+    memset(codes, 0, (size_t)(nbits == 4 ? (n + 1) / 2 : n));
+    const int64_t n_buckets = (n + bucket - 1) / bucket;
+    for (int64_t b = 0; b < n_buckets; ++b) {
+        const int64_t lo = b * (int64_t)bucket;
+        const int64_t len = lo + bucket < n ? bucket : n - lo;
+        for (int64_t k = 0; k < len; ++k)
+            v[k] = g_dtype == 1 ? oracle_bf16_to_f32(((const uint16_t *)g)[lo + k]) : ((const float *)g)[lo + k];
+        const float norm = (float)sqrt(bucket_sum_squares(v, len));
+        norms[b] = norm;
+        if (norm == 0.0f)
+            continue;
+        for (int64_t k = 0; k < len; ++k) {
+            const float t = fabsf(v[k]) / norm;
+            const float u = t * (float)s;
+            const float l = floorf(u);
+            const float p = u - l;
+            const uint64_t thr = (uint64_t)floor((double)p * 4294967296.0);
+            uint32_t level = (uint32_t)l + ((uint64_t)oracle_qsdp_uniform(seed, first_index + lo + k) < thr ? 1u : 0u);
+            const uint32_t code = (v[k] < 0.0f ? 1u << (nbits - 1) : 0u) | level;
+            const int64_t i = lo + k;
+            if (nbits == 8)
+                codes[i] = (uint8_t)code;
+            else
+                codes[i >> 1] |= (uint8_t)((i & 1) ? code << 4 : code);
+        }
+    }
+    free(v);
+    return ORACLE_OK;
+}
+
+/* The value worker w sent for element i. */
+static float qsgd_value(const uint8_t *codes, const float *norms, int64_t i, int bucket, int nbits)
+{
+    const uint32_t s = (1u << (nbits - 1)) - 1u;
+    const uint32_t code = nbits == 8 ? codes[i] : (uint32_t)((codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu);
+    const uint32_t level = code & s;
+    const float y = ((float)level * norms[i / bucket]) / (float)s;
+    return (code >> (nbits - 1)) ? -y : y;
+}
+
+/* [QSGD] decoding, averaged over W workers' streams (the reduce half of a quantized
+ * gradient reduce-scatter): out_i = fl32( (sum_w y_{w,i}) / W ), fp64 sum in worker
+ * order.  Worker w's codes start at codes + w * code_stride bytes, its norms at
+ * norms + w * norm_stride.  W = 1 is plain dequantization. */
+int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const float *norms, int64_t norm_stride,
+                       int64_t n, int bucket, int nbits, float *out_f32, uint16_t *out_bf16)
+{
+    if (W < 1 || n < 0 || bucket < 1 || (nbits != 4 && nbits != 8) || (nbits == 4 && bucket % 2 != 0))
+        return ORACLE_ERR_INVALID;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!codes || !norms || (!out_f32 && !out_bf16))
+        return ORACLE_ERR_INVALID;
+    for (int64_t i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int w = 0; w < W; ++w)
+            acc += (double)qsgd_value(codes + (int64_t)w * code_stride, norms + (int64_t)w * norm_stride, i, bucket,
+                                      nbits);
+        const float y = (float)(acc / (double)W);
         if (out_f32)
             out_f32[i] = y;
         if (out_bf16)

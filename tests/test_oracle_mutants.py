@@ -15,6 +15,7 @@ from oracle import build as obuild
 
 import test_oracle_compress as TC  # noqa: E402
 import test_oracle_qsdp as TQ
+import test_oracle_qsgd as TG
 import test_oracle_server as TS
 import test_oracle_warmup as TW
 
@@ -52,6 +53,19 @@ def _qsdp():
     TQ.test_unbiased_and_variance_closed_form_brute_force(8)
 
 
+def _qsgd():
+    TG.test_integer_ratio_buckets_are_exact(False)
+    TG.test_lone_value_zero_bucket_signed_zero_and_padding()
+    TG.test_norm_is_the_rounded_exact_norm()
+    TG.test_unbiased_and_variance_closed_form(4)
+    TG.test_average_of_workers()
+
+
+def _finish():
+    TS.test_worker_server_finish_composition_equals_fused_step()
+    TS.test_momentum_update_mask_and_closed_form()
+
+
 MUTANTS = [
     # (name, original text, mistaken text, pins expected to catch it)
     ("warmup g^2 dropped", "ob2 * (gi * gi)", "ob2 * gi", _warm),
@@ -81,6 +95,21 @@ MUTANTS = [
      _qsdp),
     ("philox wrong high half", "const uint32_t y0 = hi1 ^ x1 ^ k0;", "const uint32_t y0 = hi0 ^ x1 ^ k0;", _qsdp),
     ("philox word index", "return out[i & 3];", "return out[0];", _qsdp),
+    ("qsgd rounds the wrong way", "first_index + lo + k) < thr ? 1u : 0u", "first_index + lo + k) >= thr ? 1u : 0u", _qsgd),
+    ("qsgd sign of zero", "(v[k] < 0.0f ? 1u << (nbits - 1) : 0u)", "(v[k] <= 0.0f ? 1u << (nbits - 1) : 0u)", _qsgd),
+    ("qsgd s + 1 levels", "const float u = t * (float)s;", "const float u = t * (float)(s + 1);", _qsgd),
+    ("qsgd norm not square-rooted", "const float norm = (float)sqrt(bucket_sum_squares(v, len));",
+     "const float norm = (float)bucket_sum_squares(v, len);", _qsgd),
+    ("qsgd decode scale", "((float)level * norms[i / bucket]) / (float)s;",
+     "((float)level * norms[i / bucket]) / (float)(s + 1);", _qsgd),
+    ("qsgd pack nibble order", "codes[i >> 1] |= (uint8_t)((i & 1) ? code << 4 : code);",
+     "codes[i >> 1] |= (uint8_t)((i & 1) ? code : code << 4);", _qsgd),
+    ("qsgd decode nibble order", "(uint32_t)((codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu)",
+     "(uint32_t)((codes[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xfu)", _qsgd),
+    ("qsgd average not divided", "const float y = (float)(acc / (double)W);", "const float y = (float)acc;", _qsgd),
+    ("finish ignores the mask", "m[i] = m[i] * (mask[i] ? 1.0f : 0.0f);", "m[i] = m[i];", _finish),
+    ("finish weight decay sign", "const float update = m[i] / (sqrtf(v[i]) + eps) + weight_decay * x[i];",
+     "const float update = m[i] / (sqrtf(v[i]) + eps) - weight_decay * x[i];", _finish),
 ]
 
 
