@@ -407,6 +407,30 @@ def secondary_rows(dev, args):
     torch.cuda.empty_cache()
     log(f"[bench] qsdp {[(k, v) for k, v in rows.items() if 'qsdp' in k]}")
 
+    # QSGD on the same model's bf16 gradients: one worker's quantization of its whole
+    # gradient, then the shard owner's decode-and-average of 8 workers' streams
+    qg = W.QsgdWorkload()
+    gq = W.qsgd_gradient(qg, 0, device=dev)
+    nbq = (qg.n + qg.bucket - 1) // qg.bucket
+    norms = torch.zeros((qg.W, nbq), device=dev)
+    for bits in (4, 8):
+        cb = (qg.n + 1) // 2 if bits == 4 else qg.n
+        stride = (cb + 15) // 16 * 16
+        codes = torch.zeros((qg.W, stride), dtype=torch.uint8, device=dev)
+        for w in range(qg.W):
+            ob.qsgd_quantize(gq, qg.bucket, bits, 100 + w, codes[w], norms[w])
+        out = torch.zeros(qg.shard, device=dev)
+        tq, _ = timed(lambda: ob.qsgd_quantize(gq, qg.bucket, bits, 7, codes[0], norms[0]), steps, 1)
+        tr, _ = timed(lambda: ob.qsgd_reduce(codes, norms, qg.shard, qg.bucket, bits, out_f32=out), steps, 1)
+        bq = 2.0 + bits / 8.0 + 4.0 / qg.bucket
+        br = qg.W * (bits / 8.0 + 4.0 / qg.bucket) + 4.0
+        rows[f"qsgd{bits}_quantize"] = dict(elems_per_s=qg.n / tq, gbps=bq * qg.n / tq / 1e9)
+        rows[f"qsgd{bits}_reduce_{qg.W}x{qg.shard}"] = dict(elems_per_s=qg.shard / tr, gbps=br * qg.shard / tr / 1e9)
+        del codes, out
+    del gq, norms
+    torch.cuda.empty_cache()
+    log(f"[bench] qsgd {[(k, v) for k, v in rows.items() if 'qsgd' in k]}")
+
     # simulated compressed all-reduce: 16 workers x 64M fp32, 16 chunks of 4M
     a = W.AllreduceWorkload()
     plan = ob.onebit_plan_create(a.chunk_off)

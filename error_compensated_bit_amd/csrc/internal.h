@@ -86,7 +86,9 @@ enum ProfClass {
     kProfServerPass2 = 8,
     kProfFinalize = 9,
     kProfMomentumUpdate = 10,
-    kProfClasses = 11
+    kProfQsgdQuantize = 11,
+    kProfQsgdReduce = 12,
+    kProfClasses = 13
 };
 void prof_before(int cls, hipStream_t s);
 void prof_after(hipStream_t s);

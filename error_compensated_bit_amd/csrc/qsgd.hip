@@ -1,0 +1,433 @@
+// qsgd.hip -- the gradient side of QSDP: the standard unbiased gradient
+// compressor (QSDP review, "proposed method", naming Alistarh et al. 2017; QSGD,
+// sec. 3.1) and the decode-and-average of W workers' streams that the shard
+// owner of a quantized reduce-scatter performs.
+//
+// Per bucket of the gradient: norm = ||g||_2 (fp64 double-double sum of squares,
+// fp64 square root, one rounding to fp32); s = 2^(bits-1) - 1 levels of |g|/norm,
+// rounded up at random with probability equal to the fractional part, so the
+// decoded value norm * level / s carries the sign of g and has expectation g.
+// Codes: sign bit on top, level below; 4-bit codes two per byte (even element
+// low).  Random words: Philox4x32-10 keyed by the seed, counter = element index
+// / 4, word = element index % 4 -- the weights' layout; the caller gives the
+// gradient stream its own seed.
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace onebit {
+
+struct GArgs {
+    const void *g;
+    int64_t n;
+    int64_t n_buckets;
+    int32_t bucket;
+    uint32_t k0, k1;
+    uint8_t *codes;
+    float *norms;
+};
+
+template <int GT>
+__device__ __forceinline__ float load_grad(const void *g, int64_t i) {
+    if (GT == kGradF32) return static_cast<const float *>(g)[i];
+    return half_bits_to_float<GT>(static_cast<const uint16_t *>(g)[i]);
+}
+
+// Level and sign of one element, given its uniform word.
+template <int BITS>
+__device__ __forceinline__ uint32_t qsgd_code(float g, float norm, uint32_t u) {
+    constexpr float S = (float)((1 << (BITS - 1)) - 1);
+    if (norm == 0.0f) return 0u;
+    const float t = __fdiv_rn(fabsf(g), norm);           // <= 1: norm >= |g| exactly
+    const float v = mul_rn(t, S);
+    const float l = floorf(v);
+    const float p = sub_rn(v, l);                          // exact, in [0, 1)
+    const uint32_t thr = (uint32_t)ldexpf(p, 32);          // floor(p * 2^32), exact
+    const uint32_t level = (uint32_t)l + (u < thr ? 1u : 0u);
+    return (g < 0.0f ? (1u << (BITS - 1)) : 0u) | level;
+}
+
+__device__ __forceinline__ float norm_of(DD acc) {
+    const DD t = wave_sum_dd(acc);
+    return (float)__dsqrt_rn(t.hi);
+}
+
+// Buckets of 1024: one wave per bucket, lane l owns the 16 consecutive elements
+// 16l..16l+15 (two or four 16-byte loads), kept in registers between the norm and
+// the codes; four Philox calls per lane; one 8- or 16-byte store of codes.
+template <int BITS, int GT>
+__global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+        const int64_t base = b * 1024;
+        const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
+        const int k0 = 16 * lane;
+        float f[16];
+        if (k0 + 15 < len) {
+            if (GT == kGradF32) {
+                const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + base + k0);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float4 v = src[h];
+                    f[4 * h] = v.x; f[4 * h + 1] = v.y; f[4 * h + 2] = v.z; f[4 * h + 3] = v.w;
+                }
+            } else {
+                const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.g) + base + k0);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 v = src[h];
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f[8 * h + 2 * q] = half_bits_to_float<GT>(w[q] & 0xffffu);
+                        f[8 * h + 2 * q + 1] = half_bits_to_float<GT>(w[q] >> 16);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) f[q] = (k0 + q < len) ? load_grad<GT>(a.g, base + k0 + q) : 0.0f;
+        }
+        DD acc{0.0, 0.0};
+#pragma unroll
+        for (int q = 0; q < 16; ++q) dd_add_term(acc, (double)f[q] * (double)f[q]);   // each square exact
+        const float norm = norm_of(acc);
+        if (lane == 0) a.norms[b] = norm;
+        uint32_t code[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const uint64_t blk = (uint64_t)(base + k0 + 4 * g4) >> 2;
+            const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
+            code[4 * g4 + 0] = qsgd_code<BITS>(f[4 * g4 + 0], norm, r.a);
+            code[4 * g4 + 1] = qsgd_code<BITS>(f[4 * g4 + 1], norm, r.b);
+            code[4 * g4 + 2] = qsgd_code<BITS>(f[4 * g4 + 2], norm, r.c);
+            code[4 * g4 + 3] = qsgd_code<BITS>(f[4 * g4 + 3], norm, r.d);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (k0 + q >= len) code[q] = 0;
+        if (BITS == 4) {
+            uint2 pk;
+            pk.x = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12) | (code[4] << 16) | (code[5] << 20) |
+                   (code[6] << 24) | (code[7] << 28);
+            pk.y = code[8] | (code[9] << 4) | (code[10] << 8) | (code[11] << 12) | (code[12] << 16) |
+                   (code[13] << 20) | (code[14] << 24) | (code[15] << 28);
+            uint8_t *dst = a.codes + ((base + k0) >> 1);
+            if (k0 + 15 < len) {
+                *reinterpret_cast<uint2 *>(dst) = pk;
+            } else {
+                for (int q = 0; 2 * q < len - k0; ++q) dst[q] = (uint8_t)(((q < 4 ? pk.x : pk.y) >> (8 * (q & 3))) & 0xffu);
+            }
+        } else {
+            uint4 pk;
+            pk.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            pk.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+            pk.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
+            pk.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
+            uint8_t *dst = a.codes + base + k0;
+            if (k0 + 15 < len) {
+                *reinterpret_cast<uint4 *>(dst) = pk;
+            } else {
+                for (int q = 0; q < len - k0; ++q) dst[q] = (uint8_t)code[q];
+            }
+        }
+    }
+}
+
+// Any bucket size (even for 4-bit codes): one wave per bucket, a norm pass and a
+// code pass over lane-strided elements (the bucket is in cache for the second);
+// each lane writes whole bytes, one Philox call per element.
+template <int BITS, int GT>
+__global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+        const int64_t base = b * a.bucket;
+        const int32_t len = (int32_t)min((int64_t)a.bucket, a.n - base);
+        DD acc{0.0, 0.0};
+        for (int k = lane; k < len; k += 64) {
+            const double v = (double)load_grad<GT>(a.g, base + k);
+            dd_add_term(acc, v * v);
+        }
+        const float norm = norm_of(acc);
+        if (lane == 0) a.norms[b] = norm;
+        const int step = BITS == 4 ? 2 : 1;
+        for (int k = step * lane; k < len; k += 64 * step) {
+            uint32_t byte = 0;
+            for (int q = 0; q < step && k + q < len; ++q) {
+                const int64_t i = base + k + q;
+                const uint64_t blk = (uint64_t)i >> 2;
+                const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
+                const uint32_t w = (i & 3) == 0 ? r.a : (i & 3) == 1 ? r.b : (i & 3) == 2 ? r.c : r.d;
+                byte |= qsgd_code<BITS>(load_grad<GT>(a.g, i), norm, w) << (4 * q);
+            }
+            a.codes[BITS == 4 ? ((base + k) >> 1) : (base + k)] = (uint8_t)byte;
+        }
+    }
+}
+
+// ------------------------------------------------ decode and average
+struct RArgs {
+    const uint8_t *codes;
+    int64_t code_stride;
+    const float *norms;
+    int64_t norm_stride;
+    int64_t n;
+    int32_t bucket;
+    int32_t W;
+    float *out_f32;
+    uint16_t *out_bf16;
+    double invW;  // 1 / W, exact when W is a power of two
+};
+
+// Level spacing of a bucket.
+template <int BITS>
+__device__ __forceinline__ float level_step(float norm) {
+    return __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
+}
+// acc + (+-level * step): the product is exact in fp64 (at most 7 + 24 significant
+// bits), so one fused multiply-add is the fp64 sum of the exact decoded value.
+// The code sits at bit P of the 32-bit word w; its sign bit goes straight into the
+// sign of the converted level (the level's own sign bit is 0).
+template <int BITS, int P>
+__device__ __forceinline__ double qsgd_accumulate(double acc, uint32_t w, double step) {
+    constexpr uint32_t S = (1u << (BITS - 1)) - 1u;
+    constexpr uint32_t SIGN = 1u << (P + BITS - 1);
+    const double lv = (double)((w >> P) & S);
+    const uint32_t hi = (uint32_t)(__double_as_longlong(lv) >> 32) | ((w & SIGN) << (32 - BITS - P));
+    const double slv = __hiloint2double((int)hi, (int)(uint32_t)__double_as_longlong(lv));
+    return __fma_rn(slv, step, acc);
+}
+
+// The E codes of one 16-byte word, unrolled with compile-time bit positions.
+template <int BITS, int K = 0>
+struct Accumulate16 {
+    static constexpr int PER = 32 / BITS;
+    static constexpr int E = 128 / BITS;
+    __device__ __forceinline__ static void run(double (&acc)[E], const uint32_t (&ws)[4], const double (&step)[E]) {
+        acc[K] = qsgd_accumulate<BITS, BITS * (K % PER)>(acc[K], ws[K / PER], step[K]);
+        Accumulate16<BITS, K + 1>::run(acc, ws, step);
+    }
+};
+template <>
+struct Accumulate16<4, 32> {
+    __device__ __forceinline__ static void run(double (&)[32], const uint32_t (&)[4], const double (&)[32]) {}
+};
+template <>
+struct Accumulate16<8, 16> {
+    __device__ __forceinline__ static void run(double (&)[16], const uint32_t (&)[4], const double (&)[16]) {}
+};
+
+// The mean over W: a product with the exact reciprocal when W is a power of two
+// (the same value as the quotient), the quotient otherwise.
+template <bool POW2>
+__device__ __forceinline__ float mean_of(double acc, double Wd, double invW) {
+    return (float)(POW2 ? __dmul_rn(acc, invW) : __ddiv_rn(acc, Wd));
+}
+
+__device__ __forceinline__ void store_out(const RArgs &a, int64_t i, float y) {
+    if (a.out_f32) a.out_f32[i] = y;
+    if (a.out_bf16) a.out_bf16[i] = (uint16_t)float_to_bf16_bits(y);
+}
+
+// One 16-byte word of every worker's row per thread and iteration: E = 32
+// consecutive elements (4-bit) or 16 (8-bit), so each load moves 16 bytes.  With
+// the bucket a multiple of E the E elements share one norm (one level spacing) per
+// worker.  Sum over workers in fp64, in worker order.
+constexpr int kBatch = 4;
+
+template <int BITS, bool SHARED_NORM, bool POW2>
+__global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
+    constexpr int E = 128 / BITS;
+    const int64_t groups = a.n / E;
+    const double Wd = (double)a.W;
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < groups;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i0 = E * q;
+        double acc[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) acc[k] = 0.0;
+        const int64_t b0 = i0 / a.bucket;
+        // workers in batches of kBatch: every load of a batch is issued before its
+        // words are decoded, so each thread keeps kBatch 16-byte loads in flight
+        for (int w0 = 0; w0 < a.W; w0 += kBatch) {
+            uint4 word[kBatch];
+            float nm[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (w0 + j < a.W) {
+                    word[j] = *reinterpret_cast<const uint4 *>(a.codes + (int64_t)(w0 + j) * a.code_stride + 16 * q);
+                    nm[j] = SHARED_NORM ? a.norms[(int64_t)(w0 + j) * a.norm_stride + b0] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (w0 + j >= a.W) break;
+                const uint32_t ws[4] = {word[j].x, word[j].y, word[j].z, word[j].w};
+                double sk[E];
+                if (SHARED_NORM) {
+                    const double st = (double)level_step<BITS>(nm[j]);
+#pragma unroll
+                    for (int k = 0; k < E; ++k) sk[k] = st;
+                } else {
+                    const float *nrow = a.norms + (int64_t)(w0 + j) * a.norm_stride;
+#pragma unroll
+                    for (int k = 0; k < E; ++k) sk[k] = (double)level_step<BITS>(nrow[(i0 + k) / a.bucket]);
+                }
+                Accumulate16<BITS>::run(acc, ws, sk);
+            }
+        }
+        float y[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) y[k] = mean_of<POW2>(acc[k], Wd, a.invW);
+        if (a.out_f32) {
+            float4 *o = reinterpret_cast<float4 *>(a.out_f32 + i0);
+#pragma unroll
+            for (int h = 0; h < E / 4; ++h) o[h] = make_float4(y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]);
+        }
+        if (a.out_bf16) {
+            uint4 *o = reinterpret_cast<uint4 *>(a.out_bf16 + i0);
+#pragma unroll
+            for (int h = 0; h < E / 8; ++h) {
+                uint4 pk;
+                pk.x = float_to_bf16_bits(y[8 * h + 0]) | (float_to_bf16_bits(y[8 * h + 1]) << 16);
+                pk.y = float_to_bf16_bits(y[8 * h + 2]) | (float_to_bf16_bits(y[8 * h + 3]) << 16);
+                pk.z = float_to_bf16_bits(y[8 * h + 4]) | (float_to_bf16_bits(y[8 * h + 5]) << 16);
+                pk.w = float_to_bf16_bits(y[8 * h + 6]) | (float_to_bf16_bits(y[8 * h + 7]) << 16);
+                o[h] = pk;
+            }
+        }
+    }
+    // ragged tail (n % E elements), one thread each
+    const int64_t tail = a.n - E * groups;
+    const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (gid < tail) {
+        const int64_t i = E * groups + gid;
+        double acc = 0.0;
+        for (int w = 0; w < a.W; ++w) {
+            const uint8_t *row = a.codes + (int64_t)w * a.code_stride;
+            const uint32_t c = BITS == 4 ? (uint32_t)(row[i >> 1] >> ((i & 1) * 4)) & 15u : (uint32_t)row[i];
+            const double st = (double)level_step<BITS>(a.norms[(int64_t)w * a.norm_stride + i / a.bucket]);
+            acc = qsgd_accumulate<BITS, 0>(acc, c, st);
+        }
+        store_out(a, i, mean_of<POW2>(acc, Wd, a.invW));
+    }
+}
+
+static int device_cus() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return cus;
+}
+
+template <int BITS, int GT>
+static void launch_quantize(const GArgs &a, unsigned grid, hipStream_t s) {
+    if (a.bucket == 1024)
+        hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT>), dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_qsgd_quantize_generic<BITS, GT>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <int BITS>
+static void launch_quantize_dt(const GArgs &a, onebit_dtype_t dt, unsigned grid, hipStream_t s) {
+    if (dt == ONEBIT_BF16)
+        launch_quantize<BITS, kGradBF16>(a, grid, s);
+    else if (dt == ONEBIT_F16)
+        launch_quantize<BITS, kGradF16>(a, grid, s);
+    else
+        launch_quantize<BITS, kGradF32>(a, grid, s);
+}
+
+template <int BITS>
+static void launch_reduce(const RArgs &a, bool shared, bool pow2, unsigned grid, hipStream_t s) {
+    if (shared && pow2)
+        hipLaunchKernelGGL((k_qsgd_reduce<BITS, true, true>), dim3(grid), dim3(256), 0, s, a);
+    else if (shared)
+        hipLaunchKernelGGL((k_qsgd_reduce<BITS, true, false>), dim3(grid), dim3(256), 0, s, a);
+    else if (pow2)
+        hipLaunchKernelGGL((k_qsgd_reduce<BITS, false, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_qsgd_reduce<BITS, false, false>), dim3(grid), dim3(256), 0, s, a);
+}
+
+}  // namespace onebit
+
+using namespace onebit;
+
+extern "C" onebit_status_t qsgd_quantize(const void *g, onebit_dtype_t g_dtype, int64_t n, int bucket, int bits,
+                                         uint64_t seed, uint8_t *codes, float *norms, void *stream) {
+    if (n < 0 || bucket < 1 || bucket > 65536 || (bits != 4 && bits != 8)) return ONEBIT_ERR_INVALID;
+    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
+    if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
+    if (n == 0) return ONEBIT_OK;
+    if (!g || !codes || !norms) return ONEBIT_ERR_INVALID;
+    if (!aligned16(g) || !aligned16(codes) || !aligned_to(norms, 4)) return ONEBIT_ERR_ALIGN;
+    GArgs a{};
+    a.g = g;
+    a.n = n;
+    a.n_buckets = (n + bucket - 1) / bucket;
+    a.bucket = bucket;
+    a.k0 = (uint32_t)seed;
+    a.k1 = (uint32_t)(seed >> 32);
+    a.codes = codes;
+    a.norms = norms;
+    int64_t blocks = (a.n_buckets + 3) / 4;
+    const int64_t cap = (int64_t)device_cus() * 32;
+    if (blocks > cap) blocks = cap;
+    const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    prof_before(kProfQsgdQuantize, s);
+    if (bits == 4)
+        launch_quantize_dt<4>(a, g_dtype, grid, s);
+    else
+        launch_quantize_dt<8>(a, g_dtype, grid, s);
+    prof_after(s);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" onebit_status_t qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const float *norms,
+                                       int64_t norm_stride, int64_t n, int bucket, int bits, float *out_f32,
+                                       uint16_t *out_bf16, void *stream) {
+    if (W < 1 || W > 65536 || n < 0 || bucket < 1 || bucket > 65536 || (bits != 4 && bits != 8))
+        return ONEBIT_ERR_INVALID;
+    if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
+    if (n == 0) return ONEBIT_OK;
+    const int64_t code_bytes = bits == 4 ? (n + 1) / 2 : n;
+    const int64_t n_buckets = (n + bucket - 1) / bucket;
+    if (!codes || !norms || (!out_f32 && !out_bf16)) return ONEBIT_ERR_INVALID;
+    if (W > 1 && (code_stride < code_bytes || norm_stride < n_buckets)) return ONEBIT_ERR_INVALID;
+    if (!aligned16(codes) || (W > 1 && code_stride % 16 != 0) || !aligned_to(norms, 4)) return ONEBIT_ERR_ALIGN;
+    if ((out_f32 && !aligned16(out_f32)) || (out_bf16 && !aligned16(out_bf16))) return ONEBIT_ERR_ALIGN;
+    RArgs a{};
+    a.codes = codes;
+    a.code_stride = code_stride;
+    a.norms = norms;
+    a.norm_stride = norm_stride;
+    a.n = n;
+    a.bucket = bucket;
+    a.W = W;
+    a.out_f32 = out_f32;
+    a.out_bf16 = out_bf16;
+    int64_t blocks = (n / (128 / bits) + 255) / 256;
+    const int64_t cap = (int64_t)device_cus() * 16;
+    if (blocks > cap) blocks = cap;
+    const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    a.invW = 1.0 / (double)W;
+    const bool shared = bucket % (128 / bits) == 0;
+    const bool pow2 = (W & (W - 1)) == 0;
+    prof_before(kProfQsgdReduce, s);
+    if (bits == 4)
+        launch_reduce<4>(a, shared, pow2, grid, s);
+    else
+        launch_reduce<8>(a, shared, pow2, grid, s);
+    prof_after(s);
+    return hip_status(hipGetLastError());
+}

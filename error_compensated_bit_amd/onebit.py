@@ -41,6 +41,8 @@ _SIGS = {
     "onebit_compress_update": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
+    "qsgd_quantize": (_I, [_P, _I, _I64, _I, _I, _U64, _P, _P, _P]),
+    "qsgd_reduce": (_I, [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P, _P]),
     "qsdp_quantize": (_I, [_P, _I64, _I, _I, _U64, _P, _P, _P, _P]),
     "qsdp_dequantize": (_I, [_P, _P, _P, _I64, _I, _I, _P, _P, _P]),
     "qsdp_error_stats": (_I, [_P, _P, _I64, _P, _P, _P, _P]),
@@ -203,7 +205,7 @@ def onebit_onepass_max_elements() -> int:
 
 PROFILE_CLASSES = ("warmup", "compress_pass1", "compress_onepass", "compress_pass2", "qsdp_quantize",
                    "qsdp_dequantize", "server_pass1", "server_onepass", "server_pass2", "finalize",
-                   "momentum_update")
+                   "momentum_update", "qsgd_quantize", "qsgd_reduce")
 
 
 def onebit_profile_begin():
@@ -255,6 +257,20 @@ def onebit_momentum_update(m, mask, v, x, x_bf16, *, lr, eps, weight_decay, stre
     """mask: uint8 (or bool) tensor of n elements, or None."""
     _check(load().onebit_momentum_update(_ptr(m), _ptr(mask), _ptr(v), _ptr(x), _ptr(x_bf16), x.numel(), lr, eps,
                                          weight_decay, _stream(stream)), "onebit_momentum_update")
+
+
+def qsgd_quantize(g, bucket, bits, seed, codes, norms, stream=None):
+    _check(load().qsgd_quantize(_ptr(g), _dtype_code(g), g.numel(), int(bucket), int(bits), int(seed) & (2 ** 64 - 1),
+                                _ptr(codes), _ptr(norms), _stream(stream)), "qsgd_quantize")
+
+
+def qsgd_reduce(codes, norms, n, bucket, bits, out_f32=None, out_bf16=None, stream=None):
+    """codes: uint8 [W, stride] (or 1-D for one worker); norms: float32 [W, stride] (or 1-D)."""
+    W = codes.shape[0] if codes.dim() == 2 else 1
+    cs = codes.stride(0) if codes.dim() == 2 else 0
+    ns = norms.stride(0) if norms.dim() == 2 else 0
+    _check(load().qsgd_reduce(W, _ptr(codes), cs, _ptr(norms), ns, int(n), int(bucket), int(bits), _ptr(out_f32),
+                              _ptr(out_bf16), _stream(stream)), "qsgd_reduce")
 
 
 def qsdp_quantize(x_bf16, bucket, bits, seed, codes, bucket_min, bucket_max, stream=None):

@@ -18,6 +18,10 @@ Workloads (all synthetic; the pages' datasets and weights are not used):
               ragged), bf16 copy of x, 3 steps.
   qsdp        1.3e9 bf16 weights ~ N(0, 0.02), buckets of 1024, 4- and 8-bit codes,
               64 seeds.
+  qsgd        the gradients of the same 1.3e9-parameter model, bf16, N(0, 1) scaled
+              per block of 2^20 elements by 10^U(-4, -2) (layers differ in gradient
+              scale), one vector per worker; W = 8 workers, each owning a
+              bucket-aligned shard of ceil(n / 8 / 1024) buckets; 4- and 8-bit codes.
 "N(mu, s)" means standard deviation s.
 
 Seeds: workload k uses base seed 1000*k; step t adds t; worker w adds 100*w.
@@ -32,7 +36,7 @@ import torch
 
 HYPER = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, bias_correction=False)
 
-SEED_TINY, SEED_BERT, SEED_ALLREDUCE, SEED_GPT2, SEED_QSDP = 0, 1000, 2000, 3000, 4000
+SEED_TINY, SEED_BERT, SEED_ALLREDUCE, SEED_GPT2, SEED_QSDP, SEED_QSGD = 0, 1000, 2000, 3000, 4000, 5000
 
 
 # ----------------------------------------------------------------- tables
@@ -166,6 +170,20 @@ class QsdpWorkload:
     base_seed: int = SEED_QSDP
 
 
+@dataclass
+class QsgdWorkload:
+    n: int = 1_300_000_000
+    bucket: int = 1024
+    W: int = 8
+    block: int = 1 << 20
+    base_seed: int = SEED_QSGD
+
+    @property
+    def shard(self) -> int:
+        """Elements per worker's shard: a whole number of buckets."""
+        return -(-self.n // self.W // self.bucket) * self.bucket if self.n >= self.W * self.bucket else self.n
+
+
 # -------------------------------------------------------------- generators
 
 def _gen(device, seed: int) -> torch.Generator:
@@ -226,6 +244,19 @@ def qsdp_weights(wl: QsdpWorkload, device="cpu") -> torch.Tensor:
     """bf16 weights ~ N(0, std), returned as a bfloat16 tensor."""
     gen = _gen(device, wl.base_seed)
     return torch.randn(wl.n, generator=gen, device=device, dtype=torch.float32).mul_(wl.std).to(torch.bfloat16)
+
+
+def qsgd_gradient(wl: QsgdWorkload, worker: int, device="cpu", n: Optional[int] = None) -> torch.Tensor:
+    """bf16 gradient of one worker: N(0, 1) times a per-block scale 10^U(-4, -2)."""
+    n = wl.n if n is None else n
+    gen = _gen(device, wl.base_seed + 100 * worker)
+    nblk = -(-n // wl.block)
+    scale = torch.pow(10.0, torch.rand(nblk, generator=gen, device=device) * 2.0 - 4.0)
+    g = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+    g.view(-1)[: (n // wl.block) * wl.block].view(-1, wl.block).mul_(scale[: n // wl.block, None])
+    if n % wl.block:
+        g[(n // wl.block) * wl.block:].mul_(scale[-1])
+    return g.to(torch.bfloat16)
 
 
 def as_u16(t: torch.Tensor) -> np.ndarray:

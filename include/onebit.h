@@ -130,8 +130,9 @@ int64_t onebit_onepass_max_elements(void);
  * ONEBIT_PROFILE_CLASSES entries, nullable).  Classes: 0 warmup, 1/2/3 worker
  * compression pass 1 / one-pass / pass 2, 4 quantize, 5 dequantize, 6/7/8 server
  * pass 1 / one-pass / pass 2, 9 chunk-norm finalization of two-pass chunks, 10
- * momentum update.  Not thread-safe; diagnostics only. */
-#define ONEBIT_PROFILE_CLASSES 11
+ * momentum update, 11 QSGD quantize, 12 QSGD reduce.  Not thread-safe; diagnostics
+ * only. */
+#define ONEBIT_PROFILE_CLASSES 13
 void onebit_profile_begin(void);
 onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
 
@@ -192,6 +193,34 @@ onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *
 onebit_status_t onebit_momentum_update(float *m, const uint8_t *mask, const float *v, float *x,
                                        uint16_t *x_bf16, int64_t n, double lr, double eps,
                                        double weight_decay, void *stream);
+
+/* QSGD gradient quantizer, the gradient side of QSDP ([QSDP] "proposed method":
+ * gradients take the standard unbiased compressor of Alistarh et al. 2017; [QSGD]
+ * sec. 3.1), per bucket of `bucket` elements (the last one may be short):
+ *   norm = fl32( sqrt( sum g^2 ) )            (fp64 sum of exact squares, fp64 sqrt)
+ *   s = 2^(bits-1) - 1;  t = fl32(|g| / norm);  v = fl32(t * s);  l = floor(v);  p = v - l
+ *   u = Philox4x32-10(key = seed, counter = (i >> 2, 0, 0))[i & 3]      ([PHX])
+ *   level = l + (u < floor(p * 2^32));  code = (g < 0) << (bits-1) | level
+ *   a bucket of zeros: norm 0, codes 0.
+ * g: [n] fp32, bf16 or fp16 (widened exactly), 16-byte aligned.  codes: uint8, bits 4:
+ * two per byte, even element in the low nibble, ceil(n/2) bytes, pad nibble 0; bits
+ * 8: n bytes; 16-byte aligned.  norms: fp32 [ceil(n/bucket)] out.  1 <= bucket <=
+ * 65536, bucket even when bits == 4.  Use a seed distinct from the weights'. */
+onebit_status_t qsgd_quantize(const void *g, onebit_dtype_t g_dtype, int64_t n, int bucket, int bits,
+                              uint64_t seed, uint8_t *codes, float *norms, void *stream);
+
+/* Decode and average W workers' QSGD streams of the same n elements (the shard
+ * owner's half of a quantized reduce-scatter; W = 1 is plain decoding):
+ *   y_{w,i} = +-level * fl32(norm_{w,b} / s)   (exact in fp64; sign from the code's top bit)
+ *   out_i = fl32( (sum_{w=0..W-1} y_{w,i}) / W )          (fp64 sum in worker order)
+ * codes: worker w's codes at codes + w * code_stride bytes (code_stride >= code
+ * bytes of n and a multiple of 16 when W > 1; base 16-byte aligned).  norms:
+ * worker w's at norms + w * norm_stride (>= ceil(n/bucket) when W > 1).  out_f32
+ * [n] and/or out_bf16 [n] (round to nearest even), at least one, 16-byte aligned.
+ * 1 <= W <= 65536. */
+onebit_status_t qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const float *norms,
+                            int64_t norm_stride, int64_t n, int bucket, int bits, float *out_f32,
+                            uint16_t *out_bf16, void *stream);
 
 /* QSDP-style unbiased stochastic rounding of bf16 weights ([QSDP] "proposed
  * method"), per bucket of `bucket` elements (the last one may be short):

@@ -242,7 +242,7 @@ def qsgd_quantize(g, *, bucket, bits, seed, first_index=0):
     if g.dtype == np.uint16:
         dt = 1
     else:
-        g = _f32(g)
+        g = _widen(g)
         dt = 0
     g = np.ascontiguousarray(g)
     n = g.size

@@ -57,9 +57,9 @@
  *    fp32); s = 2^(bits-1) - 1 levels of |g| / norm; code = sign bit (top bit of
  *    the code, set iff g < 0) and the level below it; same Philox stream layout as
  *    the weights (the caller picks a different seed); dequantized value
- *    fl32(fl32(level * norm) / s), negated for a set sign bit; several workers'
- *    values are averaged as the server stage does (fp64 sum in worker order, fp64
- *    divide by W, one rounding).
+ *    level * fl32(norm / s) (exact in fp64), negated for a set sign bit; several
+ *    workers' values are averaged as the server stage does (fp64 sum in worker
+ *    order, fp64 divide by W, one rounding to fp32).
  */
 #include <math.h>
 #include <stddef.h>
@@ -608,17 +608,20 @@ int oracle_qsgd_quantize(const void *g, int g_dtype, int64_t n, int bucket, int 
     return ORACLE_OK;
 }
 
-/* The value worker w sent for element i. */
-static float qsgd_value(const uint8_t *codes, const float *norms, int64_t i, int bucket, int nbits)
+/* The value worker w sent for element i: level times the bucket's level spacing,
+ * exact in fp64 (at most 7 + 24 significant bits). */
+static double qsgd_value(const uint8_t *codes, const float *norms, int64_t i, int bucket, int nbits)
 {
     const uint32_t s = (1u << (nbits - 1)) - 1u;
     const uint32_t code = nbits == 8 ? codes[i] : (uint32_t)((codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu);
     const uint32_t level = code & s;
-    const float y = ((float)level * norms[i / bucket]) / (float)s;
+    const float step = norms[i / bucket] / (float)s; /* the bucket's level spacing */
+    const double y = (double)level * (double)step;
     return (code >> (nbits - 1)) ? -y : y;
 }
 
-/* [QSGD] decoding, averaged over W workers' streams (the reduce half of a quantized
+/* [QSGD] decoding (value = level * norm / s, formed exactly as level times the
+ * bucket's level spacing fl32(norm / s)), averaged over W workers' streams (the reduce half of a quantized
  * gradient reduce-scatter): out_i = fl32( (sum_w y_{w,i}) / W ), fp64 sum in worker
  * order.  Worker w's codes start at codes + w * code_stride bytes, its norms at
  * norms + w * norm_stride.  W = 1 is plain dequantization. */
@@ -634,7 +637,7 @@ int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const f
     for (int64_t i = 0; i < n; ++i) {
         double acc = 0.0;
         for (int w = 0; w < W; ++w)
-            acc += (double)qsgd_value(codes + (int64_t)w * code_stride, norms + (int64_t)w * norm_stride, i, bucket,
+            acc += qsgd_value(codes + (int64_t)w * code_stride, norms + (int64_t)w * norm_stride, i, bucket,
                                       nbits);
         const float y = (float)(acc / (double)W);
         if (out_f32)

@@ -1,0 +1,172 @@
+"""GPU parity of the QSGD gradient quantizer and of the W-worker decode/average
+against the oracle (codes, norms and decoded values bit for bit).
+
+Small cases cover the 1024-element fast path and the generic path (bucket sizes
+2, 30, 64, 1000, 4096), ragged last buckets, odd n (4-bit pad nibble), fp32 /
+bf16 / fp16 gradients, zero and single-value buckets, signed zeros, buckets whose
+ratios are exact levels, and a wide dynamic range.  The reduce covers W = 1, 2,
+3, 8, buckets that are and are not multiples of 8, n not a multiple of 8, fp32
+and bf16 outputs, padded worker rows.  Full size: the 1.3e9-parameter gradient of
+8 workers, bucket 1024, sampled buckets of every worker and sampled buckets of two
+shards' averages (the first and the ragged last).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from error_compensated_bit_amd import onebit as ob
+from error_compensated_bit_amd import workloads as W
+from gpu_helpers import DEV, host
+from parity import assert_exact, check_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+def code_bytes(n, bits):
+    return (n + 1) // 2 if bits == 4 else n
+
+
+def special_gradient(n, rng):
+    g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 2, n)).astype(np.float32)
+    if n >= 4096:
+        g[0:64] = 0.0                                      # zero bucket for buckets <= 64
+        g[64:128] = 0.0
+        g[100] = -889 / 16                                 # lone value
+        g[128:192] = np.tile(np.array([0.0, -0.0], np.float32), 32)
+        g[256:320] = 0.0
+        g[256:259] = [2.0, -3.0, 6.0]                      # |.| = 7: exact 4-bit levels
+        g[1024:2048] *= 1e-30                              # tiny bucket
+    return g
+
+
+def to_device(g, dt):
+    t = torch.from_numpy(g).to(DEV)
+    if dt == "bf16":
+        t = t.to(torch.bfloat16)
+        return t, host(t)
+    if dt == "f16":
+        t = t.to(torch.float16)
+        return t, t.cpu().numpy()
+    return t, g
+
+
+@pytest.mark.parametrize("bucket", [1024, 2, 30, 64, 1000, 4096])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantize_parity(bucket, bits):
+    for dt in ("f32", "bf16", "f16"):
+        for n in (1, 2 * bucket + 7, 9 * 1024 + 333):
+            if bits == 4 and n % 2 == 1 and n > 1:
+                pass                                       # odd n: pad nibble
+            rng = np.random.default_rng(n * 7 + bucket + bits)
+            g = special_gradient(n, rng)
+            if dt == "f16":
+                g = np.clip(g, -6e4, 6e4)
+            gd, gh = to_device(g, dt)
+            nb = (n + bucket - 1) // bucket
+            codes = torch.full((code_bytes(n, bits) + 16,), 0xAB, dtype=torch.uint8, device=DEV)
+            norms = torch.zeros(nb, device=DEV)
+            seed = 1234 + n
+            ob.qsgd_quantize(gd, bucket, bits, seed, codes, norms)
+            rc, rn = oracle.qsgd_quantize(gh, bucket=bucket, bits=bits, seed=seed)
+            torch.cuda.synchronize()
+            tag = f"bucket {bucket} bits {bits} {dt} n {n}"
+            assert_exact(f"{tag} norms", host(norms), rn)
+            got = host(codes)
+            assert_exact(f"{tag} codes", got[:rc.size], rc)
+            assert np.all(got[rc.size:] == 0xAB), f"{tag}: wrote past the codes"
+            y = torch.zeros(n, device=DEV)
+            ob.qsgd_reduce(codes, norms, n, bucket, bits, out_f32=y)
+            ry, _ = oracle.qsgd_reduce(rc, rn, n, bucket=bucket, bits=bits)
+            torch.cuda.synchronize()
+            assert_exact(f"{tag} decoded", host(y), ry)
+    say(f"  qsgd quantize bucket {bucket} bits {bits}: fp32 / bf16 / fp16 match")
+
+
+@pytest.mark.parametrize("workers", [1, 2, 3, 8])
+@pytest.mark.parametrize("bucket,bits", [(1024, 4), (1000, 8), (30, 4), (2, 8), (4096, 4)])
+def test_reduce_parity(workers, bucket, bits):
+    n = 3 * 4096 + 13
+    nb = (n + bucket - 1) // bucket
+    stride = (code_bytes(n, bits) + 15) // 16 * 16 + 32      # padded worker rows
+    codes = torch.zeros((workers, stride), dtype=torch.uint8, device=DEV)
+    norms = torch.zeros((workers, nb + 3), device=DEV)
+    rcs, rns = [], []
+    for w in range(workers):
+        g = (np.random.default_rng(50 + w).standard_normal(n) * 10.0 ** (-w % 4)).astype(np.float32)
+        gd = torch.from_numpy(g).to(DEV).to(torch.bfloat16)
+        ob.qsgd_quantize(gd, bucket, bits, 99 + w, codes[w], norms[w])
+        rc, rn = oracle.qsgd_quantize(host(gd), bucket=bucket, bits=bits, seed=99 + w)
+        rcs.append(np.pad(rc, (0, stride - rc.size)))
+        rns.append(np.pad(rn, (0, 3)))
+    y = torch.zeros(n, device=DEV)
+    yb = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    ob.qsgd_reduce(codes, norms, n, bucket, bits, out_f32=y, out_bf16=yb)
+    ry, ryb = oracle.qsgd_reduce(np.stack(rcs), np.stack(rns), n, bucket=bucket, bits=bits, want_bf16=True)
+    torch.cuda.synchronize()
+    tag = f"W={workers} bucket {bucket} bits {bits}"
+    assert_exact(f"{tag} codes", host(codes), np.stack(rcs))
+    assert_exact(f"{tag} mean", host(y), ry)
+    check_bf16(f"{tag} mean bf16", host(yb), ryb)
+
+
+def test_argument_errors():
+    g = torch.zeros(64, device=DEV)
+    codes = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    norms = torch.zeros(4, device=DEV)
+    for kw in (dict(bucket=3, bits=4), dict(bucket=16, bits=6), dict(bucket=0, bits=8)):
+        with pytest.raises(ob.OnebitError) as ei:
+            ob.qsgd_quantize(g, kw["bucket"], kw["bits"], 0, codes, norms)
+        assert ei.value.status == ob.ONEBIT_ERR_INVALID
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.qsgd_quantize(g[1:], 16, 8, 0, codes, norms)
+    assert ei.value.status == ob.ONEBIT_ERR_ALIGN
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.qsgd_reduce(codes, norms, 64, 16, 8)                        # no output
+    assert ei.value.status == ob.ONEBIT_ERR_INVALID
+    rows = torch.zeros((2, 72), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ob.OnebitError) as ei:                          # row stride not a multiple of 16
+        ob.qsgd_reduce(rows, torch.zeros((2, 4), device=DEV), 64, 16, 8, out_f32=torch.zeros(64, device=DEV))
+    assert ei.value.status == ob.ONEBIT_ERR_ALIGN
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_full_size_eight_workers(bits):
+    q = W.QsgdWorkload()
+    n, bucket, nb = q.n, q.bucket, (q.n + q.bucket - 1) // q.bucket
+    cb = code_bytes(n, bits)
+    stride = (cb + 15) // 16 * 16
+    codes = torch.zeros((q.W, stride), dtype=torch.uint8, device=DEV)
+    norms = torch.zeros((q.W, nb), device=DEV)
+    per = 2 if bits == 4 else 1
+    sample_b = sorted({0, nb - 1, nb - 2} | set(int(b) for b in np.random.default_rng(bits).choice(nb, 29, replace=False)))
+    keep = {}
+    for w in range(q.W):
+        gd = W.qsgd_gradient(q, w, device=DEV)
+        seed = 7000 + w
+        ob.qsgd_quantize(gd, bucket, bits, seed, codes[w], norms[w])
+        torch.cuda.synchronize()
+        for b in sample_b:
+            lo, hi = b * bucket, min((b + 1) * bucket, n)
+            gs = host(gd[lo:hi])
+            rc, rn = oracle.qsgd_quantize(gs, bucket=bucket, bits=bits, seed=seed, first_index=lo)
+            assert_exact(f"worker {w} bucket {b} codes", host(codes[w, lo // per:(hi + per - 1) // per]), rc)
+            assert_exact(f"worker {w} bucket {b} norm", host(norms[w, b:b + 1]), rn)
+        del gd
+        say(f"  qsgd{bits} worker {w}: {len(sample_b)} buckets match")
+    for s in (0, q.W - 1):
+        lo = s * q.shard
+        hi = min(lo + q.shard, n)
+        m = hi - lo
+        y = torch.zeros(m, device=DEV)
+        ob.qsgd_reduce(codes[:, lo // per:], norms[:, lo // bucket:], m, bucket, bits, out_f32=y)
+        torch.cuda.synchronize()
+        sb = (m + bucket - 1) // bucket
+        for b in sorted({0, sb - 1} | set(int(x) for x in np.random.default_rng(s).choice(sb, 14, replace=False))):
+            blo, bhi = b * bucket, min((b + 1) * bucket, m)
+            gb = (lo + blo) // bucket
+            rc = np.stack([host(codes[w, (lo + blo) // per:(lo + bhi + per - 1) // per]) for w in range(q.W)])
+            rn = np.stack([host(norms[w, gb:gb + 1]) for w in range(q.W)])
+            ry, _ = oracle.qsgd_reduce(rc, rn, bhi - blo, bucket=bucket, bits=bits)
+            assert_exact(f"shard {s} bucket {b} mean", host(y[blo:bhi]), ry)
+        say(f"  qsgd{bits} shard {s} ({m} elements): sampled buckets match")

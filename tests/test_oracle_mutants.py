@@ -100,8 +100,8 @@ MUTANTS = [
     ("qsgd s + 1 levels", "const float u = t * (float)s;", "const float u = t * (float)(s + 1);", _qsgd),
     ("qsgd norm not square-rooted", "const float norm = (float)sqrt(bucket_sum_squares(v, len));",
      "const float norm = (float)bucket_sum_squares(v, len);", _qsgd),
-    ("qsgd decode scale", "((float)level * norms[i / bucket]) / (float)s;",
-     "((float)level * norms[i / bucket]) / (float)(s + 1);", _qsgd),
+    ("qsgd decode scale", "const float step = norms[i / bucket] / (float)s;",
+     "const float step = norms[i / bucket] / (float)(s + 1);", _qsgd),
     ("qsgd pack nibble order", "codes[i >> 1] |= (uint8_t)((i & 1) ? code << 4 : code);",
      "codes[i >> 1] |= (uint8_t)((i & 1) ? code : code << 4);", _qsgd),
     ("qsgd decode nibble order", "(uint32_t)((codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu)",

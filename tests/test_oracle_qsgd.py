@@ -52,11 +52,12 @@ def test_integer_ratio_buckets_are_exact(as_bf16):
 
 
 def test_lone_value_zero_bucket_signed_zero_and_padding():
-    g = np.array([0, 0, -3.5, 0, 0, 0, 0, 0, -0.0, 0.0, -0.0, 0, 1e-30, 0, 0], np.float32)
+    big, tiny = np.float32(-889 / 16), np.float32(889 * 2.0 ** -110)   # 889 = 7 * 127: level spacings exact
+    g = np.array([0, 0, big, 0, 0, 0, 0, 0, -0.0, 0.0, -0.0, 0, tiny, 0, 0], np.float32)
     for bits in (4, 8):
         s = 2 ** (bits - 1) - 1
         codes, norms = oracle.qsgd_quantize(g, bucket=4, bits=bits, seed=3)
-        np.testing.assert_array_equal(norms, np.array([3.5, 0, 0, 1e-30], np.float32))
+        np.testing.assert_array_equal(norms, np.array([-big, 0, 0, tiny], np.float32))
         c = unpack4(codes, g.size) if bits == 4 else codes
         expect = np.zeros(g.size, np.uint8)
         expect[2] = (1 << (bits - 1)) | s
@@ -66,7 +67,7 @@ def test_lone_value_zero_bucket_signed_zero_and_padding():
             assert codes.size == 8 and codes[-1] >> 4 == 0          # pad nibble of the odd tail
         y, _ = oracle.qsgd_reduce(codes, norms, g.size, bucket=4, bits=bits)
         ref = np.zeros(g.size, np.float32)
-        ref[2], ref[12] = -3.5, np.float32(1e-30)
+        ref[2], ref[12] = big, tiny
         np.testing.assert_array_equal(y, ref)
         assert not np.signbit(y[8]) and not np.signbit(y[10])     # -0 is sent as +0
 
