@@ -39,6 +39,7 @@ def _load():
         lib.oracle_decompress.argtypes = [_P, _I64, _P, _P, _P]
         lib.oracle_qsgd_quantize.argtypes = [_P, _I, _I64, _I, _I, C.c_uint64, _I64, _P, _P]
         lib.oracle_qsgd_reduce.argtypes = [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P]
+        lib.oracle_loco_quantize.argtypes = [_P, _I, _P, _I64, _I, _I, _D, C.c_uint64, _P, _P]
         lib.oracle_momentum_update.argtypes = [_P, _P, _P, _P, _P, _I64, _D, _D, _D]
         lib.oracle_philox4x32_10.argtypes = [_P, _P, _P]
         lib.oracle_philox4x32_10.restype = None
@@ -50,6 +51,7 @@ def _load():
         lib.oracle_f32_to_bf16.restype = C.c_uint16
         for name in ("oracle_adam_warmup_step", "oracle_compress_update", "oracle_server_reduce",
                      "oracle_momentum_update", "oracle_qsgd_quantize", "oracle_qsgd_reduce",
+                     "oracle_loco_quantize",
                      "oracle_decompress", "oracle_qsdp_quantize", "oracle_qsdp_dequantize"):
             getattr(lib, name).restype = C.c_int
         _lib = lib
@@ -267,3 +269,22 @@ def qsgd_reduce(codes, norms, n, *, bucket, bits, want_bf16=False):
     _check(lib.oracle_qsgd_reduce(W, _ptr(codes), codes.shape[1], _ptr(norms), norms.shape[1], n, bucket, bits,
                                   _ptr(out), _ptr(ob)), "qsgd_reduce")
     return out[:n], (ob[:n] if want_bf16 else None)
+
+
+def loco_quantize(g, err_avg, *, bucket, bits, beta, seed):
+    """LoCo-style step, err_avg (float32) updated in place.  Returns (codes, norms)."""
+    lib = _load()
+    if g.dtype == np.uint16:
+        dt = 1
+    else:
+        g = _widen(g)
+        dt = 0
+    g = np.ascontiguousarray(g)
+    n = g.size
+    nb = (n + bucket - 1) // bucket
+    nbytes = (n + 1) // 2 if bits == 4 else n
+    codes = np.zeros(max(nbytes, 1), dtype=np.uint8)
+    norms = np.zeros(max(nb, 1), dtype=np.float32)
+    _check(lib.oracle_loco_quantize(_ptr(g), dt, _ptr(err_avg), n, bucket, bits, beta, seed, _ptr(codes),
+                                    _ptr(norms)), "loco_quantize")
+    return codes[:nbytes], norms[:nb]

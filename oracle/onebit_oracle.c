@@ -31,6 +31,12 @@
  *         SGD via Gradient Quantization and Encoding", NeurIPS 2017, sec. 3.1 (the
  *         stochastic quantizer Q_s) and its bucketed form; named by [QSDP] as the
  *         standard unbiased compressor applied to gradients.
+ *  [LOCO] shd-paper.top summary of "LoCo: Low-Bit Communication Adaptor for Large-scale
+ *         Model Training", core points and method details: before compressing, the
+ *         local gradient is compensated with a moving average of the historical
+ *         compensation errors, which estimates the current compression error.  The
+ *         page gives no formula, window or weights (parity unpinned: the steps
+ *         below are this oracle's reading, pinned only by its special cases).
  *  [PHX]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
  *         SC'11, section 4 (the Philox-4x32 bijection, 10 rounds).
  *
@@ -646,4 +652,45 @@ int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const f
             out_bf16[i] = oracle_f32_to_bf16(y);
     }
     return ORACLE_OK;
+}
+
+/* ------------------------------- O8: LoCo-style compensated gradient quantizer
+ * [LOCO] method details, steps 2-4: estimate the compression error by the moving
+ * average of past errors, add it to the gradient, compress the sum.  Reading
+ * (binary32, unfused; beta and 1 - beta formed in binary64, rounded once):
+ *   h = fl32(g + err_avg);  (codes, norms) = QSGD of h, as O7;  y = decoded h as
+ *   the W = 1 decode of O7;  err_avg = fl32( fl32(beta * err_avg) + fl32((1 - beta) * (h - y)) ).
+ * beta = 0 is plain error feedback (err_avg = h - y).  err_avg: fp32 [n] in place.
+ */
+int oracle_loco_quantize(const void *g, int g_dtype, float *err_avg, int64_t n, int bucket, int nbits, double beta_d,
+                         uint64_t seed, uint8_t *codes, float *norms)
+{
+    if (n < 0 || (g_dtype != 0 && g_dtype != 1))
+        return ORACLE_ERR_INVALID;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!g || !err_avg)
+        return ORACLE_ERR_INVALID;
+    float *h = (float *)malloc((size_t)n * sizeof(float));
+    float *y = (float *)malloc((size_t)n * sizeof(float));
+    if (!h || !y) {
+        free(h);
+        free(y);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        const float gi = g_dtype == 1 ? oracle_bf16_to_f32(((const uint16_t *)g)[i]) : ((const float *)g)[i];
+        h[i] = gi + err_avg[i];
+    }
+    int rc = oracle_qsgd_quantize(h, 0, n, bucket, nbits, seed, 0, codes, norms);
+    if (rc == ORACLE_OK)
+        rc = oracle_qsgd_reduce(1, codes, 0, norms, 0, n, bucket, nbits, y, NULL);
+    if (rc == ORACLE_OK) {
+        const float beta = (float)beta_d, one_minus_beta = (float)(1.0 - beta_d);
+        for (int64_t i = 0; i < n; ++i)
+            err_avg[i] = beta * err_avg[i] + one_minus_beta * (h[i] - y[i]);
+    }
+    free(h);
+    free(y);
+    return rc;
 }

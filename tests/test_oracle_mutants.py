@@ -15,6 +15,7 @@ from oracle import build as obuild
 
 import test_oracle_compress as TC  # noqa: E402
 import test_oracle_qsdp as TQ
+import test_oracle_loco as TL
 import test_oracle_qsgd as TG
 import test_oracle_server as TS
 import test_oracle_warmup as TW
@@ -59,6 +60,12 @@ def _qsgd():
     TG.test_norm_is_the_rounded_exact_norm()
     TG.test_unbiased_and_variance_closed_form(4)
     TG.test_average_of_workers()
+
+
+def _loco():
+    TL.test_zero_average_is_plain_qsgd_and_error(4)
+    TL.test_beta_zero_is_error_feedback(8)
+    TL.test_moving_average_closed_form(0.9)
 
 
 def _finish():
@@ -107,6 +114,11 @@ MUTANTS = [
     ("qsgd decode nibble order", "(uint32_t)((codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu)",
      "(uint32_t)((codes[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xfu)", _qsgd),
     ("qsgd average not divided", "const float y = (float)(acc / (double)W);", "const float y = (float)acc;", _qsgd),
+    ("loco compensation sign", "h[i] = gi + err_avg[i];", "h[i] = gi - err_avg[i];", _loco),
+    ("loco weights swapped", "err_avg[i] = beta * err_avg[i] + one_minus_beta * (h[i] - y[i]);",
+     "err_avg[i] = one_minus_beta * err_avg[i] + beta * (h[i] - y[i]);", _loco),
+    ("loco error sign", "err_avg[i] = beta * err_avg[i] + one_minus_beta * (h[i] - y[i]);",
+     "err_avg[i] = beta * err_avg[i] + one_minus_beta * (y[i] - h[i]);", _loco),
     ("finish ignores the mask", "m[i] = m[i] * (mask[i] ? 1.0f : 0.0f);", "m[i] = m[i];", _finish),
     ("finish weight decay sign", "const float update = m[i] / (sqrtf(v[i]) + eps) + weight_decay * x[i];",
      "const float update = m[i] / (sqrtf(v[i]) + eps) - weight_decay * x[i];", _finish),
