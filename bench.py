@@ -111,13 +111,13 @@ def compress_setup(wl, dev):
 
 
 def onepass_elements(wl, plan):
-    """Elements of the chunks the one-pass kernel handles (chunks <= capacity tiles)."""
+    """Elements of the chunks the one-pass kernel handles: a chunk goes there when
+    its tiles fit the resident pipeline, i.e. it has at most
+    onebit_onepass_max_elements() elements."""
     import numpy as np
     from error_compensated_bit_amd import onebit as ob
-    cap = ob.onebit_plan_stats(plan)["coop_capacity"]
     lens = np.diff(wl.chunk_off)
-    tiles = np.maximum(1, (lens + 4095) // 4096)
-    return int(lens[tiles <= cap].sum())
+    return int(lens[lens <= ob.onebit_onepass_max_elements()].sum())
 
 
 def bench_compress(wl, steps, warmup, dev, bpe):
@@ -178,10 +178,15 @@ ONEPASS_SOURCE = os.path.join(ROOT, "error_compensated_bit_amd", "csrc", "compre
 CALIBRATION_FLOATS = 1 << 28          # 1 GiB copied by the profile mode
 
 
+# What the profiled one-pass kernel and its launch are built from: its source, the
+# headers it includes, the plan code that lays out its tiles, and the build flags.
+DIGEST_FILES = ("csrc/compress.hip", "csrc/device_common.h", "csrc/internal.h", "csrc/plan.hip", "build.py")
+
+
 def source_digest():
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "error_compensated_bit_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
+    for rel in DIGEST_FILES:
+        with open(os.path.join(ROOT, "error_compensated_bit_amd", rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -426,6 +431,11 @@ def secondary_rows(dev, args):
         br = qg.W * (bits / 8.0 + 4.0 / qg.bucket) + 4.0
         rows[f"qsgd{bits}_quantize"] = dict(elems_per_s=qg.n / tq, gbps=bq * qg.n / tq / 1e9)
         rows[f"qsgd{bits}_reduce_{qg.W}x{qg.shard}"] = dict(elems_per_s=qg.shard / tr, gbps=br * qg.shard / tr / 1e9)
+        if bits == 4:
+            err = torch.zeros(qg.n, device=dev)
+            tl, _ = timed(lambda: ob.loco_quantize(gq, err, qg.bucket, bits, 0.9, 7, codes[0], norms[0]), steps, 1)
+            rows["loco4_quantize"] = dict(elems_per_s=qg.n / tl, gbps=(bq + 8.0) * qg.n / tl / 1e9)
+            del err
         del codes, out
     del gq, norms
     torch.cuda.empty_cache()

@@ -88,7 +88,8 @@ enum ProfClass {
     kProfMomentumUpdate = 10,
     kProfQsgdQuantize = 11,
     kProfQsgdReduce = 12,
-    kProfClasses = 13
+    kProfLocoQuantize = 13,
+    kProfClasses = 14
 };
 void prof_before(int cls, hipStream_t s);
 void prof_after(hipStream_t s);

@@ -1,7 +1,9 @@
 // qsgd.hip -- the gradient side of QSDP: the standard unbiased gradient
 // compressor (QSDP review, "proposed method", naming Alistarh et al. 2017; QSGD,
 // sec. 3.1) and the decode-and-average of W workers' streams that the shard
-// owner of a quantized reduce-scatter performs.
+// owner of a quantized reduce-scatter performs.  The LoCo variant (LoCo summary,
+// method details) quantizes g + err, where err is a moving average of past
+// compression errors, and updates that average in the same pass.
 //
 // Per bucket of the gradient: norm = ||g||_2 (fp64 double-double sum of squares,
 // fp64 square root, one rounding to fp32); s = 2^(bits-1) - 1 levels of |g|/norm,
@@ -20,6 +22,8 @@ namespace onebit {
 
 struct GArgs {
     const void *g;
+    float *err;          // LoCo: moving average of the compression error, in place
+    float beta, obeta;   // LoCo: its weights beta and 1 - beta
     int64_t n;
     int64_t n_buckets;
     int32_t bucket;
@@ -48,6 +52,17 @@ __device__ __forceinline__ uint32_t qsgd_code(float g, float norm, uint32_t u) {
     return (g < 0.0f ? (1u << (BITS - 1)) : 0u) | level;
 }
 
+// LoCo: the new moving average of the compression error, from the old one, the
+// compensated value h, its code and the bucket's level spacing (decode as the
+// W = 1 average: +-fl32(level * spacing)).
+template <int BITS>
+__device__ __forceinline__ float loco_update(const GArgs &a, float ea, float h, uint32_t code, float step) {
+    constexpr uint32_t S = (1u << (BITS - 1)) - 1u;
+    const float y = mul_rn((float)(code & S), step);
+    const float err = sub_rn(h, (code >> (BITS - 1)) ? -y : y);
+    return add_rn(mul_rn(a.beta, ea), mul_rn(a.obeta, err));
+}
+
 __device__ __forceinline__ float norm_of(DD acc) {
     const DD t = wave_sum_dd(acc);
     return (float)__dsqrt_rn(t.hi);
@@ -56,7 +71,7 @@ __device__ __forceinline__ float norm_of(DD acc) {
 // Buckets of 1024: one wave per bucket, lane l owns the 16 consecutive elements
 // 16l..16l+15 (two or four 16-byte loads), kept in registers between the norm and
 // the codes; four Philox calls per lane; one 8- or 16-byte store of codes.
-template <int BITS, int GT>
+template <int BITS, int GT, bool LOCO>
 __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -91,6 +106,22 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) f[q] = (k0 + q < len) ? load_grad<GT>(a.g, base + k0 + q) : 0.0f;
         }
+        float ea[LOCO ? 16 : 1];
+        if (LOCO) {
+            if (k0 + 15 < len) {
+                const float4 *src = reinterpret_cast<const float4 *>(a.err + base + k0);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float4 v = src[h];
+                    ea[4 * h] = v.x; ea[4 * h + 1] = v.y; ea[4 * h + 2] = v.z; ea[4 * h + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) ea[q] = (k0 + q < len) ? a.err[base + k0 + q] : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) f[q] = add_rn(f[q], ea[q]);     // compensated gradient h
+        }
         DD acc{0.0, 0.0};
 #pragma unroll
         for (int q = 0; q < 16; ++q) dd_add_term(acc, (double)f[q] * (double)f[q]);   // each square exact
@@ -109,6 +140,18 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q)
             if (k0 + q >= len) code[q] = 0;
+        if (LOCO) {
+            const float st = __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
+#pragma unroll
+            for (int q = 0; q < 16; ++q) ea[q] = loco_update<BITS>(a, ea[q], f[q], code[q], st);
+            if (k0 + 15 < len) {
+                float4 *dst = reinterpret_cast<float4 *>(a.err + base + k0);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) dst[h] = make_float4(ea[4 * h], ea[4 * h + 1], ea[4 * h + 2], ea[4 * h + 3]);
+            } else {
+                for (int q = 0; q < len - k0; ++q) a.err[base + k0 + q] = ea[q];
+            }
+        }
         if (BITS == 4) {
             uint2 pk;
             pk.x = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12) | (code[4] << 16) | (code[5] << 20) |
@@ -137,10 +180,17 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
     }
 }
 
+// The value that is quantized: g, or with LoCo the compensated h = g + err.
+template <int GT, bool LOCO>
+__device__ __forceinline__ float value_at(const GArgs &a, int64_t i) {
+    const float g = load_grad<GT>(a.g, i);
+    return LOCO ? add_rn(g, a.err[i]) : g;
+}
+
 // Any bucket size (even for 4-bit codes): one wave per bucket, a norm pass and a
 // code pass over lane-strided elements (the bucket is in cache for the second);
 // each lane writes whole bytes, one Philox call per element.
-template <int BITS, int GT>
+template <int BITS, int GT, bool LOCO>
 __global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -150,11 +200,12 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
         const int32_t len = (int32_t)min((int64_t)a.bucket, a.n - base);
         DD acc{0.0, 0.0};
         for (int k = lane; k < len; k += 64) {
-            const double v = (double)load_grad<GT>(a.g, base + k);
+            const double v = (double)value_at<GT, LOCO>(a, base + k);
             dd_add_term(acc, v * v);
         }
         const float norm = norm_of(acc);
         if (lane == 0) a.norms[b] = norm;
+        const float st = LOCO ? __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u)) : 0.0f;
         const int step = BITS == 4 ? 2 : 1;
         for (int k = step * lane; k < len; k += 64 * step) {
             uint32_t byte = 0;
@@ -163,7 +214,10 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
                 const uint64_t blk = (uint64_t)i >> 2;
                 const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
                 const uint32_t w = (i & 3) == 0 ? r.a : (i & 3) == 1 ? r.b : (i & 3) == 2 ? r.c : r.d;
-                byte |= qsgd_code<BITS>(load_grad<GT>(a.g, i), norm, w) << (4 * q);
+                const float h = value_at<GT, LOCO>(a, i);
+                const uint32_t code = qsgd_code<BITS>(h, norm, w);
+                if (LOCO) a.err[i] = loco_update<BITS>(a, a.err[i], h, code, st);
+                byte |= code << (4 * q);
             }
             a.codes[BITS == 4 ? ((base + k) >> 1) : (base + k)] = (uint8_t)byte;
         }
@@ -327,22 +381,63 @@ static int device_cus() {
     return cus;
 }
 
-template <int BITS, int GT>
+template <int BITS, int GT, bool LOCO>
 static void launch_quantize(const GArgs &a, unsigned grid, hipStream_t s) {
     if (a.bucket == 1024)
-        hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO>), dim3(grid), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((k_qsgd_quantize_generic<BITS, GT>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_qsgd_quantize_generic<BITS, GT, LOCO>), dim3(grid), dim3(256), 0, s, a);
 }
 
-template <int BITS>
+template <int BITS, bool LOCO>
 static void launch_quantize_dt(const GArgs &a, onebit_dtype_t dt, unsigned grid, hipStream_t s) {
     if (dt == ONEBIT_BF16)
-        launch_quantize<BITS, kGradBF16>(a, grid, s);
+        launch_quantize<BITS, kGradBF16, LOCO>(a, grid, s);
     else if (dt == ONEBIT_F16)
-        launch_quantize<BITS, kGradF16>(a, grid, s);
+        launch_quantize<BITS, kGradF16, LOCO>(a, grid, s);
     else
-        launch_quantize<BITS, kGradF32>(a, grid, s);
+        launch_quantize<BITS, kGradF32, LOCO>(a, grid, s);
+}
+
+// Validation and launch shared by the plain and the LoCo quantizer.
+static onebit_status_t quantize_entry(const void *g, onebit_dtype_t g_dtype, float *err, double beta, int64_t n,
+                                      int bucket, int bits, uint64_t seed, uint8_t *codes, float *norms,
+                                      void *stream) {
+    if (n < 0 || bucket < 1 || bucket > 65536 || (bits != 4 && bits != 8)) return ONEBIT_ERR_INVALID;
+    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
+    if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
+    if (n == 0) return ONEBIT_OK;
+    if (!g || !codes || !norms) return ONEBIT_ERR_INVALID;
+    if (!aligned16(g) || !aligned16(codes) || !aligned_to(norms, 4) || (err && !aligned16(err)))
+        return ONEBIT_ERR_ALIGN;
+    GArgs a{};
+    a.g = g;
+    a.err = err;
+    a.beta = (float)beta;
+    a.obeta = (float)(1.0 - beta);
+    a.n = n;
+    a.n_buckets = (n + bucket - 1) / bucket;
+    a.bucket = bucket;
+    a.k0 = (uint32_t)seed;
+    a.k1 = (uint32_t)(seed >> 32);
+    a.codes = codes;
+    a.norms = norms;
+    int64_t blocks = (a.n_buckets + 3) / 4;
+    const int64_t cap = (int64_t)device_cus() * 32;
+    if (blocks > cap) blocks = cap;
+    const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    prof_before(err ? kProfLocoQuantize : kProfQsgdQuantize, s);
+    if (bits == 4 && err)
+        launch_quantize_dt<4, true>(a, g_dtype, grid, s);
+    else if (bits == 4)
+        launch_quantize_dt<4, false>(a, g_dtype, grid, s);
+    else if (err)
+        launch_quantize_dt<8, true>(a, g_dtype, grid, s);
+    else
+        launch_quantize_dt<8, false>(a, g_dtype, grid, s);
+    prof_after(s);
+    return hip_status(hipGetLastError());
 }
 
 template <int BITS>
@@ -363,33 +458,15 @@ using namespace onebit;
 
 extern "C" onebit_status_t qsgd_quantize(const void *g, onebit_dtype_t g_dtype, int64_t n, int bucket, int bits,
                                          uint64_t seed, uint8_t *codes, float *norms, void *stream) {
-    if (n < 0 || bucket < 1 || bucket > 65536 || (bits != 4 && bits != 8)) return ONEBIT_ERR_INVALID;
-    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
-    if (bits == 4 && (bucket & 1)) return ONEBIT_ERR_INVALID;
-    if (n == 0) return ONEBIT_OK;
-    if (!g || !codes || !norms) return ONEBIT_ERR_INVALID;
-    if (!aligned16(g) || !aligned16(codes) || !aligned_to(norms, 4)) return ONEBIT_ERR_ALIGN;
-    GArgs a{};
-    a.g = g;
-    a.n = n;
-    a.n_buckets = (n + bucket - 1) / bucket;
-    a.bucket = bucket;
-    a.k0 = (uint32_t)seed;
-    a.k1 = (uint32_t)(seed >> 32);
-    a.codes = codes;
-    a.norms = norms;
-    int64_t blocks = (a.n_buckets + 3) / 4;
-    const int64_t cap = (int64_t)device_cus() * 32;
-    if (blocks > cap) blocks = cap;
-    const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    prof_before(kProfQsgdQuantize, s);
-    if (bits == 4)
-        launch_quantize_dt<4>(a, g_dtype, grid, s);
-    else
-        launch_quantize_dt<8>(a, g_dtype, grid, s);
-    prof_after(s);
-    return hip_status(hipGetLastError());
+    return quantize_entry(g, g_dtype, nullptr, 0.0, n, bucket, bits, seed, codes, norms, stream);
+}
+
+extern "C" onebit_status_t loco_quantize(const void *g, onebit_dtype_t g_dtype, float *err_avg, int64_t n, int bucket,
+                                         int bits, double beta, uint64_t seed, uint8_t *codes, float *norms,
+                                         void *stream) {
+    if (n > 0 && !err_avg) return ONEBIT_ERR_INVALID;
+    if (!(beta >= 0.0 && beta <= 1.0)) return ONEBIT_ERR_INVALID;
+    return quantize_entry(g, g_dtype, err_avg, beta, n, bucket, bits, seed, codes, norms, stream);
 }
 
 extern "C" onebit_status_t qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const float *norms,

@@ -43,6 +43,7 @@ _SIGS = {
     "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
     "qsgd_quantize": (_I, [_P, _I, _I64, _I, _I, _U64, _P, _P, _P]),
     "qsgd_reduce": (_I, [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P, _P]),
+    "loco_quantize": (_I, [_P, _I, _P, _I64, _I, _I, _D, _U64, _P, _P, _P]),
     "qsdp_quantize": (_I, [_P, _I64, _I, _I, _U64, _P, _P, _P, _P]),
     "qsdp_dequantize": (_I, [_P, _P, _P, _I64, _I, _I, _P, _P, _P]),
     "qsdp_error_stats": (_I, [_P, _P, _I64, _P, _P, _P, _P]),
@@ -205,7 +206,7 @@ def onebit_onepass_max_elements() -> int:
 
 PROFILE_CLASSES = ("warmup", "compress_pass1", "compress_onepass", "compress_pass2", "qsdp_quantize",
                    "qsdp_dequantize", "server_pass1", "server_onepass", "server_pass2", "finalize",
-                   "momentum_update", "qsgd_quantize", "qsgd_reduce")
+                   "momentum_update", "qsgd_quantize", "qsgd_reduce", "loco_quantize")
 
 
 def onebit_profile_begin():
@@ -262,6 +263,11 @@ def onebit_momentum_update(m, mask, v, x, x_bf16, *, lr, eps, weight_decay, stre
 def qsgd_quantize(g, bucket, bits, seed, codes, norms, stream=None):
     _check(load().qsgd_quantize(_ptr(g), _dtype_code(g), g.numel(), int(bucket), int(bits), int(seed) & (2 ** 64 - 1),
                                 _ptr(codes), _ptr(norms), _stream(stream)), "qsgd_quantize")
+
+
+def loco_quantize(g, err_avg, bucket, bits, beta, seed, codes, norms, stream=None):
+    _check(load().loco_quantize(_ptr(g), _dtype_code(g), _ptr(err_avg), g.numel(), int(bucket), int(bits), float(beta),
+                                int(seed) & (2 ** 64 - 1), _ptr(codes), _ptr(norms), _stream(stream)), "loco_quantize")
 
 
 def qsgd_reduce(codes, norms, n, bucket, bits, out_f32=None, out_bf16=None, stream=None):

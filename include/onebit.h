@@ -16,6 +16,10 @@
  *  [QSDP] nubint.ai review of "Quantized Distributed Training of Large Models with
  *         Convergence Guarantees", "proposed method": weights rounded at random to
  *         one of the two nearest quantization levels, unbiased.
+ *  [QSGD] Alistarh et al., "QSGD: Communication-Efficient SGD via Gradient Quantization
+ *         and Encoding", NeurIPS 2017, sec. 3.1 (named by [QSDP] for gradients).
+ *  [LOCO] shd-paper.top summary of "LoCo: Low-Bit Communication Adaptor for
+ *         Large-scale Model Training", core points and method details.
  *  [PHX]  Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11.
  *
  * Conventions for every call:
@@ -130,9 +134,9 @@ int64_t onebit_onepass_max_elements(void);
  * ONEBIT_PROFILE_CLASSES entries, nullable).  Classes: 0 warmup, 1/2/3 worker
  * compression pass 1 / one-pass / pass 2, 4 quantize, 5 dequantize, 6/7/8 server
  * pass 1 / one-pass / pass 2, 9 chunk-norm finalization of two-pass chunks, 10
- * momentum update, 11 QSGD quantize, 12 QSGD reduce.  Not thread-safe; diagnostics
- * only. */
-#define ONEBIT_PROFILE_CLASSES 13
+ * momentum update, 11 QSGD quantize, 12 QSGD reduce, 13 LoCo quantize.  Not
+ * thread-safe; diagnostics only. */
+#define ONEBIT_PROFILE_CLASSES 14
 void onebit_profile_begin(void);
 onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
 
@@ -208,6 +212,18 @@ onebit_status_t onebit_momentum_update(float *m, const uint8_t *mask, const floa
  * 65536, bucket even when bits == 4.  Use a seed distinct from the weights'. */
 onebit_status_t qsgd_quantize(const void *g, onebit_dtype_t g_dtype, int64_t n, int bucket, int bits,
                               uint64_t seed, uint8_t *codes, float *norms, void *stream);
+
+/* LoCo-style compensated gradient quantizer ([LOCO] method details: the gradient is
+ * compensated, before compression, by a moving average of the past compression
+ * errors; the page gives no formula, so these steps are this library's reading):
+ *   h = fl32(g + err_avg);  codes, norms = qsgd_quantize of h (same seed use)
+ *   y = h decoded (W = 1 of qsgd_reduce);  err_avg = fl32( fl32(beta err_avg) + fl32((1-beta)(h - y)) )
+ * beta = 0 is plain error feedback.  err_avg: fp32 [n] in place, 16-byte aligned;
+ * 0 <= beta <= 1 (rounded to binary32 once, 1 - beta formed in binary64).  Other
+ * arguments as qsgd_quantize. */
+onebit_status_t loco_quantize(const void *g, onebit_dtype_t g_dtype, float *err_avg, int64_t n, int bucket,
+                              int bits, double beta, uint64_t seed, uint8_t *codes, float *norms,
+                              void *stream);
 
 /* Decode and average W workers' QSGD streams of the same n elements (the shard
  * owner's half of a quantized reduce-scatter; W = 1 is plain decoding):

@@ -39,7 +39,7 @@ def _load():
         lib.oracle_decompress.argtypes = [_P, _I64, _P, _P, _P]
         lib.oracle_qsgd_quantize.argtypes = [_P, _I, _I64, _I, _I, C.c_uint64, _I64, _P, _P]
         lib.oracle_qsgd_reduce.argtypes = [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P]
-        lib.oracle_loco_quantize.argtypes = [_P, _I, _P, _I64, _I, _I, _D, C.c_uint64, _P, _P]
+        lib.oracle_loco_quantize.argtypes = [_P, _I, _P, _I64, _I, _I, _D, C.c_uint64, _I64, _P, _P]
         lib.oracle_momentum_update.argtypes = [_P, _P, _P, _P, _P, _I64, _D, _D, _D]
         lib.oracle_philox4x32_10.argtypes = [_P, _P, _P]
         lib.oracle_philox4x32_10.restype = None
@@ -271,7 +271,7 @@ def qsgd_reduce(codes, norms, n, *, bucket, bits, want_bf16=False):
     return out[:n], (ob[:n] if want_bf16 else None)
 
 
-def loco_quantize(g, err_avg, *, bucket, bits, beta, seed):
+def loco_quantize(g, err_avg, *, bucket, bits, beta, seed, first_index=0):
     """LoCo-style step, err_avg (float32) updated in place.  Returns (codes, norms)."""
     lib = _load()
     if g.dtype == np.uint16:
@@ -285,6 +285,6 @@ def loco_quantize(g, err_avg, *, bucket, bits, beta, seed):
     nbytes = (n + 1) // 2 if bits == 4 else n
     codes = np.zeros(max(nbytes, 1), dtype=np.uint8)
     norms = np.zeros(max(nb, 1), dtype=np.float32)
-    _check(lib.oracle_loco_quantize(_ptr(g), dt, _ptr(err_avg), n, bucket, bits, beta, seed, _ptr(codes),
-                                    _ptr(norms)), "loco_quantize")
+    _check(lib.oracle_loco_quantize(_ptr(g), dt, _ptr(err_avg), n, bucket, bits, beta, seed, first_index,
+                                    _ptr(codes), _ptr(norms)), "loco_quantize")
     return codes[:nbytes], norms[:nb]

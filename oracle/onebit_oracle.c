@@ -661,9 +661,10 @@ int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const f
  *   h = fl32(g + err_avg);  (codes, norms) = QSGD of h, as O7;  y = decoded h as
  *   the W = 1 decode of O7;  err_avg = fl32( fl32(beta * err_avg) + fl32((1 - beta) * (h - y)) ).
  * beta = 0 is plain error feedback (err_avg = h - y).  err_avg: fp32 [n] in place.
+ * first_index: global index of g[0], as in O7.
  */
 int oracle_loco_quantize(const void *g, int g_dtype, float *err_avg, int64_t n, int bucket, int nbits, double beta_d,
-                         uint64_t seed, uint8_t *codes, float *norms)
+                         uint64_t seed, int64_t first_index, uint8_t *codes, float *norms)
 {
     if (n < 0 || (g_dtype != 0 && g_dtype != 1))
         return ORACLE_ERR_INVALID;
@@ -682,7 +683,7 @@ int oracle_loco_quantize(const void *g, int g_dtype, float *err_avg, int64_t n, 
         const float gi = g_dtype == 1 ? oracle_bf16_to_f32(((const uint16_t *)g)[i]) : ((const float *)g)[i];
         h[i] = gi + err_avg[i];
     }
-    int rc = oracle_qsgd_quantize(h, 0, n, bucket, nbits, seed, 0, codes, norms);
+    int rc = oracle_qsgd_quantize(h, 0, n, bucket, nbits, seed, first_index, codes, norms);
     if (rc == ORACLE_OK)
         rc = oracle_qsgd_reduce(1, codes, 0, norms, 0, n, bucket, nbits, y, NULL);
     if (rc == ORACLE_OK) {

@@ -170,3 +170,65 @@ def test_full_size_eight_workers(bits):
             ry, _ = oracle.qsgd_reduce(rc, rn, bhi - blo, bucket=bucket, bits=bits)
             assert_exact(f"shard {s} bucket {b} mean", host(y[blo:bhi]), ry)
         say(f"  qsgd{bits} shard {s} ({m} elements): sampled buckets match")
+
+
+@pytest.mark.parametrize("bucket,bits", [(1024, 4), (1024, 8), (30, 4), (1000, 8)])
+@pytest.mark.parametrize("beta", [0.0, 0.5, 0.9])
+def test_loco_parity(bucket, bits, beta):
+    n = 5 * 1024 + 77
+    rng = np.random.default_rng(bucket + bits)
+    e0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        ed = torch.from_numpy(e0.copy()).to(DEV)
+        er = e0.copy()
+        codes = torch.zeros(code_bytes(n, bits), dtype=torch.uint8, device=DEV)
+        norms = torch.zeros((n + bucket - 1) // bucket, device=DEV)
+        for step in range(3):
+            g = (np.random.default_rng(step).standard_normal(n) * 10.0 ** -(2 + step)).astype(np.float32)
+            gd, gh = to_device(g, dt)
+            ob.loco_quantize(gd, ed, bucket, bits, beta, 500 + step, codes, norms)
+            rc, rn = oracle.loco_quantize(gh, er, bucket=bucket, bits=bits, beta=beta, seed=500 + step)
+            torch.cuda.synchronize()
+            tag = f"loco bucket {bucket} bits {bits} beta {beta} {dt} step {step}"
+            assert_exact(f"{tag} codes", host(codes), rc)
+            assert_exact(f"{tag} norms", host(norms), rn)
+            assert_exact(f"{tag} err_avg", host(ed), er)
+
+
+def test_loco_argument_errors():
+    g = torch.zeros(64, device=DEV)
+    e = torch.zeros(64, device=DEV)
+    codes = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    norms = torch.zeros(4, device=DEV)
+    for beta in (-0.1, 1.5, float("nan")):
+        with pytest.raises(ob.OnebitError) as ei:
+            ob.loco_quantize(g, e, 16, 8, beta, 0, codes, norms)
+        assert ei.value.status == ob.ONEBIT_ERR_INVALID
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.loco_quantize(g, e[1:], 16, 8, 0.5, 0, codes, norms)
+    assert ei.value.status == ob.ONEBIT_ERR_ALIGN
+
+
+def test_loco_full_size_two_steps():
+    q = W.QsgdWorkload()
+    n, bucket, bits = q.n, q.bucket, 4
+    nb = (n + bucket - 1) // bucket
+    e = torch.zeros(n, device=DEV)
+    codes = torch.zeros(code_bytes(n, bits), dtype=torch.uint8, device=DEV)
+    norms = torch.zeros(nb, device=DEV)
+    sample_b = sorted({0, nb - 1} | set(int(b) for b in np.random.default_rng(9).choice(nb, 30, replace=False)))
+    for step in range(2):
+        gd = W.qsgd_gradient(q, step, device=DEV)
+        before = {b: (host(gd[b * bucket:min((b + 1) * bucket, n)]), host(e[b * bucket:min((b + 1) * bucket, n)]))
+                  for b in sample_b}
+        ob.loco_quantize(gd, e, bucket, bits, 0.9, 900 + step, codes, norms)
+        torch.cuda.synchronize()
+        for b in sample_b:
+            lo, hi = b * bucket, min((b + 1) * bucket, n)
+            gs, es = before[b]
+            rc, rn = oracle.loco_quantize(gs, es, bucket=bucket, bits=bits, beta=0.9, seed=900 + step, first_index=lo)
+            assert_exact(f"step {step} bucket {b} codes", host(codes[lo // 2:(hi + 1) // 2]), rc)
+            assert_exact(f"step {step} bucket {b} norm", host(norms[b:b + 1]), rn)
+            assert_exact(f"step {step} bucket {b} err_avg", host(e[lo:hi]), es)
+        del gd
+        say(f"  loco step {step}: {len(sample_b)} buckets match")
