@@ -140,6 +140,15 @@ int64_t onebit_onepass_max_elements(void);
 void onebit_profile_begin(void);
 onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
 
+/* Diagnostics: a plain streaming kernel over `reads` fp32 input streams and `writes`
+ * output streams of n elements each (out_k = sum of the inputs + k), to measure what
+ * HBM delivers for that mix on this device.  in / out: DEVICE arrays of `reads` /
+ * `writes` device pointers, each 16-byte aligned; n a multiple of 4.  Supported
+ * mixes: 5 reads + 3 writes (the compression kernel's), 1 + 1 (a copy); others
+ * return ONEBIT_ERR_UNSUPPORTED.  grid: workgroups of 256 threads. */
+onebit_status_t onebit_stream_probe(const float *const *in, int reads, float *const *out, int writes,
+                                    int64_t n, int grid, void *stream);
+
 /* Warmup step t (1-based) of full-precision Adam over n elements ([DSG] sec. 4,
  * phase one; [1BA]):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
  *   x -= lr * ( mhat / (sqrt(vhat) + eps) + weight_decay * x ),
