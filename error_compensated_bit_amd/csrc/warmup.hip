@@ -44,7 +44,7 @@ __device__ __forceinline__ void load_g4w(const void *g, int64_t i, float (&gg)[4
 
 // Each thread takes kWU groups of four elements per iteration (all loads of an
 // iteration in flight together), grid-stride over the vector.
-constexpr int kWU = 2;
+constexpr int kWU = 4;
 
 template <int GT>
 __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
@@ -130,7 +130,7 @@ extern "C" onebit_status_t onebit_adam_warmup_step(float *x, float *m, float *v,
     }
     const int64_t groups = n / 4;
     int64_t blocks = (groups + 256 * kWU - 1) / (256 * kWU);
-    const int64_t cap = (int64_t)cus * 8;  // resident waves enough to cover HBM latency
+    const int64_t cap = (int64_t)cus * 6;  // six workgroups per CU: enough bytes in flight, fewer DRAM page conflicts
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
