@@ -211,6 +211,119 @@ def profile_mode(steps):
     log(f"[profile] {steps} steps of {wl.name} and one {CALIBRATION_FLOATS * 4} B copy done")
 
 
+QUANT_SUMMARY = os.path.join(ROOT, "profiles", "quantizers_valu.md")
+QUANT_FILES = ("csrc/qsdp.hip", "csrc/qsgd.hip", "csrc/device_common.h", "build.py")
+VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9     # 256 CUs x 64 lanes (4 SIMD16, one wave64 op per 4 clocks) x 2.4 GHz
+
+
+def quant_digest():
+    h = hashlib.sha256()
+    for rel in QUANT_FILES:
+        with open(os.path.join(ROOT, "error_compensated_bit_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def quantizer_calls(dev):
+    """(kernel-name fragment, label, elements, call) for the ALU-bound quantizers at full size."""
+    import torch
+    from error_compensated_bit_amd import onebit as ob
+    from error_compensated_bit_amd import workloads as W
+    q = W.QsdpWorkload()
+    xq = W.qsdp_weights(q, device=dev)
+    gq = W.qsgd_gradient(W.QsgdWorkload(), 0, device=dev)
+    nb = (q.n + q.bucket - 1) // q.bucket
+    codes = torch.zeros(q.n, dtype=torch.uint8, device=dev)
+    f1, f2 = torch.zeros(nb, device=dev), torch.zeros(nb, device=dev)
+    err = torch.zeros(q.n, device=dev)
+    return [
+        ("k_qsdp_quantize_1024<4>", "qsdp4_quantize", q.n, lambda: ob.qsdp_quantize(xq, q.bucket, 4, 0, codes, f1, f2)),
+        ("k_qsdp_quantize_1024<8>", "qsdp8_quantize", q.n, lambda: ob.qsdp_quantize(xq, q.bucket, 8, 0, codes, f1, f2)),
+        ("k_qsgd_quantize_1024<4, 1, false>", "qsgd4_quantize", q.n,
+         lambda: ob.qsgd_quantize(gq, q.bucket, 4, 0, codes, f1)),
+        ("k_qsgd_quantize_1024<8, 1, false>", "qsgd8_quantize", q.n,
+         lambda: ob.qsgd_quantize(gq, q.bucket, 8, 0, codes, f1)),
+        ("k_qsgd_quantize_1024<4, 1, true>", "loco4_quantize", q.n,
+         lambda: ob.loco_quantize(gq, err, q.bucket, 4, 0.9, 0, codes, f1)),
+    ]
+
+
+def profile_quantizers():
+    """Work for rocprofv3: each ALU-bound quantizer twice at full size."""
+    import torch
+    ensure_built()
+    for _, label, _, call in quantizer_calls("cuda:0"):
+        call()
+        call()
+        torch.cuda.synchronize()
+        log(f"[profile] {label} done")
+
+
+def summarize_quantizers(kt_dir, pmc_dir):
+    """VALU instructions per element of each quantizer and its issue-rate bound."""
+    import numpy as np
+    stats = {_short(r["Name"]): r for r in _rows(kt_dir, "kernel_stats.csv")}
+    valu = {}
+    for r in _rows(pmc_dir, "counter_collection.csv"):
+        if r.get("Counter_Name") == "SQ_INSTS_VALU":
+            valu.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    out = ["# ALU-bound quantizers: VALU instructions per element and issue-rate bound", ""]
+    out.append("Commands (from the repository root, on one MI355X):")
+    out.append("```")
+    out.append(f"rocprofv3 --kernel-trace --stats --output-format csv -d {kt_dir} -o bench -- python3 bench.py "
+               f"--profile-quantizers")
+    out.append(f"rocprofv3 --pmc SQ_INSTS_VALU --output-format csv -d {pmc_dir} -o bench -- python3 bench.py "
+               f"--profile-quantizers")
+    out.append(f"python bench.py --summarize-quantizers {kt_dir} {pmc_dir}")
+    out.append("```")
+    out.append(f"Quantizer source digest: {quant_digest()}")
+    out.append("")
+    out.append(f"Issue-rate bound: {VALU_LANE_OPS_PER_S / 1e12:.2f} T VALU lane-instructions/s (256 CUs x 4 SIMD16 x "
+               f"one wave64 instruction per 4 clocks x 2.4 GHz); elements/s bound = that / (SQ_INSTS_VALU x 64 / "
+               f"elements).  Transcendental and fp64 instructions issue at lower rates, so the bound is optimistic.")
+    out.append("")
+    out.append("| kernel | elements | average ns | SQ_INSTS_VALU per dispatch | VALU lane-instr per element | "
+               "bound G elem/s | achieved G elem/s | fraction |")
+    out.append("|---|---|---|---|---|---|---|---|")
+    for frag, label, n, _ in quantizer_calls_meta():
+        key = next((k for k in stats if frag in k), None)
+        vkey = next((k for k in valu if frag in k), None)
+        if key is None or vkey is None:
+            continue
+        ns = float(stats[key]["AverageNs"])
+        per_elem = float(np.median(valu[vkey])) * 64.0 / n
+        bound = VALU_LANE_OPS_PER_S / per_elem
+        ach = n / (ns * 1e-9)
+        out.append(f"| {label} | {n} | {ns:.0f} | {np.median(valu[vkey]):.0f} | {per_elem:.2f} | {bound / 1e9:.0f} | "
+                   f"{ach / 1e9:.0f} | {ach / bound:.3f} |")
+        out.append(f"<!-- {label} valu_lane_instr_per_element={per_elem:.4f} -->")
+    return "\n".join(out) + "\n"
+
+
+def quantizer_calls_meta():
+    n = 1_300_000_000
+    return [("k_qsdp_quantize_1024<4>", "qsdp4_quantize", n, None), ("k_qsdp_quantize_1024<8>", "qsdp8_quantize", n, None),
+            ("k_qsgd_quantize_1024<4, 1, false>", "qsgd4_quantize", n, None),
+            ("k_qsgd_quantize_1024<8, 1, false>", "qsgd8_quantize", n, None),
+            ("k_qsgd_quantize_1024<4, 1, true>", "loco4_quantize", n, None)]
+
+
+def valu_per_element():
+    """{label: VALU lane-instructions per element} from the committed summary, if the sources match."""
+    try:
+        text = open(QUANT_SUMMARY).read()
+    except OSError:
+        return {}
+    if f"Quantizer source digest: {quant_digest()}" not in text:
+        return {}
+    res = {}
+    for line in text.splitlines():
+        if line.startswith("<!-- ") and "valu_lane_instr_per_element=" in line:
+            label, kv = line[5:-4].split(" ", 1)
+            res[label] = float(kv.split("=")[1])
+    return res
+
+
 def _rows(dirname, suffix):
     files = glob.glob(os.path.join(dirname, "**", f"*{suffix}"), recursive=True)
     if not files:
@@ -301,9 +414,17 @@ def main():
     ap.add_argument("--workload", default="bert_large", choices=["bert_large", "gpt2_xl"])
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--profile-quantizers", action="store_true")
+    ap.add_argument("--summarize-quantizers", nargs=2, metavar=("KT_DIR", "PMC_DIR"))
     args = ap.parse_args()
     if args.summarize_profile:
         sys.stdout.write(summarize_profile(*args.summarize_profile))
+        return
+    if args.summarize_quantizers:
+        sys.stdout.write(summarize_quantizers(*args.summarize_quantizers))
+        return
+    if args.profile_quantizers:
+        profile_quantizers()
         return
     if args.profile:
         profile_mode(max(1, min(args.steps, 5)))
@@ -404,6 +525,19 @@ def stream_ceiling(dev, n=335_544_320):
             "kernel": "onebit_stream_probe"}
 
 
+def roof(gbps, elems_per_s=None, label=None, valu=None):
+    """Roofline of a row: HBM fraction of 8 TB/s, and for the quantizers the fraction of
+    the VALU issue-rate bound (from the committed instruction counts); bound = the
+    larger fraction."""
+    r = {"hbm_frac": gbps / PEAK_HBM_GBPS}
+    per = (valu or {}).get(label)
+    if per and elems_per_s:
+        r["alu_peak_elems_per_s"] = VALU_LANE_OPS_PER_S / per
+        r["alu_frac"] = elems_per_s / r["alu_peak_elems_per_s"]
+    r["bound"] = "alu" if r.get("alu_frac", 0.0) > r["hbm_frac"] else "hbm"
+    return r
+
+
 def secondary_rows(dev, args):
     import numpy as np
     import torch
@@ -411,6 +545,7 @@ def secondary_rows(dev, args):
     from error_compensated_bit_amd import workloads as W
     rows = {}
     steps = max(3, args.steps // 3)
+    valu = valu_per_element()
 
     # warmup Adam step on the BERT-Large-sized vector
     n = 335_143_938
@@ -425,7 +560,8 @@ def secondary_rows(dev, args):
     t, kt = timed(warm, steps, 2)
     km = kt.mean_ms("warmup")
     rows["warmup_adam_bert_large"] = dict(params_per_s=n / t, gbps=B_WARMUP * n / t / 1e9,
-                                          kernel_gbps=B_WARMUP * n / (km * 1e-3) / 1e9)
+                                          kernel_gbps=B_WARMUP * n / (km * 1e-3) / 1e9,
+                                          roofline=roof(B_WARMUP * n / (km * 1e-3) / 1e9))
     del x, m, v, g
     torch.cuda.empty_cache()
     log(f"[bench] warmup {rows['warmup_adam_bert_large']}")
@@ -442,7 +578,9 @@ def secondary_rows(dev, args):
         tq, ktq = timed(lambda: ob.qsdp_quantize(xq, q.bucket, bits, 0, codes, bmin, bmax), steps, 1)
         td, ktd = timed(lambda: ob.qsdp_dequantize(codes, bmin, bmax, q.n, q.bucket, bits, out), steps, 1)
         rows[f"qsdp{bits}_quantize"] = dict(elems_per_s=q.n / tq, gbps=bpe * q.n / tq / 1e9)
+        rows[f"qsdp{bits}_quantize"]["roofline"] = roof(bpe * q.n / tq / 1e9, q.n / tq, f"qsdp{bits}_quantize", valu)
         rows[f"qsdp{bits}_dequantize"] = dict(elems_per_s=q.n / td, gbps=bpe * q.n / td / 1e9)
+        rows[f"qsdp{bits}_dequantize"]["roofline"] = roof(bpe * q.n / td / 1e9)
         del codes, out
     del xq, bmin, bmax
     torch.cuda.empty_cache()
@@ -465,12 +603,15 @@ def secondary_rows(dev, args):
         tr, _ = timed(lambda: ob.qsgd_reduce(codes, norms, qg.shard, qg.bucket, bits, out_f32=out), steps, 1)
         bq = 2.0 + bits / 8.0 + 4.0 / qg.bucket
         br = qg.W * (bits / 8.0 + 4.0 / qg.bucket) + 4.0
-        rows[f"qsgd{bits}_quantize"] = dict(elems_per_s=qg.n / tq, gbps=bq * qg.n / tq / 1e9)
-        rows[f"qsgd{bits}_reduce_{qg.W}x{qg.shard}"] = dict(elems_per_s=qg.shard / tr, gbps=br * qg.shard / tr / 1e9)
+        rows[f"qsgd{bits}_quantize"] = dict(elems_per_s=qg.n / tq, gbps=bq * qg.n / tq / 1e9,
+                                            roofline=roof(bq * qg.n / tq / 1e9, qg.n / tq, f"qsgd{bits}_quantize", valu))
+        rows[f"qsgd{bits}_reduce_{qg.W}x{qg.shard}"] = dict(elems_per_s=qg.shard / tr, gbps=br * qg.shard / tr / 1e9,
+                                                            roofline=roof(br * qg.shard / tr / 1e9))
         if bits == 4:
             err = torch.zeros(qg.n, device=dev)
             tl, _ = timed(lambda: ob.loco_quantize(gq, err, qg.bucket, bits, 0.9, 7, codes[0], norms[0]), steps, 1)
-            rows["loco4_quantize"] = dict(elems_per_s=qg.n / tl, gbps=(bq + 8.0) * qg.n / tl / 1e9)
+            rows["loco4_quantize"] = dict(elems_per_s=qg.n / tl, gbps=(bq + 8.0) * qg.n / tl / 1e9,
+                                          roofline=roof((bq + 8.0) * qg.n / tl / 1e9, qg.n / tl, "loco4_quantize", valu))
             del err
         del codes, out
     del gq, norms
@@ -503,7 +644,9 @@ def secondary_rows(dev, args):
     rows["allreduce_16x64M"] = dict(ms_per_step=t * 1e3, gbps=step_bytes / t / 1e9,
                                     worker_kernel_gbps=B_WORKER * a.n / (w_ms * 1e-3) / 1e9,
                                     server_kernel_gbps=14.125 * a.n / (s_ms * 1e-3) / 1e9,
-                                    server_kernel_ms=s_ms, worker_kernel_ms=w_ms)
+                                    server_kernel_ms=s_ms, worker_kernel_ms=w_ms,
+                                    worker_roofline=roof(B_WORKER * a.n / (w_ms * 1e-3) / 1e9),
+                                    server_roofline=roof(14.125 * a.n / (s_ms * 1e-3) / 1e9))
     # the same exchange as a full step: fp16 gradients, the server's result masked
     # per element into the momentum, frozen-v update of x
     g16 = grads.to(torch.float16)
@@ -525,7 +668,8 @@ def secondary_rows(dev, args):
                                              worker_kernel_gbps=B_WORKER_F16 * a.n /
                                              (kt.mean_ms("compress_onepass") * 1e-3) / 1e9,
                                              finish_kernel_gbps=B_FINISH_MASK * a.n / (f_ms * 1e-3) / 1e9,
-                                             finish_kernel_ms=f_ms)
+                                             finish_kernel_ms=f_ms,
+                                             finish_roofline=roof(B_FINISH_MASK * a.n / (f_ms * 1e-3) / 1e9))
     del m, e, es, g16, v, x, mask, wbits, wsc, sbits, ssc, wsp, plan
     torch.cuda.empty_cache()
     log(f"[bench] allreduce {rows['allreduce_16x64M']} full step {rows['full_step_16x64M_f16_mask']}")
@@ -535,6 +679,8 @@ def secondary_rows(dev, args):
     r = bench_compress(wl, steps, 1, dev, B_COMPRESS_BF16_COPY)
     rows["compress_gpt2_xl_bf16"] = {k: r[k] for k in ("params_per_s", "gbps", "onepass_gbps", "plan")
                                      if k in r}
+    if r.get("onepass_gbps"):
+        rows["compress_gpt2_xl_bf16"]["roofline"] = roof(r["onepass_gbps"])
     torch.cuda.empty_cache()
     log(f"[bench] gpt2 {rows['compress_gpt2_xl_bf16']}")
     return rows
