@@ -251,19 +251,20 @@ __device__ __forceinline__ void spin_pause() { __builtin_amdgcn_s_sleep(2); }
 // result does not depend on which tile finished last.  All loads of a batch are
 // in flight before any is checked; a slot that is not yet visible is re-polled.
 // Slots are cleared after reading (zero = empty for the next call).
+template <int NT = kBlock, int kBatch = 8>
 __device__ double chunk_sum(const CompressArgs &a, const ChunkDesc &ch, DD *s_red, double *s_total) {
+    constexpr int kW = NT / 64;
     DD acc = {0.0, 0.0};
-    constexpr int kBatch = 8;
-    for (int base = 0; base < ch.ntiles; base += kBlock * kBatch) {
+    for (int base = 0; base < ch.ntiles; base += NT * kBatch) {
         uint64_t w[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int k = base + u * kBlock + (int)threadIdx.x;
+            const int k = base + u * NT + (int)threadIdx.x;
             w[u] = k < ch.ntiles ? ld_agent(a.slots + ch.first_tile + k) : kTag;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int k = base + u * kBlock + (int)threadIdx.x;
+            const int k = base + u * NT + (int)threadIdx.x;
             if (k < ch.ntiles) {
                 uint64_t *slot = a.slots + ch.first_tile + k;
                 uint32_t spins = 0;
@@ -285,7 +286,7 @@ __device__ double chunk_sum(const CompressArgs &a, const ChunkDesc &ch, DD *s_re
     if (threadIdx.x == 0) {
         DD t = s_red[0];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) t = dd_add(t, s_red[w]);
+        for (int w = 1; w < kW; ++w) t = dd_add(t, s_red[w]);
         *s_total = __dadd_rn(t.hi, t.lo);
     }
     __syncthreads();
@@ -606,12 +607,16 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     (void)s_total;
 }
 
-__global__ __launch_bounds__(kBlock) void k_finalize_chunks(CompressArgs a, const int32_t *chunk_list) {
-    __shared__ DD s_red[kWaves];
+// One 1024-thread workgroup per two-pass chunk, 16 slot loads per thread in flight:
+// a chunk of up to 16384 tiles is summed in one round of loads.
+constexpr int kFinalizeThreads = 1024;
+
+__global__ __launch_bounds__(kFinalizeThreads) void k_finalize_chunks(CompressArgs a, const int32_t *chunk_list) {
+    __shared__ DD s_red[kFinalizeThreads / 64];
     __shared__ double s_total;
     const int chunk = chunk_list[blockIdx.x];
     const ChunkDesc ch = a.chunks[chunk];
-    const double S = chunk_sum(a, ch, s_red, &s_total);
+    const double S = chunk_sum<kFinalizeThreads, 16>(a, ch, s_red, &s_total);
     if (threadIdx.x == 0) a.scales[chunk] = scale_of(S, ch.len);
 }
 
@@ -640,7 +645,7 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e);
         prof_before(kProfFinalize, stream);
-        hipLaunchKernelGGL(k_finalize_chunks, dim3(p->n_big_chunks), dim3(kBlock), 0, stream, a,
+        hipLaunchKernelGGL(k_finalize_chunks, dim3(p->n_big_chunks), dim3(kFinalizeThreads), 0, stream, a,
                            (const int32_t *)p->d_big_chunks);
         prof_after(stream);
         e = hipGetLastError();
