@@ -43,6 +43,7 @@ PEAK_HBM_GBPS = 8000.0
 B_COMPRESS_F32 = 32.125      # read g,m,e,v,x (20 B); write m,e,x (12 B); bits (1/8 B)
 B_COMPRESS_BF16_COPY = 32.125  # read g bf16 (2),m,e,v,x (16); write m,e,x (12), x_bf16 (2); bits
 B_WARMUP = 28.0              # read g,m,v,x; write m,v,x
+B_COMPRESS_PACKED = 24.25    # read g,e,v,x (16 B) and 1/8 B of momentum words; write e,x (8 B), bits
 B_WORKER = 16.125            # read g,m,e; write e; bits
 B_WORKER_F16 = 14.125        # read g fp16 (2), m, e; write e; bits
 B_FINISH_MASK = 21.0         # read m, mask (1), v, x; write m, x
@@ -673,6 +674,36 @@ def secondary_rows(dev, args):
     del m, e, es, g16, v, x, mask, wbits, wsc, sbits, ssc, wsp, plan
     torch.cuda.empty_cache()
     log(f"[bench] allreduce {rows['allreduce_16x64M']} full step {rows['full_step_16x64M_f16_mask']}")
+
+    # the headline step with the momentum kept as the previous step's words and scales
+    wl = W.bert_like()
+    x, m, e, v = W.init_state(wl, device=dev)
+    g = W.gradient(wl, 1, device=dev)
+    plan = ob.onebit_plan_create(wl.chunk_off, wl.tensor_off, wl.tensor_keep)
+    words, nch = ob.onebit_plan_words(plan), ob.onebit_plan_chunks(plan)
+    wsp = torch.zeros(ob.onebit_plan_workspace_bytes(plan) // 8, dtype=torch.int64, device=dev)
+    pb = [torch.zeros(words, dtype=torch.int32, device=dev) for _ in range(2)]
+    ps = [torch.zeros(nch, device=dev) for _ in range(2)]
+    hp = dict(lr=wl.hyper["lr"], beta1=wl.hyper["beta1"], eps=wl.hyper["eps"], weight_decay=wl.hyper["weight_decay"])
+    ob.onebit_compress_update(plan, g, m, e, v, x, None, pb[0], ps[0], workspace=wsp, **hp)
+    del m
+    flip = [0]
+
+    def packed_step():
+        c = flip[0]
+        ob.onebit_compress_update_packed(plan, g, pb[c], ps[c], e, v, x, None, pb[1 - c], ps[1 - c], workspace=wsp,
+                                         **hp)
+        flip[0] = 1 - c
+    t, kt = timed(packed_step, steps, 1)
+    assert ob.onebit_workspace_status(wsp) == 0
+    n1 = onepass_elements(wl, plan)
+    k_ms = kt.mean_ms("compress_onepass")
+    rows["compress_bert_large_packed_m"] = dict(params_per_s=wl.n / t, gbps=B_COMPRESS_PACKED * wl.n / t / 1e9,
+                                                onepass_gbps=B_COMPRESS_PACKED * n1 / (k_ms * 1e-3) / 1e9,
+                                                roofline=roof(B_COMPRESS_PACKED * n1 / (k_ms * 1e-3) / 1e9))
+    del x, e, v, g, pb, ps, wsp, plan
+    torch.cuda.empty_cache()
+    log(f"[bench] packed momentum {rows['compress_bert_large_packed_m']}")
 
     # GPT-2-XL-shaped vector, bf16 gradients, bf16 copy of x
     wl = W.gpt2_like()

@@ -28,7 +28,9 @@
 
 namespace onebit {
 
-enum Mode { kUpdate = 0, kCompressOnly = 1, kServer = 2 };
+// kUpdatePM: the update mode with the momentum held in its compressed form (the
+// previous step's sign words and chunk scales) instead of an fp32 array.
+enum Mode { kUpdate = 0, kCompressOnly = 1, kServer = 2, kUpdatePM = 3 };
 
 struct CompressArgs {
     const TileDesc *tiles;
@@ -40,6 +42,8 @@ struct CompressArgs {
     // worker inputs / state
     const void *g;
     float *m;
+    const uint32_t *m_bits;  // kUpdatePM: m = decompression of these words and scales
+    const float *m_scales;
     float *e;         // worker error, or the server error in server mode
     const float *v;
     float *x;
@@ -165,21 +169,54 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
     }
 }
 
+// Masked elements among this thread's 2 x 4 elements of a tile: bit 4r+q for
+// element lane_k0(r)+q, from one pass over the intervals that touch the tile.
+__device__ __forceinline__ uint32_t thread_mask_bits(const CompressArgs &a, const TileDesc &t) {
+    if (t.mask_lo < 0) return 0xFFu;
+    uint32_t bits = 0u;
+    for (int k = t.mask_lo; k < t.mask_hi; ++k) {
+        const int64_t lo = a.mask_iv[2 * k], hi = a.mask_iv[2 * k + 1];
+#pragma unroll
+        for (int r = 0; r < kGroups; ++r) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = t.start + (int64_t)lane_k0(r) + q;
+                bits |= (uint32_t)((i >= lo) & (i < hi)) << (4 * r + q);
+            }
+        }
+    }
+    return bits;
+}
+
+// The momentum of four elements from the previous step's packed form: +-scale by
+// sign bit, 0 for masked elements (as the fp32 form holds them).
+__device__ __forceinline__ void load_packed_m4(const CompressArgs &a, const TileDesc &t, uint32_t k0,
+                                               uint32_t masked4, float (&m4)[4]) {
+    const float s = a.m_scales[t.chunk];
+    const uint32_t wi = k0 >> 5;
+    const uint32_t word = wi < (((uint32_t)t.len + 31u) >> 5) ? a.m_bits[t.word + wi] : 0u;
+    const uint32_t nib = word >> (k0 & 31u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m4[q] = ((masked4 >> q) & 1u) ? 0.0f : (((nib >> q) & 1u) ? -s : s);
+}
+
 template <int MODE, int GT>
 __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const TileDesc &t,
                                                float (&c)[kPerThread], double *s_wscale_d,
                                                uint32_t *s_words) {
     const bool full = tile_full(a, t);
     if (MODE != kServer) {
-        const float *mb = a.m + t.start;
+        const float *mb = MODE == kUpdatePM ? nullptr : a.m + t.start;
         const float *eb = a.e + t.start;
+        const uint32_t masked = MODE == kUpdatePM ? thread_mask_bits(a, t) : 0u;
 #pragma unroll
         for (int r = 0; r < kGroups; ++r) {
             const uint32_t k0 = lane_k0(r);
             float g4[4], m4[4], e4[4];
+            if (MODE == kUpdatePM) load_packed_m4(a, t, k0, (masked >> (4 * r)) & 0xFu, m4);
             if (full) {
                 load_g4<GT>(a.g, t.start, k0, g4);
-                load4(mb, k0, m4);
+                if (MODE != kUpdatePM) load4(mb, k0, m4);
                 load4(eb, k0, e4);
             } else {
 #pragma unroll
@@ -189,7 +226,7 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
                     g4[q] = in ? (GT != kGradF32 ? half_bits_to_float<GT>(static_cast<const uint16_t *>(a.g)[t.start + k])
                                                  : static_cast<const float *>(a.g)[t.start + k])
                                : 0.0f;
-                    m4[q] = in ? mb[k] : 0.0f;
+                    if (MODE != kUpdatePM) m4[q] = in ? mb[k] : 0.0f;
                     e4[q] = in ? eb[k] : 0.0f;
                 }
             }
@@ -362,11 +399,6 @@ __device__ float wait_scale(const CompressArgs &a, int chunk, const Posted &r, u
     return scale;
 }
 
-__device__ __forceinline__ bool masked_at(const CompressArgs &a, const TileDesc &t, int64_t i) {
-    bool mk = false;
-    for (int k = t.mask_lo; k < t.mask_hi; ++k) mk |= (i >= a.mask_iv[2 * k]) && (i < a.mask_iv[2 * k + 1]);
-    return mk;
-}
 
 __device__ __forceinline__ void store4(float *base, uint32_t k0, const float (&v)[4]) {
     *reinterpret_cast<float4 *>(base + k0) = make_float4(v[0], v[1], v[2], v[3]);
@@ -378,8 +410,7 @@ template <int MODE, bool XB>
 __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDesc &t,
                                             const float (&c)[kPerThread], float scale) {
     const bool full = tile_full(a, t);
-    const bool all_masked = t.mask_lo < 0;
-    const bool some_masked = t.mask_hi > t.mask_lo;
+    const uint32_t masked = MODE != kServer ? thread_mask_bits(a, t) : 0u;
     float *eb = a.e + t.start;
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
@@ -390,12 +421,9 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
             const float cq = c[4 * r + q];
             q4[q] = cq < 0.0f ? -scale : scale;
             e4[q] = sub_rn(cq, q4[q]);
-            if (MODE != kServer) {
-                const bool mk = all_masked || (some_masked && masked_at(a, t, t.start + k0 + q));
-                if (mk) {
-                    q4[q] = 0.0f;
-                    e4[q] = 0.0f;
-                }
+            if ((masked >> (4 * r + q)) & 1u) {
+                q4[q] = 0.0f;
+                e4[q] = 0.0f;
             }
         }
         if (MODE == kServer) {
@@ -422,7 +450,7 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
         } else {
             const float *vb = a.v + t.start;
             float *xb = a.x + t.start;
-            float *mb = a.m + t.start;
+            float *mb = MODE == kUpdatePM ? nullptr : a.m + t.start;
             float v4[4], x4[4];
             if (full) {
                 load4(vb, k0, v4);
@@ -441,7 +469,7 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
                 xn[q] = x4[q] - a.lr * upd;
             }
             if (full) {
-                store4(mb, k0, q4);
+                if (MODE != kUpdatePM) store4(mb, k0, q4);
                 store4(eb, k0, e4);
                 store4(xb, k0, xn);
                 if (XB) {
@@ -454,7 +482,7 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     if (k0 + q < (uint32_t)t.len) {
-                        mb[k0 + q] = q4[q];
+                        if (MODE != kUpdatePM) mb[k0 + q] = q4[q];
                         eb[k0 + q] = e4[q];
                         xb[k0 + q] = xn[q];
                         if (XB) a.xb[t.start + k0 + q] = (uint16_t)float_to_bf16_bits(xn[q]);
@@ -714,6 +742,12 @@ int32_t coop_capacity(int device) {
         reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, kGradBF16, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, kGradF16, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kServer, kGradF32, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF32, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF32, true>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradBF16, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradBF16, true>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF16, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF16, true>),
     };
     int per_cu = 1 << 30;
     for (const void *f : fns) {
@@ -729,23 +763,29 @@ int32_t coop_capacity(int device) {
 
 using namespace onebit;
 
-extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
-                                                  float *m, float *e, const float *v, float *x,
-                                                  uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
-                                                  double beta1, double eps, double weight_decay,
-                                                  void *workspace, void *stream) {
+// Validation and dispatch shared by the fp32-momentum and the packed-momentum
+// entry points (exactly one of m and m_bits is given).
+static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype, float *m,
+                                      const uint32_t *m_bits, const float *m_scales, float *e, const float *v,
+                                      float *x, uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
+                                      double beta1, double eps, double weight_decay, void *workspace,
+                                      void *stream) {
     if (!plan) return ONEBIT_ERR_INVALID;
     if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
+    const bool packed = m_bits != nullptr || m_scales != nullptr;
     const bool update = (v != nullptr) || (x != nullptr);
     if (update && (!v || !x)) return ONEBIT_ERR_INVALID;
-    if (!update && x_bf16) return ONEBIT_ERR_INVALID;
+    if (!update && (x_bf16 || packed)) return ONEBIT_ERR_INVALID;
     if (plan->n_chunks == 0) return ONEBIT_OK;
     if (!scales || !workspace) return ONEBIT_ERR_INVALID;
-    if (plan->n > 0 && (!g || !m || !e || !bits)) return ONEBIT_ERR_INVALID;
+    if (packed && (!m_scales || (plan->n > 0 && !m_bits) || m_scales == scales || (m_bits && m_bits == bits)))
+        return ONEBIT_ERR_INVALID;
+    if (plan->n > 0 && (!g || (!packed && !m) || !e || !bits)) return ONEBIT_ERR_INVALID;
     const void *vec[] = {g, m, e, v, x, x_bf16};
     for (const void *q : vec)
         if (q && !aligned16(q)) return ONEBIT_ERR_ALIGN;
     if (!aligned_to(bits, 4) || !aligned_to(scales, 4) || !aligned_to(workspace, 8)) return ONEBIT_ERR_ALIGN;
+    if (!aligned_to(m_bits, 4) || !aligned_to(m_scales, 4)) return ONEBIT_ERR_ALIGN;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return ONEBIT_ERR_INVALID;
 
@@ -756,6 +796,8 @@ extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void
     a.aligned = plan->aligned ? 1 : 0;
     a.g = g;
     a.m = m;
+    a.m_bits = m_bits;
+    a.m_scales = m_scales;
     a.e = e;
     a.v = v;
     a.x = x;
@@ -773,6 +815,19 @@ extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void
     a.slots = ws.slots;
     a.spin_limit = kSpinLimit;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (packed) {
+        switch (g_dtype) {
+            case ONEBIT_BF16:
+                return x_bf16 ? launch<kUpdatePM, kGradBF16, true>(plan, a, s)
+                              : launch<kUpdatePM, kGradBF16, false>(plan, a, s);
+            case ONEBIT_F16:
+                return x_bf16 ? launch<kUpdatePM, kGradF16, true>(plan, a, s)
+                              : launch<kUpdatePM, kGradF16, false>(plan, a, s);
+            default:
+                return x_bf16 ? launch<kUpdatePM, kGradF32, true>(plan, a, s)
+                              : launch<kUpdatePM, kGradF32, false>(plan, a, s);
+        }
+    }
     switch (g_dtype) {
         case ONEBIT_BF16:
             if (!update) return launch<kCompressOnly, kGradBF16, false>(plan, a, s);
@@ -784,6 +839,25 @@ extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void
             if (!update) return launch<kCompressOnly, kGradF32, false>(plan, a, s);
             return x_bf16 ? launch<kUpdate, kGradF32, true>(plan, a, s) : launch<kUpdate, kGradF32, false>(plan, a, s);
     }
+}
+
+extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
+                                                  float *m, float *e, const float *v, float *x,
+                                                  uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
+                                                  double beta1, double eps, double weight_decay,
+                                                  void *workspace, void *stream) {
+    return compress_entry(plan, g, g_dtype, m, nullptr, nullptr, e, v, x, x_bf16, bits, scales, lr, beta1, eps,
+                          weight_decay, workspace, stream);
+}
+
+extern "C" onebit_status_t onebit_compress_update_packed(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
+                                                         const uint32_t *m_bits, const float *m_scales, float *e,
+                                                         const float *v, float *x, uint16_t *x_bf16, uint32_t *bits,
+                                                         float *scales, double lr, double beta1, double eps,
+                                                         double weight_decay, void *workspace, void *stream) {
+    if (!m_scales || !v || !x) return ONEBIT_ERR_INVALID;
+    return compress_entry(plan, g, g_dtype, nullptr, m_bits, m_scales, e, v, x, x_bf16, bits, scales, lr, beta1,
+                          eps, weight_decay, workspace, stream);
 }
 
 extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *worker_bits,

@@ -180,6 +180,23 @@ onebit_status_t onebit_compress_update(onebit_plan_t plan, const void *g, onebit
                                        double beta1, double eps, double weight_decay,
                                        void *workspace, void *stream);
 
+/* onebit_compress_update in update mode with the momentum kept in its compressed
+ * form.  After every compressed step m is exactly the decompression of that step's
+ * sign words and chunk scales (0 in masked tensors), so it need not be stored as
+ * fp32: this call takes the previous step's words and scales as m,
+ *   m_i = masked(i) ? 0 : (bit_i(m_bits) ? -m_scales[j] : +m_scales[j]),
+ * performs the same step as onebit_compress_update (bits, scales, e, x, x_bf16
+ * identical bit for bit) and writes no m: the new momentum is (bits, scales).
+ * Per element it moves 24.25 bytes instead of 32.125.  m_bits: uint32
+ * [plan_words], m_scales: fp32 [n_chunks], both read-only and distinct from bits
+ * and scales (callers alternate two pairs).  The first compressed step after the
+ * warmup, whose m is the fp32 Adam momentum, uses onebit_compress_update. */
+onebit_status_t onebit_compress_update_packed(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
+                                              const uint32_t *m_bits, const float *m_scales, float *e,
+                                              const float *v, float *x, uint16_t *x_bf16, uint32_t *bits,
+                                              float *scales, double lr, double beta1, double eps,
+                                              double weight_decay, void *workspace, void *stream);
+
 /* Server stage of the compressed all-reduce over W workers' streams held in one
  * GPU's memory ([DSG] sec. 4, server_error; [1BA] "proposed method"):
  *   a_i = fl32( (sum_{w=0..W-1} (bit_{w,i} ? -s_{w,j} : +s_{w,j})) / W )   (fp64)

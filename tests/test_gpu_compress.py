@@ -172,7 +172,9 @@ def test_unaligned_chunk_starts_and_compress_only():
     run_steps(off, 3, init=init, grads=grads, compress_only=True)
 
 
-def test_masks_sharing_chunks_and_tiles():
+@pytest.mark.parametrize("grad_dtype,mode", [("f32", "update_xbf16"), ("bf16", "update"), ("f16", "update"),
+                                             ("f32", "compress_only"), ("bf16", "compress_only")])
+def test_masks_sharing_chunks_and_tiles(grad_dtype, mode):
     rng = np.random.default_rng(23)
     t_off = W.offsets_from_sizes([100, 37, 5000, 64, 9000, 4096, 4096, 11])
     keep = np.array([1, 0, 1, 0, 1, 0, 0, 1], np.uint8)
@@ -180,9 +182,16 @@ def test_masks_sharing_chunks_and_tiles():
     n = int(t_off[-1])
     assert int(c_off[-1]) == n
     init = rand_state(n, rng)
-    grads = lambda s: (np.random.default_rng(300 + s).standard_normal(n) * 1e-3).astype(np.float32)  # noqa: E731
-    say("masks sharing chunks")
-    run_steps(c_off, 3, init=init, grads=grads, tensor_off=t_off, tensor_keep=keep, x_bf16=True)
+
+    def grads(s):
+        g = (np.random.default_rng(300 + s).standard_normal(n) * 1e-3).astype(np.float32)
+        if grad_dtype == "bf16":
+            return torch.from_numpy(g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return g.astype(np.float16) if grad_dtype == "f16" else g
+
+    say(f"masks sharing chunks, {grad_dtype} gradients, {mode}")
+    run_steps(c_off, 3, init=init, grads=grads, tensor_off=t_off, tensor_keep=keep, x_bf16=mode == "update_xbf16",
+              compress_only=mode == "compress_only")
 
 
 def test_weight_decay_and_hyperparameters():
