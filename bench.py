@@ -47,6 +47,7 @@ B_COMPRESS_PACKED = 24.25    # read g,e,v,x (16 B) and 1/8 B of momentum words; 
 B_WORKER = 16.125            # read g,m,e; write e; bits
 B_WORKER_F16 = 14.125        # read g fp16 (2), m, e; write e; bits
 B_FINISH_MASK = 21.0         # read m, mask (1), v, x; write m, x
+B_FINISH_PACKED = 13.125     # read 1/8 B of server words, mask (1), v, x; write x
 B_QSDP4, B_QSDP8 = 2.0 + 0.5 + 8.0 / 1024, 2.0 + 1.0 + 8.0 / 1024
 
 
@@ -671,9 +672,62 @@ def secondary_rows(dev, args):
                                              finish_kernel_gbps=B_FINISH_MASK * a.n / (f_ms * 1e-3) / 1e9,
                                              finish_kernel_ms=f_ms,
                                              finish_roofline=roof(B_FINISH_MASK * a.n / (f_ms * 1e-3) / 1e9))
-    del m, e, es, g16, v, x, mask, wbits, wsc, sbits, ssc, wsp, plan
+    # the same full step with the momentum kept as the server's words and scales
+    pb = [sbits, torch.zeros_like(sbits)]
+    pss = [ssc, torch.zeros_like(ssc)]
+    flip = [0]
+
+    def full_step_packed():
+        c = flip[0]
+        for w in range(a.W):
+            ob.onebit_compress_update_packed(plan, g16[w], pb[c], pss[c], e[w], None, None, None, wbits[w], wsc[w],
+                                             lr=0.0, beta1=0.9, eps=1e-8, weight_decay=0.0, workspace=wsp,
+                                             m_mask=mask)
+        ob.onebit_server_reduce(plan, wbits, wsc, es, pb[1 - c], pss[1 - c], None, wsp)
+        ob.onebit_momentum_update_packed(plan, pb[1 - c], pss[1 - c], mask, v, x, None, lr=1e-3, eps=1e-8,
+                                         weight_decay=0.01)
+        flip[0] = 1 - c
+    t, kt = timed(full_step_packed, steps, 1)
+    assert ob.onebit_workspace_status(wsp) == 0
+    step_bytes = ((B_WORKER_F16 - 4.0 + 1.125) * a.W + 10.125 + B_FINISH_PACKED) * a.n
+    rows["full_step_16x64M_f16_mask_packed_m"] = dict(ms_per_step=t * 1e3, gbps=step_bytes / t / 1e9,
+                                                      finish_kernel_ms=kt.mean_ms("momentum_update"))
+    # one GPU's share of the same step on 16 GPUs: its own worker over the whole
+    # vector, the server stage over its 4M-element shard with 16 workers' streams of
+    # that shard, and the finish over the whole vector (the all-gather between them is
+    # not simulated); fp32 momentum, then the packed momentum
+    shard = int(a.chunk_off[1])
+    plan_s = ob.onebit_plan_create(np.array([0, shard], np.int64))
+    ws_s = torch.zeros(ob.onebit_plan_workspace_bytes(plan_s) // 8, dtype=torch.int64, device=dev)
+    sw = ob.onebit_plan_words(plan_s)
+    wbits_s = wbits[:, :sw].contiguous()
+    wsc_s = wsc[:, :1].contiguous()
+    es_s = torch.zeros(shard, device=dev)
+    sb_s, ss_s, mo_s = torch.zeros(sw, dtype=torch.int32, device=dev), torch.zeros(1, device=dev), \
+        torch.zeros(shard, device=dev)
+
+    def gpu_share():
+        ob.onebit_compress_update(plan, g16[0], m, e[0], None, None, None, wbits[0], wsc[0], lr=0.0, beta1=0.9,
+                                  eps=1e-8, weight_decay=0.0, workspace=wsp)
+        ob.onebit_server_reduce(plan_s, wbits_s, wsc_s, es_s, sb_s, ss_s, mo_s, ws_s)
+        ob.onebit_momentum_update(m, mask, v, x, None, lr=1e-3, eps=1e-8, weight_decay=0.01)
+
+    def gpu_share_packed():
+        c = flip[0]
+        ob.onebit_compress_update_packed(plan, g16[0], pb[c], pss[c], e[0], None, None, None, wbits[0], wsc[0],
+                                         lr=0.0, beta1=0.9, eps=1e-8, weight_decay=0.0, workspace=wsp, m_mask=mask)
+        ob.onebit_server_reduce(plan_s, wbits_s, wsc_s, es_s, sb_s, ss_s, None, ws_s)
+        ob.onebit_momentum_update_packed(plan, pb[c], pss[c], mask, v, x, None, lr=1e-3, eps=1e-8,
+                                         weight_decay=0.01)
+    t1, _ = timed(gpu_share, steps, 1)
+    t2, _ = timed(gpu_share_packed, steps, 1)
+    rows["gpu_share_of_16_64M_f16_mask"] = dict(ms_per_step=t1 * 1e3, params_per_s=a.n / t1)
+    rows["gpu_share_of_16_64M_f16_mask_packed_m"] = dict(ms_per_step=t2 * 1e3, params_per_s=a.n / t2)
+    del m, e, es, g16, v, x, mask, wbits, wsc, sbits, ssc, wsp, plan, pb, pss, plan_s, ws_s, wbits_s, wsc_s, es_s
     torch.cuda.empty_cache()
-    log(f"[bench] allreduce {rows['allreduce_16x64M']} full step {rows['full_step_16x64M_f16_mask']}")
+    log(f"[bench] allreduce {rows['allreduce_16x64M']} full step {rows['full_step_16x64M_f16_mask']} "
+        f"packed {rows['full_step_16x64M_f16_mask_packed_m']} one GPU's share "
+        f"{rows['gpu_share_of_16_64M_f16_mask']} packed {rows['gpu_share_of_16_64M_f16_mask_packed_m']}")
 
     # the headline step with the momentum kept as the previous step's words and scales
     wl = W.bert_like()

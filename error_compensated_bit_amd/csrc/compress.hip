@@ -28,9 +28,12 @@
 
 namespace onebit {
 
-// kUpdatePM: the update mode with the momentum held in its compressed form (the
-// previous step's sign words and chunk scales) instead of an fp32 array.
-enum Mode { kUpdate = 0, kCompressOnly = 1, kServer = 2, kUpdatePM = 3 };
+// kUpdatePM / kCompressPM: the update / compress-only modes with the momentum held
+// in its compressed form (the previous step's sign words and chunk scales) instead
+// of an fp32 array.
+enum Mode { kUpdate = 0, kCompressOnly = 1, kServer = 2, kUpdatePM = 3, kCompressPM = 4 };
+constexpr bool packed_m(int mode) { return mode == kUpdatePM || mode == kCompressPM; }
+constexpr bool compress_only(int mode) { return mode == kCompressOnly || mode == kCompressPM; }
 
 struct CompressArgs {
     const TileDesc *tiles;
@@ -42,8 +45,9 @@ struct CompressArgs {
     // worker inputs / state
     const void *g;
     float *m;
-    const uint32_t *m_bits;  // kUpdatePM: m = decompression of these words and scales
-    const float *m_scales;
+    const uint32_t *m_bits;  // packed modes: m = decompression of these words and scales,
+    const float *m_scales;   // zero where m_mask (uint8 per element, nullable) is 0
+    const uint8_t *m_mask;
     float *e;         // worker error, or the server error in server mode
     const float *v;
     float *x;
@@ -188,16 +192,44 @@ __device__ __forceinline__ uint32_t thread_mask_bits(const CompressArgs &a, cons
     return bits;
 }
 
+// Elements of this thread whose byte in the caller's element mask is 0 (same bit
+// layout as thread_mask_bits; none without a mask).
+__device__ __forceinline__ uint32_t element_mask_bits(const CompressArgs &a, const TileDesc &t) {
+    if (!a.m_mask) return 0u;
+    uint32_t bits = 0u;
+    const bool full = tile_full(a, t);
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+        const uint32_t k0 = lane_k0(r);
+        if (full) {  // four mask bytes as one aligned word
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(a.m_mask + t.start + k0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (((w >> (8 * q)) & 0xffu) == 0) bits |= 1u << (4 * r + q);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t k = k0 + q;
+                if (k < (uint32_t)t.len && a.m_mask[t.start + k] == 0) bits |= 1u << (4 * r + q);
+            }
+        }
+    }
+    return bits;
+}
+
 // The momentum of four elements from the previous step's packed form: +-scale by
 // sign bit, 0 for masked elements (as the fp32 form holds them).
 __device__ __forceinline__ void load_packed_m4(const CompressArgs &a, const TileDesc &t, uint32_t k0,
-                                               uint32_t masked4, float (&m4)[4]) {
+                                               uint32_t masked4, uint32_t dropped4, float (&m4)[4]) {
     const float s = a.m_scales[t.chunk];
     const uint32_t wi = k0 >> 5;
     const uint32_t word = wi < (((uint32_t)t.len + 31u) >> 5) ? a.m_bits[t.word + wi] : 0u;
     const uint32_t nib = word >> (k0 & 31u);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) m4[q] = ((masked4 >> q) & 1u) ? 0.0f : (((nib >> q) & 1u) ? -s : s);
+    for (int q = 0; q < 4; ++q) {
+        const float mq = ((nib >> q) & 1u) ? -s : s;
+        m4[q] = ((masked4 >> q) & 1u) ? 0.0f : (((dropped4 >> q) & 1u) ? mul_rn(mq, 0.0f) : mq);
+    }
 }
 
 template <int MODE, int GT>
@@ -206,17 +238,21 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
                                                uint32_t *s_words) {
     const bool full = tile_full(a, t);
     if (MODE != kServer) {
-        const float *mb = MODE == kUpdatePM ? nullptr : a.m + t.start;
+        const float *mb = packed_m(MODE) ? nullptr : a.m + t.start;
         const float *eb = a.e + t.start;
+        // the packed momentum is 0 where the fp32 one would hold 0: +0 in masked
+        // tensors in the update mode (whose step stores +0), and +-s * 0 where the
+        // caller's element mask is 0 (as the finish multiplies by the mask)
         const uint32_t masked = MODE == kUpdatePM ? thread_mask_bits(a, t) : 0u;
+        const uint32_t dropped = packed_m(MODE) ? element_mask_bits(a, t) : 0u;
 #pragma unroll
         for (int r = 0; r < kGroups; ++r) {
             const uint32_t k0 = lane_k0(r);
             float g4[4], m4[4], e4[4];
-            if (MODE == kUpdatePM) load_packed_m4(a, t, k0, (masked >> (4 * r)) & 0xFu, m4);
+            if (packed_m(MODE)) load_packed_m4(a, t, k0, (masked >> (4 * r)) & 0xFu, (dropped >> (4 * r)) & 0xFu, m4);
             if (full) {
                 load_g4<GT>(a.g, t.start, k0, g4);
-                if (MODE != kUpdatePM) load4(mb, k0, m4);
+                if (!packed_m(MODE)) load4(mb, k0, m4);
                 load4(eb, k0, e4);
             } else {
 #pragma unroll
@@ -226,7 +262,7 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
                     g4[q] = in ? (GT != kGradF32 ? half_bits_to_float<GT>(static_cast<const uint16_t *>(a.g)[t.start + k])
                                                  : static_cast<const float *>(a.g)[t.start + k])
                                : 0.0f;
-                    if (MODE != kUpdatePM) m4[q] = in ? mb[k] : 0.0f;
+                    if (!packed_m(MODE)) m4[q] = in ? mb[k] : 0.0f;
                     e4[q] = in ? eb[k] : 0.0f;
                 }
             }
@@ -439,7 +475,7 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
                         if (mo) mo[k0 + q] = q4[q];
                     }
             }
-        } else if (MODE == kCompressOnly) {
+        } else if (compress_only(MODE)) {
             if (full) {
                 store4(eb, k0, e4);
             } else {
@@ -748,6 +784,9 @@ int32_t coop_capacity(int device) {
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradBF16, true>),
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF16, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF16, true>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kCompressPM, kGradF32, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kCompressPM, kGradBF16, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kCompressPM, kGradF16, false>),
     };
     int per_cu = 1 << 30;
     for (const void *f : fns) {
@@ -766,7 +805,8 @@ using namespace onebit;
 // Validation and dispatch shared by the fp32-momentum and the packed-momentum
 // entry points (exactly one of m and m_bits is given).
 static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype, float *m,
-                                      const uint32_t *m_bits, const float *m_scales, float *e, const float *v,
+                                      const uint32_t *m_bits, const float *m_scales, const uint8_t *m_mask,
+                                      float *e, const float *v,
                                       float *x, uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
                                       double beta1, double eps, double weight_decay, void *workspace,
                                       void *stream) {
@@ -775,7 +815,8 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     const bool packed = m_bits != nullptr || m_scales != nullptr;
     const bool update = (v != nullptr) || (x != nullptr);
     if (update && (!v || !x)) return ONEBIT_ERR_INVALID;
-    if (!update && (x_bf16 || packed)) return ONEBIT_ERR_INVALID;
+    if (!update && x_bf16) return ONEBIT_ERR_INVALID;
+    if (m_mask && !packed) return ONEBIT_ERR_INVALID;
     if (plan->n_chunks == 0) return ONEBIT_OK;
     if (!scales || !workspace) return ONEBIT_ERR_INVALID;
     if (packed && (!m_scales || (plan->n > 0 && !m_bits) || m_scales == scales || (m_bits && m_bits == bits)))
@@ -785,7 +826,7 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     for (const void *q : vec)
         if (q && !aligned16(q)) return ONEBIT_ERR_ALIGN;
     if (!aligned_to(bits, 4) || !aligned_to(scales, 4) || !aligned_to(workspace, 8)) return ONEBIT_ERR_ALIGN;
-    if (!aligned_to(m_bits, 4) || !aligned_to(m_scales, 4)) return ONEBIT_ERR_ALIGN;
+    if (!aligned_to(m_bits, 4) || !aligned_to(m_scales, 4) || !aligned_to(m_mask, 4)) return ONEBIT_ERR_ALIGN;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return ONEBIT_ERR_INVALID;
 
@@ -798,6 +839,7 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     a.m = m;
     a.m_bits = m_bits;
     a.m_scales = m_scales;
+    a.m_mask = m_mask;
     a.e = e;
     a.v = v;
     a.x = x;
@@ -815,6 +857,13 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     a.slots = ws.slots;
     a.spin_limit = kSpinLimit;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (packed && !update) {
+        switch (g_dtype) {
+            case ONEBIT_BF16: return launch<kCompressPM, kGradBF16, false>(plan, a, s);
+            case ONEBIT_F16: return launch<kCompressPM, kGradF16, false>(plan, a, s);
+            default: return launch<kCompressPM, kGradF32, false>(plan, a, s);
+        }
+    }
     if (packed) {
         switch (g_dtype) {
             case ONEBIT_BF16:
@@ -846,18 +895,19 @@ extern "C" onebit_status_t onebit_compress_update(onebit_plan_t plan, const void
                                                   uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
                                                   double beta1, double eps, double weight_decay,
                                                   void *workspace, void *stream) {
-    return compress_entry(plan, g, g_dtype, m, nullptr, nullptr, e, v, x, x_bf16, bits, scales, lr, beta1, eps,
-                          weight_decay, workspace, stream);
+    return compress_entry(plan, g, g_dtype, m, nullptr, nullptr, nullptr, e, v, x, x_bf16, bits, scales, lr, beta1,
+                          eps, weight_decay, workspace, stream);
 }
 
 extern "C" onebit_status_t onebit_compress_update_packed(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
-                                                         const uint32_t *m_bits, const float *m_scales, float *e,
-                                                         const float *v, float *x, uint16_t *x_bf16, uint32_t *bits,
-                                                         float *scales, double lr, double beta1, double eps,
-                                                         double weight_decay, void *workspace, void *stream) {
-    if (!m_scales || !v || !x) return ONEBIT_ERR_INVALID;
-    return compress_entry(plan, g, g_dtype, nullptr, m_bits, m_scales, e, v, x, x_bf16, bits, scales, lr, beta1,
-                          eps, weight_decay, workspace, stream);
+                                                         const uint32_t *m_bits, const float *m_scales,
+                                                         const uint8_t *m_mask, float *e, const float *v, float *x,
+                                                         uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
+                                                         double beta1, double eps, double weight_decay,
+                                                         void *workspace, void *stream) {
+    if (!m_scales) return ONEBIT_ERR_INVALID;
+    return compress_entry(plan, g, g_dtype, nullptr, m_bits, m_scales, m_mask, e, v, x, x_bf16, bits, scales, lr,
+                          beta1, eps, weight_decay, workspace, stream);
 }
 
 extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *worker_bits,

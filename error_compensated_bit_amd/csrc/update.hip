@@ -79,9 +79,127 @@ __global__ __launch_bounds__(256) void k_momentum_update(UpdateArgs a) {
     }
 }
 
+// The finish with the all-reduced momentum in its compressed form: the server's
+// sign words and chunk scales of a plan, m = +-scale times the mask (0 or 1).
+// One 2048-element tile of the plan per workgroup and iteration, eight elements per
+// thread as two groups of four (the layout of the compression kernels), so each
+// thread's four signs sit in one word.  Nothing is written to m.
+struct PackedUpdateArgs {
+    const TileDesc *tiles;
+    int64_t n_tiles;
+    const uint32_t *m_bits;
+    const float *m_scales;
+    const uint8_t *mask;
+    const float *v;
+    float *x;
+    uint16_t *xb;
+    float lr, eps, wd;
+};
+
+template <bool XB>
+__global__ __launch_bounds__(256) void k_momentum_update_packed(PackedUpdateArgs a) {
+    for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+        const TileDesc t = a.tiles[tile];
+        if (t.len == 0) continue;
+        const float s = a.m_scales[t.chunk];
+        const bool full = t.len == kTile && (t.start & 3) == 0;
+#pragma unroll
+        for (int r = 0; r < kGroups; ++r) {
+            const uint32_t k0 = 4u * (threadIdx.x + kBlock * r);
+            if (k0 >= (uint32_t)t.len) continue;
+            const uint32_t nib = a.m_bits[t.word + (k0 >> 5)] >> (k0 & 31u);
+            const int64_t i0 = t.start + k0;
+            float m4[4], v4[4], x4[4], xn[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool in = k0 + q < (uint32_t)t.len;
+                const bool keep = !a.mask || (in && a.mask[i0 + q] != 0);
+                // as onebit_momentum_update forms it: m * (mask ? 1 : 0)
+                m4[q] = mul_rn(((nib >> q) & 1u) ? -s : s, keep ? 1.0f : 0.0f);
+            }
+            if (full) {
+                const float4 vv = *reinterpret_cast<const float4 *>(a.v + i0);
+                const float4 xx = *reinterpret_cast<const float4 *>(a.x + i0);
+                v4[0] = vv.x; v4[1] = vv.y; v4[2] = vv.z; v4[3] = vv.w;
+                x4[0] = xx.x; x4[1] = xx.y; x4[2] = xx.z; x4[3] = xx.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bool in = k0 + q < (uint32_t)t.len;
+                    v4[q] = in ? a.v[i0 + q] : 1.0f;
+                    x4[q] = in ? a.x[i0 + q] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float upd = add_rn(m4[q] / (sqrtf(v4[q]) + a.eps), mul_rn(a.wd, x4[q]));
+                xn[q] = sub_rn(x4[q], mul_rn(a.lr, upd));
+            }
+            if (full) {
+                *reinterpret_cast<float4 *>(a.x + i0) = make_float4(xn[0], xn[1], xn[2], xn[3]);
+                if (XB) {
+                    uint2 pk;
+                    pk.x = float_to_bf16_bits(xn[0]) | (float_to_bf16_bits(xn[1]) << 16);
+                    pk.y = float_to_bf16_bits(xn[2]) | (float_to_bf16_bits(xn[3]) << 16);
+                    *reinterpret_cast<uint2 *>(a.xb + i0) = pk;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (k0 + q < (uint32_t)t.len) {
+                        a.x[i0 + q] = xn[q];
+                        if (XB) a.xb[i0 + q] = (uint16_t)float_to_bf16_bits(xn[q]);
+                    }
+            }
+        }
+    }
+}
+
 }  // namespace onebit
 
 using namespace onebit;
+
+extern "C" onebit_status_t onebit_momentum_update_packed(onebit_plan_t plan, const uint32_t *m_bits,
+                                                         const float *m_scales, const uint8_t *mask, const float *v,
+                                                         float *x, uint16_t *x_bf16, double lr, double eps,
+                                                         double weight_decay, void *stream) {
+    if (!plan) return ONEBIT_ERR_INVALID;
+    if (plan->n == 0) return ONEBIT_OK;
+    if (!m_bits || !m_scales || !v || !x) return ONEBIT_ERR_INVALID;
+    if (!aligned_to(m_bits, 4) || !aligned_to(m_scales, 4) || !aligned16(v) || !aligned16(x) ||
+        (x_bf16 && !aligned16(x_bf16)))
+        return ONEBIT_ERR_ALIGN;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return ONEBIT_ERR_INVALID;
+    PackedUpdateArgs a{};
+    a.tiles = plan->d_tiles;
+    a.n_tiles = plan->n_tiles;
+    a.m_bits = m_bits;
+    a.m_scales = m_scales;
+    a.mask = mask;
+    a.v = v;
+    a.x = x;
+    a.xb = x_bf16;
+    a.lr = (float)lr;
+    a.eps = (float)eps;
+    a.wd = (float)weight_decay;
+    int cus = 256;
+    int v_cus = 0;
+    if (hipDeviceGetAttribute(&v_cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v_cus > 0)
+        cus = v_cus;
+    int64_t blocks = plan->n_tiles;
+    const int64_t cap = (int64_t)cus * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    prof_before(kProfMomentumUpdate, s);
+    if (x_bf16)
+        hipLaunchKernelGGL(k_momentum_update_packed<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_momentum_update_packed<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    prof_after(s);
+    return hip_status(hipGetLastError());
+}
 
 extern "C" onebit_status_t onebit_momentum_update(float *m, const uint8_t *mask, const float *v, float *x,
                                                   uint16_t *x_bf16, int64_t n, double lr, double eps,

@@ -39,7 +39,8 @@ _SIGS = {
     "onebit_profile_end": (_I, [_P, _P]),
     "onebit_adam_warmup_step": (_I, [_P, _P, _P, _P, _I, _I64, _D, _D, _D, _D, _D, _I, _I64, _P]),
     "onebit_compress_update": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
-    "onebit_compress_update_packed": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
+    "onebit_compress_update_packed": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
+    "onebit_momentum_update_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _P]),
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _P]),
     "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
@@ -249,11 +250,18 @@ def onebit_compress_update(plan, g, m, e, v, x, x_bf16, bits, scales, *, lr, bet
 
 
 def onebit_compress_update_packed(plan, g, m_bits, m_scales, e, v, x, x_bf16, bits, scales, *, lr, beta1, eps,
-                                  weight_decay, workspace, stream=None):
+                                  weight_decay, workspace, m_mask=None, stream=None):
     _check(load().onebit_compress_update_packed(plan.handle, _ptr(g), _dtype_code(g), _ptr(m_bits), _ptr(m_scales),
-                                                _ptr(e), _ptr(v), _ptr(x), _ptr(x_bf16), _ptr(bits), _ptr(scales),
-                                                lr, beta1, eps, weight_decay, _ptr(workspace), _stream(stream)),
+                                                _ptr(m_mask), _ptr(e), _ptr(v), _ptr(x), _ptr(x_bf16), _ptr(bits),
+                                                _ptr(scales), lr, beta1, eps, weight_decay, _ptr(workspace),
+                                                _stream(stream)),
            "onebit_compress_update_packed")
+
+
+def onebit_momentum_update_packed(plan, m_bits, m_scales, mask, v, x, x_bf16, *, lr, eps, weight_decay, stream=None):
+    _check(load().onebit_momentum_update_packed(plan.handle, _ptr(m_bits), _ptr(m_scales), _ptr(mask), _ptr(v), _ptr(x),
+                                                _ptr(x_bf16), lr, eps, weight_decay, _stream(stream)),
+           "onebit_momentum_update_packed")
 
 
 def onebit_server_reduce(plan, worker_bits, worker_scales, server_error, server_bits, server_scales, m_out,

@@ -180,22 +180,29 @@ onebit_status_t onebit_compress_update(onebit_plan_t plan, const void *g, onebit
                                        double beta1, double eps, double weight_decay,
                                        void *workspace, void *stream);
 
-/* onebit_compress_update in update mode with the momentum kept in its compressed
- * form.  After every compressed step m is exactly the decompression of that step's
- * sign words and chunk scales (0 in masked tensors), so it need not be stored as
- * fp32: this call takes the previous step's words and scales as m,
- *   m_i = masked(i) ? 0 : (bit_i(m_bits) ? -m_scales[j] : +m_scales[j]),
+/* onebit_compress_update with the momentum kept in its compressed form.  After
+ * every compressed step m is exactly the decompression of that step's sign words
+ * and chunk scales (the worker's own in the fused single-worker step, 0 in masked
+ * tensors; the server's in the W-worker step, times the element mask), so it need
+ * not be stored as fp32: this call takes those words and scales as m,
+ *   m_i = bit_i(m_bits) ? -m_scales[j] : +m_scales[j],  then
+ *   m_i = m_i * 0 where m_mask[i] == 0 (m_mask: uint8 [n], 4-byte aligned, nullable; a signed zero,
+ *   as onebit_momentum_update leaves it) and, in update mode, m_i = +0 in the
+ *   plan's masked tensors (as onebit_compress_update leaves them),
  * performs the same step as onebit_compress_update (bits, scales, e, x, x_bf16
- * identical bit for bit) and writes no m: the new momentum is (bits, scales).
- * Per element it moves 24.25 bytes instead of 32.125.  m_bits: uint32
- * [plan_words], m_scales: fp32 [n_chunks], both read-only and distinct from bits
- * and scales (callers alternate two pairs).  The first compressed step after the
- * warmup, whose m is the fp32 Adam momentum, uses onebit_compress_update. */
+ * identical bit for bit) and writes no m.  Update mode (v, x given): the new
+ * momentum is (bits, scales); 24.25 bytes per element instead of 32.125.
+ * Compress-only mode (v = x = x_bf16 = NULL): the worker half of the all-reduce
+ * with m the previous server result.  m_bits: uint32 [plan_words], m_scales: fp32
+ * [n_chunks], both read-only and distinct from bits and scales (callers alternate
+ * two pairs).  The first compressed step after the warmup, whose m is the fp32
+ * Adam momentum, uses onebit_compress_update. */
 onebit_status_t onebit_compress_update_packed(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
-                                              const uint32_t *m_bits, const float *m_scales, float *e,
-                                              const float *v, float *x, uint16_t *x_bf16, uint32_t *bits,
-                                              float *scales, double lr, double beta1, double eps,
-                                              double weight_decay, void *workspace, void *stream);
+                                              const uint32_t *m_bits, const float *m_scales,
+                                              const uint8_t *m_mask, float *e, const float *v, float *x,
+                                              uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
+                                              double beta1, double eps, double weight_decay,
+                                              void *workspace, void *stream);
 
 /* Server stage of the compressed all-reduce over W workers' streams held in one
  * GPU's memory ([DSG] sec. 4, server_error; [1BA] "proposed method"):
@@ -223,6 +230,20 @@ onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *
 onebit_status_t onebit_momentum_update(float *m, const uint8_t *mask, const float *v, float *x,
                                        uint16_t *x_bf16, int64_t n, double lr, double eps,
                                        double weight_decay, void *stream);
+
+/* onebit_momentum_update with the all-reduced momentum in its compressed form (the
+ * server's sign words and chunk scales of `plan`):
+ *   m_i = (bit_i ? -m_scales[j] : +m_scales[j]) * (mask_i ? 1 : 0)   (mask nullable: all kept)
+ *   x -= lr * ( m / (sqrt(v) + eps) + weight_decay * x );  x_bf16 = bf16(x)
+ * with the same binary32 operations as onebit_momentum_update; no m is written (the
+ * next step's workers take the same words, scales and mask as their packed m).
+ * m_bits: uint32 [plan_words]; m_scales: fp32 [n_chunks]; mask: uint8 [n]; v: fp32
+ * [n] read-only; x: fp32 [n] in place; x_bf16: uint16 [n] out, nullable.  v, x,
+ * x_bf16 16-byte aligned. */
+onebit_status_t onebit_momentum_update_packed(onebit_plan_t plan, const uint32_t *m_bits,
+                                              const float *m_scales, const uint8_t *mask, const float *v,
+                                              float *x, uint16_t *x_bf16, double lr, double eps,
+                                              double weight_decay, void *stream);
 
 /* QSGD gradient quantizer, the gradient side of QSDP ([QSDP] "proposed method":
  * gradients take the standard unbiased compressor of Alistarh et al. 2017; [QSGD]

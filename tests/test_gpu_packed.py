@@ -1,5 +1,6 @@
-"""GPU parity of onebit_compress_update_packed: the update step with the momentum
-held as the previous step's sign words and chunk scales.
+"""GPU parity of the packed-momentum calls (onebit_compress_update_packed,
+onebit_momentum_update_packed): the momentum held as the previous step's sign words
+and chunk scales.
 
 From a common state, one fp32-momentum step is taken; then for three steps the
 fp32 path (onebit_compress_update) and the packed path run side by side on copies
@@ -8,7 +9,9 @@ the bf16 copy), the fp32 path's m must equal the masked decompression of the pac
 path's words, and the packed path must match the oracle run with m taken as that
 decompression.  Cases: edge chunk lengths (empty, 1, 31-33, ragged tails,
 2^20 + 5), masked tensors sharing chunks and tiles, a two-pass chunk next to
-one-pass chunks, fp32 / bf16 / fp16 gradients, full-size BERT-Large vector.
+one-pass chunks, fp32 / bf16 / fp16 gradients, full-size BERT-Large vector.  The
+W-worker step (packed compress-only workers with an element mask, server, packed
+finish) must reproduce the fp32-momentum W-worker step bit for bit in every buffer.
 """
 import numpy as np
 import pytest
@@ -160,7 +163,90 @@ def test_packed_argument_errors():
     with pytest.raises(ob.OnebitError) as ei:          # words aliasing the output words
         ob.onebit_compress_update_packed(plan, g, bits, sc[1:], f, f, f, None, bits, sc[:1], workspace=ws, **H)
     assert ei.value.status == ob.ONEBIT_ERR_INVALID
-    with pytest.raises(ob.OnebitError) as ei:          # no v / x: the packed form is for the update mode only
-        ob.onebit_compress_update_packed(plan, g, bits[4:], sc[1:], f, None, None, None, bits[:4], sc[:1],
+    xb = torch.zeros(128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ob.OnebitError) as ei:          # a bf16 copy of x without an update
+        ob.onebit_compress_update_packed(plan, g, bits[4:], sc[1:], f, None, None, xb, bits[:4], sc[:1],
                                          workspace=ws, **H)
     assert ei.value.status == ob.ONEBIT_ERR_INVALID
+    with pytest.raises(ob.OnebitError) as ei:          # no scales to decompress
+        ob.onebit_compress_update_packed(plan, g, bits[4:], None, f, f, f, None, bits[:4], sc[:1], workspace=ws, **H)
+    assert ei.value.status == ob.ONEBIT_ERR_INVALID
+
+
+@pytest.mark.parametrize("workers,dt", [(3, "f16"), (4, "bf16")])
+def test_packed_w_worker_step_with_element_mask(workers, dt):
+    """W workers on one GPU with the momentum as the server's words and scales: the
+    packed compress-only workers, the server and the packed finish must reproduce the
+    fp32-momentum step (compress-only workers, server with m_out, masked finish) bit
+    for bit in every buffer, 3 steps after a common first step."""
+    lengths = [5000, 4097, 33, (1 << 14) + 7, 1, 2048 * 3, 65]
+    off = W.offsets_from_sizes(lengths)
+    n = int(off[-1])
+    rng = np.random.default_rng(60 + workers)
+    hp = dict(lr=1e-3, eps=1e-8, weight_decay=0.01)
+    x0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    v = torch.from_numpy((rng.uniform(0.5, 2.0, n) * 1e-6).astype(np.float32)).to(DEV)
+    mask = np.ones(n, np.uint8)
+    mask[rng.random(n) < 0.05] = 0
+    maskd = torch.from_numpy(mask).to(DEV)
+    plan = ob.onebit_plan_create(off)
+    words, nch = ob.onebit_plan_words(plan), ob.onebit_plan_chunks(plan)
+    ws = torch.zeros(ob.onebit_plan_workspace_bytes(plan) // 8, dtype=torch.int64, device=DEV)
+    npad = (n + 3) // 4 * 4
+    Z = lambda *shape, dt=torch.float32: torch.zeros(shape, dtype=dt, device=DEV)  # noqa: E731
+    # path A: fp32 momentum
+    mA, eA, esA, xA = Z(n), Z(workers, npad), Z(n), torch.from_numpy(x0.copy()).to(DEV)
+    wbA, wsA, sbA, ssA, moA = Z(workers, words, dt=torch.int32), Z(workers, nch), Z(words, dt=torch.int32), Z(nch), Z(n)
+    xbA = Z(n, dt=torch.bfloat16)
+    # path B: packed momentum (server words / scales ping-pong)
+    eB, esB, xB = Z(workers, npad), Z(n), torch.from_numpy(x0.copy()).to(DEV)
+    wbB, wsB = Z(workers, words, dt=torch.int32), Z(workers, nch)
+    sbB, ssB = [Z(words, dt=torch.int32), Z(words, dt=torch.int32)], [Z(nch), Z(nch)]
+    xbB = Z(n, dt=torch.bfloat16)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    h0 = dict(lr=0.0, beta1=0.9, eps=1e-8, weight_decay=0.0)
+    for step in range(4):
+        gd = [(torch.from_numpy((np.random.default_rng(900 + 10 * step + w).standard_normal(n) * 1e-3)
+                                .astype(np.float32)).to(DEV)).to(tdt) for w in range(workers)]
+        # A
+        for w in range(workers):
+            ob.onebit_compress_update(plan, gd[w], mA, eA[w, :n], None, None, None, wbA[w], wsA[w], workspace=ws, **h0)
+        ob.onebit_server_reduce(plan, wbA, wsA, esA, sbA, ssA, moA, ws)
+        ob.onebit_momentum_update(moA, maskd, v, xA, xbA, **hp)
+        mA.copy_(moA)
+        if step == 0:            # B starts from A's state after a common first step
+            eB.copy_(eA)
+            esB.copy_(esA)
+            xB.copy_(xA)
+            sbB[0].copy_(sbA)
+            ssB[0].copy_(ssA)
+            continue
+        cur, nxt = (step - 1) % 2, step % 2
+        for w in range(workers):
+            ob.onebit_compress_update_packed(plan, gd[w], sbB[cur], ssB[cur], eB[w, :n], None, None, None, wbB[w],
+                                             wsB[w], workspace=ws, m_mask=maskd, **h0)
+        ob.onebit_server_reduce(plan, wbB, wsB, esB, sbB[nxt], ssB[nxt], None, ws)
+        ob.onebit_momentum_update_packed(plan, sbB[nxt], ssB[nxt], maskd, v, xB, xbB, **hp)
+        torch.cuda.synchronize()
+        tag = f"W={workers} {dt} step {step}"
+        assert torch.equal(wbB, wbA) and torch.equal(wsB, wsA), f"{tag}: worker words / scales"
+        assert torch.equal(eB, eA), f"{tag}: worker errors"
+        assert torch.equal(sbB[nxt], sbA) and torch.equal(ssB[nxt], ssA) and torch.equal(esB, esA), f"{tag}: server"
+        assert torch.equal(xB, xA) and torch.equal(xbB, xbA), f"{tag}: x"
+        m_dec = oracle.decompress(off, host(sbB[nxt]).view(np.uint32), host(ssB[nxt]))
+        assert_exact(f"{tag} fp32 m = masked server decompression", host(mA),
+                     np.where(mask == 0, m_dec * np.float32(0), m_dec))
+        say(f"  {tag}: packed W-worker step identical to the fp32-momentum step")
+    assert ob.onebit_workspace_status(ws) == 0
+
+
+def test_packed_finish_errors():
+    plan = ob.onebit_plan_create(W.offsets_from_sizes([100]))
+    f = torch.zeros(128, device=DEV)
+    b = torch.zeros(8, dtype=torch.int32, device=DEV)
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_momentum_update_packed(plan, b, None, None, f, f, None, lr=1e-3, eps=1e-8, weight_decay=0.0)
+    assert ei.value.status == ob.ONEBIT_ERR_INVALID
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_momentum_update_packed(plan, b, f, None, f[1:], f, None, lr=1e-3, eps=1e-8, weight_decay=0.0)
+    assert ei.value.status == ob.ONEBIT_ERR_ALIGN
