@@ -642,11 +642,20 @@ def secondary_rows(dev, args):
     t, kt = timed(allreduce_step, steps, 1)
     w_ms = kt.mean_ms("compress_onepass")
     s_ms = kt.mean_ms("server_onepass")
+    # the same 17 launches captured once in a HIP graph and replayed
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        allreduce_step()
+    t_graph, _ = timed(graph.replay, steps, 1)
+    del graph
     step_bytes = (B_WORKER * a.W + 14.125) * a.n
     rows["allreduce_16x64M"] = dict(ms_per_step=t * 1e3, gbps=step_bytes / t / 1e9,
                                     worker_kernel_gbps=B_WORKER * a.n / (w_ms * 1e-3) / 1e9,
                                     server_kernel_gbps=14.125 * a.n / (s_ms * 1e-3) / 1e9,
                                     server_kernel_ms=s_ms, worker_kernel_ms=w_ms,
+                                    ms_per_step_graph_replay=t_graph * 1e3,
                                     worker_roofline=roof(B_WORKER * a.n / (w_ms * 1e-3) / 1e9),
                                     server_roofline=roof(14.125 * a.n / (s_ms * 1e-3) / 1e9))
     # the same exchange as a full step: fp16 gradients, the server's result masked
