@@ -76,6 +76,9 @@ struct CompressArgs {
 // A wait that runs out records an error in the workspace; from then on no wait
 // of any workgroup spins again, so a kernel always drains in bounded time.
 constexpr uint32_t kSpinLimit = 1u << 20;
+// Limit used by the next launches (diagnostics can lower it to exercise the
+// failure path; a wait that gives up records an error in the workspace).
+static uint32_t g_spin_limit = kSpinLimit;
 
 __device__ __forceinline__ bool give_up(const CompressArgs &a, uint32_t spins) {
     return spins >= a.spin_limit || ((spins & 255u) == 255u && ld_agent(a.err) != 0);
@@ -855,7 +858,7 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     a.err = ws.err;
     a.publish = ws.publish;
     a.slots = ws.slots;
-    a.spin_limit = kSpinLimit;
+    a.spin_limit = g_spin_limit;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (packed && !update) {
         switch (g_dtype) {
@@ -945,6 +948,8 @@ extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const
     a.err = ws.err;
     a.publish = ws.publish;
     a.slots = ws.slots;
-    a.spin_limit = kSpinLimit;
+    a.spin_limit = g_spin_limit;
     return launch<kServer, kGradF32, false>(plan, a, static_cast<hipStream_t>(stream));
 }
+
+extern "C" void onebit_set_spin_limit(uint32_t limit) { g_spin_limit = limit ? limit : kSpinLimit; }

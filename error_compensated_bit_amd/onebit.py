@@ -23,6 +23,7 @@ _P, _I64, _I, _D, _U64, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_double, C.c_ui
 
 _SIGS = {
     "onebit_status_string": (C.c_char_p, [_I]),
+    "onebit_set_spin_limit": (None, [C.c_uint32]),
     "onebit_plan_create": (_I, [_P, _I64, _P, _P, _I64, C.POINTER(_P)]),
     "onebit_plan_destroy": (None, [_P]),
     "onebit_plan_host_tables": (_I, [_P, _I64, _P, _P, _I64, _P, _P, _P, _P, _P]),
@@ -281,6 +282,10 @@ def onebit_stream_probe(inputs, outputs, grid, stream=None):
     _check(load().onebit_stream_probe(_ptr(pin), len(inputs), _ptr(pout), len(outputs), inputs[0].numel(), int(grid),
                                       _stream(stream)), "onebit_stream_probe")
     return pin, pout           # keep the pointer arrays alive until the launch has run
+
+
+def onebit_set_spin_limit(limit: int) -> None:
+    load().onebit_set_spin_limit(int(limit))
 
 
 def onebit_momentum_update(m, mask, v, x, x_bf16, *, lr, eps, weight_decay, stream=None):

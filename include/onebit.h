@@ -127,6 +127,13 @@ void onebit_plan_stats(onebit_plan_t plan, int64_t *out6);
  * larger chunks take the two-pass path. */
 int64_t onebit_onepass_max_elements(void);
 
+/* Diagnostics: the number of re-polls after which a cross-workgroup wait gives up
+ * (0 restores the default, 2^20).  A wait that gives up stores an error code in the
+ * workspace (read it with onebit_workspace_status) and the call still completes,
+ * with unspecified results; a workspace with an error must be re-initialized with
+ * onebit_workspace_init before further use.  Not thread-safe; applies to later calls. */
+void onebit_set_spin_limit(uint32_t limit);
+
 /* Launch timing.  Between onebit_profile_begin and onebit_profile_end every kernel
  * the library launches is bracketed by two HIP events on its own stream.
  * onebit_profile_end synchronises on those events and returns, per kernel class,

@@ -70,3 +70,45 @@ def test_server_at_the_worker_limit():
         more = torch.zeros((Wn + 1, words), dtype=torch.int32, device=DEV)
         ob.onebit_server_reduce(plan, more, torch.zeros((Wn + 1, nch), device=DEV), esd, sbits, sscales, None, ws)
     assert ei.value.status == ob.ONEBIT_ERR_INVALID
+
+
+def test_forced_wait_timeouts_are_reported_and_recoverable():
+    """With a spin limit of one re-poll, cross-workgroup waits on large chunks give up:
+    the call still completes, the workspace reports the failure, and after
+    onebit_workspace_init and the default limit the same step matches the oracle.
+    (Should every wait happen to succeed, the results must already match.)"""
+    off = W.fixed_chunks(16 << 20, 4 << 20)
+    n = int(off[-1])
+    rng = np.random.default_rng(77)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    e0 = np.zeros(n, np.float32)
+    plan = ob.onebit_plan_create(off)
+    words, nch = ob.onebit_plan_words(plan), ob.onebit_plan_chunks(plan)
+    ws = torch.zeros(ob.onebit_plan_workspace_bytes(plan) // 8, dtype=torch.int64, device=DEV)
+    bits = torch.zeros(words, dtype=torch.int32, device=DEV)
+    sc = torch.zeros(nch, device=DEV)
+    gd = torch.from_numpy(g).to(DEV)
+    er = e0.copy()
+    rb, rs, _ = oracle.compress_update(off, g, m0.copy(), er, **H)
+    try:
+        ob.onebit_set_spin_limit(1)
+        md, ed = torch.from_numpy(m0.copy()).to(DEV), torch.from_numpy(e0.copy()).to(DEV)
+        ob.onebit_compress_update(plan, gd, md, ed, None, None, None, bits, sc, workspace=ws, **H)
+        torch.cuda.synchronize()
+        status = ob.onebit_workspace_status(ws)
+    finally:
+        ob.onebit_set_spin_limit(0)
+    say(f"  spin limit 1: workspace status {status}")
+    if status == 0:
+        assert_exact("bits with every wait satisfied", host(bits).view(np.uint32), rb)
+    else:
+        assert status in (1, 2)
+    ob.onebit_workspace_init(ws)
+    md, ed = torch.from_numpy(m0.copy()).to(DEV), torch.from_numpy(e0.copy()).to(DEV)
+    ob.onebit_compress_update(plan, gd, md, ed, None, None, None, bits, sc, workspace=ws, **H)
+    torch.cuda.synchronize()
+    assert ob.onebit_workspace_status(ws) == 0
+    assert_exact("bits after re-initialization", host(bits).view(np.uint32), rb)
+    assert check_scales("scales after re-initialization", host(sc), rs) == 0
+    assert_exact("e after re-initialization", host(ed), er)
