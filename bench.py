@@ -310,6 +310,26 @@ def quantizer_calls_meta():
             ("k_qsgd_quantize_1024<4, 1, true>", "loco4_quantize", n, None)]
 
 
+def summarize_kernels(kt_dir, command):
+    """Markdown table of the library's kernels in a kernel-trace + stats run."""
+    stats = _rows(kt_dir, "kernel_stats.csv")
+    out = ["# Kernel times of a whole benchmark run (rocprofv3 --kernel-trace --stats)", ""]
+    out.append("Commands (from the repository root, on one MI355X):")
+    out.append("```")
+    out.append(f"rocprofv3 --kernel-trace --stats --output-format csv -d {kt_dir} -o bench -- python3 {command}")
+    out.append(f"python bench.py --summarize-kernels {kt_dir} '{command}'")
+    out.append("```")
+    out.append(f"Library source digest: {source_digest()}; quantizer source digest: {quant_digest()}")
+    out.append("")
+    out.append("| kernel | calls | average ns | min ns | max ns | share of GPU time |")
+    out.append("|---|---|---|---|---|---|")
+    for r in stats:
+        if "onebit::" in r["Name"]:
+            out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                       f"{r['MaxNs']} | {float(r['Percentage']):.2f}% |")
+    return "\n".join(out) + "\n"
+
+
 def valu_per_element():
     """{label: VALU lane-instructions per element} from the committed summary, if the sources match."""
     try:
@@ -418,9 +438,13 @@ def main():
     ap.add_argument("--summarize-profile", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-quantizers", action="store_true")
     ap.add_argument("--summarize-quantizers", nargs=2, metavar=("KT_DIR", "PMC_DIR"))
+    ap.add_argument("--summarize-kernels", nargs=2, metavar=("KT_DIR", "COMMAND"))
     args = ap.parse_args()
     if args.summarize_profile:
         sys.stdout.write(summarize_profile(*args.summarize_profile))
+        return
+    if args.summarize_kernels:
+        sys.stdout.write(summarize_kernels(*args.summarize_kernels))
         return
     if args.summarize_quantizers:
         sys.stdout.write(summarize_quantizers(*args.summarize_quantizers))
