@@ -94,9 +94,23 @@ def _check(status, what):
 
 
 def _ptr(t):
+    """Device address of a tensor whose innermost dimension is dense.  Host tensors
+    are refused here: the kernels would fault on a host address."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise TypeError(f"expected a device (GPU) tensor, got one on {t.device}")
+    if t.numel() > 1 and t.stride(-1) != 1:
+        raise ValueError("the innermost dimension of a tensor argument must be contiguous")
+    if t.dim() == 1 and t.numel() > 1 and not t.is_contiguous():
+        raise ValueError("one-dimensional tensor arguments must be contiguous")
     return t.data_ptr()
+
+
+def _rows(t, row_len, what):
+    """A [rows, row_len] tensor laid out row-major with no padding between rows."""
+    if t.dim() != 2 or t.shape[1] < row_len or (t.shape[0] > 1 and t.stride(0) != row_len):
+        raise ValueError(f"{what} must be a [W, {row_len}] row-major tensor with rows of exactly {row_len} entries")
 
 
 def _stream(stream):
@@ -268,6 +282,8 @@ def onebit_momentum_update_packed(plan, m_bits, m_scales, mask, v, x, x_bf16, *,
 def onebit_server_reduce(plan, worker_bits, worker_scales, server_error, server_bits, server_scales, m_out,
                          workspace, stream=None):
     W = int(worker_scales.shape[0])
+    _rows(worker_bits, onebit_plan_words(plan), "worker_bits")
+    _rows(worker_scales, onebit_plan_chunks(plan), "worker_scales")
     _check(load().onebit_server_reduce(plan.handle, W, _ptr(worker_bits), _ptr(worker_scales), _ptr(server_error),
                                        _ptr(server_bits), _ptr(server_scales), _ptr(m_out), _ptr(workspace),
                                        _stream(stream)), "onebit_server_reduce")

@@ -63,3 +63,14 @@ def test_calls_reject_invalid_arguments_before_any_launch():
     # n == 0 is a no-op that succeeds without touching pointers
     assert lib.qsdp_quantize(None, 0, 1024, 4, 0, None, None, None, None) == ob.ONEBIT_OK
     assert lib.onebit_workspace_init(None, 64, None) == ob.ONEBIT_ERR_INVALID
+
+
+def test_host_tensors_are_refused_before_any_launch():
+    """A host tensor handed to a call would give the kernels a host address; the
+    binding refuses it (no GPU needed: nothing reaches the library)."""
+    import torch
+    t = torch.zeros(64)
+    with pytest.raises(TypeError):
+        ob.onebit_momentum_update(t, None, t, t, None, lr=1e-3, eps=1e-8, weight_decay=0.0)
+    with pytest.raises(TypeError):
+        ob.qsdp_dequantize(torch.zeros(32, dtype=torch.uint8), t, t, 64, 32, 4, None, t)
