@@ -177,6 +177,140 @@ def cpu_baseline(wl, dev, budget_s=12.0):
                 seconds=spent)
 
 
+def _oracle_rate(call, units, budget_s):
+    """Repeat call() until budget_s of CPU time is spent; units processed per second."""
+    spent, calls = 0.0, 0
+    while spent < budget_s or calls == 0:
+        t0 = time.perf_counter()
+        call()
+        spent += time.perf_counter() - t0
+        calls += 1
+    return units * calls / spent, calls
+
+
+def cpu_row_baselines(rows, budget_s=1.0):
+    """The CPU oracle timed beside each secondary row, on a bounded seeded sample of
+    that row's workload (same dtypes, distributions and bucket or chunk sizes, fewer
+    elements); single-threaded, in place on host arrays.  Step rows are scaled from
+    the sample to the row's full size."""
+    import numpy as np
+    import torch
+    import oracle
+    from error_compensated_bit_amd import workloads as W
+
+    rng = np.random.default_rng(4242)
+
+    def put(key, value, unit, sample, calls):
+        if key in rows:
+            rows[key]["cpu_oracle"] = dict(value=value, unit=unit, cores=1, kind="oracle",
+                                           sample=f"{sample}; {calls} call(s)")
+
+    # warmup Adam
+    n = 1 << 22
+    x, m, v = (rng.standard_normal(n) * 0.02).astype(np.float32), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    r, c = _oracle_rate(lambda: oracle.adam_warmup_step(x, m, v, g, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                                                        weight_decay=0.0, bias_correction=False, step=1), n, budget_s)
+    put("warmup_adam_bert_large", r, "params/s", f"{n} fp32 params", c)
+
+    # QSDP: bf16 weights N(0, 0.02), buckets of 1024
+    q = W.QsdpWorkload()
+    n = 1 << 21
+    xq = (torch.from_numpy(rng.standard_normal(n).astype(np.float32)) * q.std).to(torch.bfloat16)
+    xb = xq.view(torch.int16).numpy().view(np.uint16)
+    for bits in (4, 8):
+        r, c = _oracle_rate(lambda: oracle.qsdp_quantize(xb, bucket=q.bucket, bits=bits, seed=0), n, budget_s)
+        put(f"qsdp{bits}_quantize", r, "elems/s", f"{n} bf16 weights, buckets of {q.bucket}", c)
+        codes, bmin, bmax = oracle.qsdp_quantize(xb, bucket=q.bucket, bits=bits, seed=0)
+        r, c = _oracle_rate(lambda: oracle.qsdp_dequantize(codes, bmin, bmax, n, bucket=q.bucket, bits=bits), n,
+                            budget_s)
+        put(f"qsdp{bits}_dequantize", r, "elems/s", f"{n} bf16 weights, buckets of {q.bucket}", c)
+
+    # QSGD / LoCo on bf16 gradients with per-block scales
+    qg = W.QsgdWorkload()
+    n = 1 << 20
+    gw = [W.qsgd_gradient(qg, w, device="cpu", n=n).view(torch.int16).numpy().view(np.uint16) for w in range(qg.W)]
+    for bits in (4, 8):
+        r, c = _oracle_rate(lambda: oracle.qsgd_quantize(gw[0], bucket=qg.bucket, bits=bits, seed=7), n, budget_s)
+        put(f"qsgd{bits}_quantize", r, "elems/s", f"{n} bf16 gradient elements, buckets of {qg.bucket}", c)
+        enc = [oracle.qsgd_quantize(gw[w], bucket=qg.bucket, bits=bits, seed=100 + w) for w in range(qg.W)]
+        codes = np.stack([e_[0] for e_ in enc])
+        norms = np.stack([e_[1] for e_ in enc])
+        r, c = _oracle_rate(lambda: oracle.qsgd_reduce(codes, norms, n, bucket=qg.bucket, bits=bits), n, budget_s)
+        put(f"qsgd{bits}_reduce_{qg.W}x{qg.shard}", r, "elems/s",
+            f"{qg.W} workers' streams over a {n}-element shard", c)
+    err = np.zeros(n, np.float32)
+    g32 = oracle.bf16_bits_to_f32(gw[0])
+    r, c = _oracle_rate(lambda: oracle.loco_quantize(g32, err, bucket=qg.bucket, bits=4, beta=0.9, seed=7), n,
+                        budget_s)
+    put("loco4_quantize", r, "elems/s", f"{n} gradient elements, buckets of {qg.bucket}", c)
+
+    # the simulated all-reduce and full step: one chunk of the sample per worker
+    a = W.AllreduceWorkload()
+    n = 1 << 20
+    off = np.array([0, n], np.int64)
+    gs = [(rng.standard_normal(n) * a.grad_std).astype(np.float32) for _ in range(a.W)]
+    g16 = [gg.astype(np.float16) for gg in gs]
+    ms = np.zeros(n, np.float32)
+    es = [np.zeros(n, np.float32) for _ in range(a.W)]
+    e_s = np.zeros(n, np.float32)
+    vv = (rng.uniform(0.5, 2.0, n) * 1e-6).astype(np.float32)
+    xx = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    mask = (rng.random(n) < 0.98).astype(np.uint8)
+
+    def exchange(grads, finish):
+        enc = [oracle.compress_update(off, grads[w], ms, es[w], beta1=0.9) for w in range(a.W)]
+        wb = np.stack([e_[0] for e_ in enc])
+        wsc = np.stack([e_[1] for e_ in enc])
+        _, _, mo = oracle.server_reduce(off, wb, wsc, e_s)
+        if finish:
+            oracle.momentum_update(mo, vv, xx, mask=mask, lr=1e-3, eps=1e-8, weight_decay=0.01)
+
+    scale = a.n / n * 1e3
+    for key, grads, fin in (("allreduce_16x64M", gs, False), ("full_step_16x64M_f16_mask", g16, True),
+                            ("full_step_16x64M_f16_mask_packed_m", g16, True)):
+        r, c = _oracle_rate(lambda: exchange(grads, fin), 1.0, budget_s)
+        put(key, scale / r, "ms_per_step", f"{a.W} workers over a {n}-element sample, time scaled by {a.n // n}", c)
+
+    shard = n // a.W
+    soff = np.array([0, shard], np.int64)
+
+    def share_timed():
+        # the workers' shard encodings stand in for data received from peers: not timed
+        wb, wsc, _ = oracle.compress_update(off, g16[0], ms, es[0], beta1=0.9)
+        oracle.server_reduce(soff, shard_bits, shard_scales, e_s[:shard], want_m=True)
+        oracle.momentum_update(oracle.decompress(off, wb, wsc), vv, xx, mask=mask, lr=1e-3, eps=1e-8,
+                               weight_decay=0.01)
+    sw = (shard + 31) // 32
+    enc = [oracle.compress_update(soff, g16[w][:shard], ms[:shard].copy(), es[w][:shard], beta1=0.9)
+           for w in range(a.W)]
+    shard_bits = np.stack([e_[0][:sw] for e_ in enc])
+    shard_scales = np.stack([e_[1] for e_ in enc])
+    r, c = _oracle_rate(share_timed, 1.0, budget_s)
+    for key in ("gpu_share_of_16_64M_f16_mask", "gpu_share_of_16_64M_f16_mask_packed_m"):
+        put(key, scale / r, "ms_per_step", f"own worker and finish over a {n}-element sample, server over "
+                                          f"{shard} elements of 16 workers, time scaled by {a.n // n}", c)
+
+    # packed momentum (the oracle decompresses the previous words into m) and GPT-2-XL chunks
+    n = 1 << 21
+    off2 = np.array([0, n // 2, n], np.int64)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m, e = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    v = (rng.uniform(0.5, 2.0, n) * 1e-6).astype(np.float32)
+    x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    pb, psc, _ = oracle.compress_update(off2, g, m, e, v, x, lr=1e-3, beta1=0.9, eps=1e-8)
+
+    def packed():
+        mm = oracle.decompress(off2, pb, psc)
+        oracle.compress_update(off2, g, mm, e, v, x, lr=1e-3, beta1=0.9, eps=1e-8)
+    r, c = _oracle_rate(packed, n, budget_s)
+    put("compress_bert_large_packed_m", r, "params/s", f"two chunks of {n // 2} fp32 params", c)
+    gb = oracle.f32_to_bf16_bits(g)
+    r, c = _oracle_rate(lambda: oracle.compress_update(off2, gb, m, e, v, x, lr=1e-3, beta1=0.9, eps=1e-8,
+                                                       want_bf16=True), n, budget_s)
+    put("compress_gpt2_xl_bf16", r, "params/s", f"two chunks of {n // 2} params, bf16 g, bf16 copy of x", c)
+
+
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "compress_onepass_bert_large.md")
 ONEPASS_SOURCE = os.path.join(ROOT, "error_compensated_bit_amd", "csrc", "compress.hip")
 CALIBRATION_FLOATS = 1 << 28          # 1 GiB copied by the profile mode
@@ -486,6 +620,9 @@ def main():
         rows = secondary_rows(dev, args)
 
     base = None if args.no_cpu_baseline else cpu_baseline(wl, dev)
+    if rows and not args.no_cpu_baseline:
+        cpu_row_baselines(rows)
+        log(f"[bench] cpu oracle per row: {[(k, round(r['cpu_oracle']['value'], 3)) for k, r in rows.items() if 'cpu_oracle' in r]}")
     if base:
         log(f"[bench] cpu oracle {base['value'] / 1e6:.1f} M params/s on {base['sample']}")
 
