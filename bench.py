@@ -348,7 +348,7 @@ def profile_mode(steps):
 
 
 QUANT_SUMMARY = os.path.join(ROOT, "profiles", "quantizers_valu.md")
-QUANT_FILES = ("csrc/qsdp.hip", "csrc/qsgd.hip", "csrc/device_common.h", "build.py")
+QUANT_FILES = ("csrc/qsdp.hip", "csrc/qsgd.hip", "csrc/quant_common.h", "csrc/device_common.h", "build.py")
 VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9     # 256 CUs x 64 lanes (4 SIMD16, one wave64 op per 4 clocks) x 2.4 GHz
 
 

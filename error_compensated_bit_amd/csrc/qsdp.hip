@@ -13,6 +13,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "quant_common.h"
 
 namespace onebit {
 
@@ -50,12 +51,12 @@ struct QArgs {
     float *out_f32;
 };
 
-// Stochastic rounding of one element given its uniform word.
+// Stochastic rounding of one element given its uniform word; rdelta = RN64(1 / delta).
 template <int BITS>
-__device__ __forceinline__ uint32_t sr_code(float x, float mn, float delta, uint32_t u) {
+__device__ __forceinline__ uint32_t sr_code(float x, float mn, float delta, double rdelta, uint32_t u) {
     constexpr float L = (float)((1 << BITS) - 1);
     if (delta == 0.0f) return 0u;
-    const float t = __fdiv_rn(sub_rn(x, mn), delta);
+    const float t = div_by_recip(sub_rn(x, mn), rdelta);  // = fl32((x - mn) / delta)
     const float k = fminf(floorf(t), L);
     const float p = sub_rn(t, k);                          // exact
     // floor(p * 2^32), exact; p >= 1 only when k was clamped to L, where any
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize(QArgs a) {
         kmax = wave_max_i(kmax);
         const float mn = key_to_float(kmin), mx = key_to_float(kmax);
         const float delta = __fdiv_rn(sub_rn(mx, mn), L);
+        const double rdelta = recip_rn64(delta);
         if (lane == 0) {
             a.bmin[b] = mn;
             a.bmax[b] = mx;
@@ -115,10 +117,10 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize(QArgs a) {
             }
             const uint64_t blk = (uint64_t)i >> 2;
             const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
-            uint32_t c0 = sr_code<BITS>(f[0], mn, delta, r.a);
-            uint32_t c1 = sr_code<BITS>(f[1], mn, delta, r.b);
-            uint32_t c2 = sr_code<BITS>(f[2], mn, delta, r.c);
-            uint32_t c3 = sr_code<BITS>(f[3], mn, delta, r.d);
+            uint32_t c0 = sr_code<BITS>(f[0], mn, delta, rdelta, r.a);
+            uint32_t c1 = sr_code<BITS>(f[1], mn, delta, rdelta, r.b);
+            uint32_t c2 = sr_code<BITS>(f[2], mn, delta, rdelta, r.c);
+            uint32_t c3 = sr_code<BITS>(f[3], mn, delta, rdelta, r.d);
             if (g4 + 1 >= len) c1 = 0;
             if (g4 + 2 >= len) c2 = 0;
             if (g4 + 3 >= len) c3 = 0;
@@ -191,6 +193,7 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
         kmax = wave_max_i(kmax);
         const float mn = key_to_float(kmin), mx = key_to_float(kmax);
         const float delta = __fdiv_rn(sub_rn(mx, mn), L);
+        const double rdelta = recip_rn64(delta);
         if (lane == 0) {
             a.bmin[b] = mn;
             a.bmax[b] = mx;
@@ -200,10 +203,10 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
         for (int g = 0; g < 4; ++g) {
             const uint64_t blk = (uint64_t)(base + k0 + 4 * g) >> 2;
             const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
-            code[4 * g + 0] = sr_code<BITS>(f[4 * g + 0], mn, delta, r.a);
-            code[4 * g + 1] = sr_code<BITS>(f[4 * g + 1], mn, delta, r.b);
-            code[4 * g + 2] = sr_code<BITS>(f[4 * g + 2], mn, delta, r.c);
-            code[4 * g + 3] = sr_code<BITS>(f[4 * g + 3], mn, delta, r.d);
+            code[4 * g + 0] = sr_code<BITS>(f[4 * g + 0], mn, delta, rdelta, r.a);
+            code[4 * g + 1] = sr_code<BITS>(f[4 * g + 1], mn, delta, rdelta, r.b);
+            code[4 * g + 2] = sr_code<BITS>(f[4 * g + 2], mn, delta, rdelta, r.c);
+            code[4 * g + 3] = sr_code<BITS>(f[4 * g + 3], mn, delta, rdelta, r.d);
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q)
@@ -359,6 +362,7 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_generic(QArgs a) {
         kmax = wave_max_i(kmax);
         const float mn = key_to_float(kmin), mx = key_to_float(kmax);
         const float delta = __fdiv_rn(sub_rn(mx, mn), L);
+        const double rdelta = recip_rn64(delta);
         if (lane == 0) {
             a.bmin[b] = mn;
             a.bmax[b] = mx;
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_generic(QArgs a) {
                 const uint64_t blk = (uint64_t)i >> 2;
                 const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
                 const uint32_t w = (i & 3) == 0 ? r.a : (i & 3) == 1 ? r.b : (i & 3) == 2 ? r.c : r.d;
-                byte |= sr_code<BITS>(bf16_bits_to_float(a.x[i]), mn, delta, w) << (4 * q);
+                byte |= sr_code<BITS>(bf16_bits_to_float(a.x[i]), mn, delta, rdelta, w) << (4 * q);
             }
             a.codes[BITS == 4 ? ((base + k) >> 1) : (base + k)] = (uint8_t)byte;
         }

@@ -17,6 +17,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "quant_common.h"
 
 namespace onebit {
 
@@ -38,12 +39,12 @@ __device__ __forceinline__ float load_grad(const void *g, int64_t i) {
     return half_bits_to_float<GT>(static_cast<const uint16_t *>(g)[i]);
 }
 
-// Level and sign of one element, given its uniform word.
+// Level and sign of one element, given its uniform word; rnorm = RN64(1 / norm).
 template <int BITS>
-__device__ __forceinline__ uint32_t qsgd_code(float g, float norm, uint32_t u) {
+__device__ __forceinline__ uint32_t qsgd_code(float g, float norm, double rnorm, uint32_t u) {
     constexpr float S = (float)((1 << (BITS - 1)) - 1);
     if (norm == 0.0f) return 0u;
-    const float t = __fdiv_rn(fabsf(g), norm);           // <= 1: norm >= |g| exactly
+    const float t = div_by_recip(fabsf(g), rnorm);       // = fl32(|g| / norm) <= 1: norm >= |g|
     const float v = mul_rn(t, S);
     const float l = floorf(v);
     const float p = sub_rn(v, l);                          // exact, in [0, 1)
@@ -126,16 +127,17 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) dd_add_term(acc, (double)f[q] * (double)f[q]);   // each square exact
         const float norm = norm_of(acc);
+        const double rnorm = recip_rn64(norm);
         if (lane == 0) a.norms[b] = norm;
         uint32_t code[16];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const uint64_t blk = (uint64_t)(base + k0 + 4 * g4) >> 2;
             const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
-            code[4 * g4 + 0] = qsgd_code<BITS>(f[4 * g4 + 0], norm, r.a);
-            code[4 * g4 + 1] = qsgd_code<BITS>(f[4 * g4 + 1], norm, r.b);
-            code[4 * g4 + 2] = qsgd_code<BITS>(f[4 * g4 + 2], norm, r.c);
-            code[4 * g4 + 3] = qsgd_code<BITS>(f[4 * g4 + 3], norm, r.d);
+            code[4 * g4 + 0] = qsgd_code<BITS>(f[4 * g4 + 0], norm, rnorm, r.a);
+            code[4 * g4 + 1] = qsgd_code<BITS>(f[4 * g4 + 1], norm, rnorm, r.b);
+            code[4 * g4 + 2] = qsgd_code<BITS>(f[4 * g4 + 2], norm, rnorm, r.c);
+            code[4 * g4 + 3] = qsgd_code<BITS>(f[4 * g4 + 3], norm, rnorm, r.d);
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q)
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
             dd_add_term(acc, v * v);
         }
         const float norm = norm_of(acc);
+        const double rnorm = recip_rn64(norm);
         if (lane == 0) a.norms[b] = norm;
         const float st = LOCO ? __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u)) : 0.0f;
         const int step = BITS == 4 ? 2 : 1;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
                 const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
                 const uint32_t w = (i & 3) == 0 ? r.a : (i & 3) == 1 ? r.b : (i & 3) == 2 ? r.c : r.d;
                 const float h = value_at<GT, LOCO>(a, i);
-                const uint32_t code = qsgd_code<BITS>(h, norm, w);
+                const uint32_t code = qsgd_code<BITS>(h, norm, rnorm, w);
                 if (LOCO) a.err[i] = loco_update<BITS>(a, a.err[i], h, code, st);
                 byte |= code << (4 * q);
             }

@@ -64,6 +64,32 @@ def test_special_buckets(bits):
     quantize_both(bf16_dev(vals), 1024, bits, 3)
 
 
+def extreme_bf16(n, rng):
+    """bf16 bit patterns over the whole finite exponent range (subnormals and signed
+    zeros included; |x| < 2^126 so that every bucket's max - min stays finite), with
+    buckets of tiny values only, a bucket whose minimum is +0 and one spanning
+    2^-100 .. 2^100."""
+    u = rng.integers(0, 1 << 16, n).astype(np.uint16)
+    e = (u >> 7) & 0xFF
+    big = e > 252
+    u[big] = (u[big] & 0x807F) | (rng.integers(0, 253, int(big.sum())).astype(np.uint16) << 7)
+    u[6 * 1024:7 * 1024] &= 0x80FF                                   # exponents 0..1: subnormal / tiny
+    u[7 * 1024:8 * 1024] &= 0x7FFF                                   # non-negative ...
+    u[7 * 1024 + 5] = 0                                              # ... with minimum +0
+    ex = rng.integers(27, 228, 1024).astype(np.uint16)               # 2^-100 .. 2^100
+    u[8 * 1024:9 * 1024] = (u[8 * 1024:9 * 1024] & 0x807F) | (ex << 7)
+    return torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bucket", [1024, 1000, 64])
+def test_extreme_exponents(bits, bucket):
+    """The quotient (x - min) / step is formed from one fp64 reciprocal of the step per
+    bucket; it must round exactly as the oracle's fp32 division on every range."""
+    say(f"qsdp extreme exponents bits={bits} bucket={bucket}")
+    quantize_both(extreme_bf16(16 * 1024 + 300, np.random.default_rng(bits * 1000 + bucket)), bucket, bits, 9)
+
+
 def test_argument_errors():
     xd = bf16_dev(np.zeros(10))
     c = torch.zeros(16, dtype=torch.uint8, device=DEV)

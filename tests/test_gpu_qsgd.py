@@ -83,6 +83,40 @@ def test_quantize_parity(bucket, bits):
     say(f"  qsgd quantize bucket {bucket} bits {bits}: fp32 / bf16 / fp16 match")
 
 
+def extreme_f32(n, rng):
+    """fp32 gradients over the whole exponent range below 2^61 (subnormals and signed
+    zeros included), with a bucket of subnormals only and one spanning 2^-120 .. 2^60."""
+    u = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    e = (u >> 23) & 0xFF
+    big = e > 187
+    u[big] = (u[big] & 0x807FFFFF) | (rng.integers(0, 188, int(big.sum())).astype(np.uint32) << 23)
+    u[2048:3072] &= 0x807FFFFF                                       # subnormal bucket
+    ex = rng.integers(7, 188, 1024).astype(np.uint32)
+    u[4096:5120] = (u[4096:5120] & 0x807FFFFF) | (ex << 23)
+    return u.view(np.float32)
+
+
+@pytest.mark.parametrize("bucket", [1024, 1000])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_extreme_exponents(bucket, bits):
+    """|g| / norm is formed from one fp64 reciprocal of the norm per bucket; it must
+    round exactly as the oracle's fp32 division, subnormal quotients included."""
+    for dt in ("f32", "bf16"):
+        n = 8 * 1024 + 77
+        g = extreme_f32(n, np.random.default_rng(bucket + bits))
+        gd, gh = to_device(g, dt)
+        nb = (n + bucket - 1) // bucket
+        codes = torch.zeros(code_bytes(n, bits), dtype=torch.uint8, device=DEV)
+        norms = torch.zeros(nb, device=DEV)
+        ob.qsgd_quantize(gd, bucket, bits, 31, codes, norms)
+        rc, rn = oracle.qsgd_quantize(gh, bucket=bucket, bits=bits, seed=31)
+        torch.cuda.synchronize()
+        tag = f"extreme bucket {bucket} bits {bits} {dt}"
+        say(tag)
+        assert_exact(f"{tag} norms", host(norms), rn)
+        assert_exact(f"{tag} codes", host(codes), rc)
+
+
 @pytest.mark.parametrize("workers", [1, 2, 3, 8])
 @pytest.mark.parametrize("bucket,bits", [(1024, 4), (1000, 8), (30, 4), (2, 8), (4096, 4)])
 def test_reduce_parity(workers, bucket, bits):
