@@ -24,6 +24,19 @@ __device__ __forceinline__ int32_t order_key(float f) {
 }
 __device__ __forceinline__ float key_to_float(int32_t k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff)); }
 
+// The same order on bf16 values, two at a time in the halves of a 32-bit word
+// (packed 16-bit integer operations), and the 32-bit key of a 16-bit one:
+// order_key(float(bf16 b)) is key16(b) << 16, with the low half all ones when the
+// value is negative.
+typedef short short2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ short2_v bf16x2_keys(uint32_t w) {
+    const short2_v v = __builtin_bit_cast(short2_v, w);
+    return v ^ ((v >> (short)15) & (short2_v)(short)0x7fff);
+}
+__device__ __forceinline__ int32_t key16_to_key32(int32_t k) {
+    return (int32_t)((uint32_t)k << 16) | (k < 0 ? 0xffff : 0);
+}
+
 __device__ __forceinline__ int32_t wave_min_i(int32_t v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, 64));
@@ -162,16 +175,40 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     constexpr float L = (float)((1 << BITS) - 1);
+    const int64_t n_full = a.n >> 10;                 // buckets with all 1024 elements
+    const int k0 = 16 * lane;
+    // the next full bucket's 32 bytes per lane are loaded while this one is coded
+    uint4 nx0 = make_uint4(0u, 0u, 0u, 0u), nx1 = nx0;
+    if (wave < n_full) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + wave * 1024 + k0);
+        nx0 = src[0];
+        nx1 = src[1];
+    }
     for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
         const int64_t base = b * 1024;
         const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
-        const int k0 = 16 * lane;
+        const uint4 h0 = nx0, h1 = nx1;
+        if (b + nwaves < n_full) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (b + nwaves) * 1024 + k0);
+            nx0 = src[0];
+            nx1 = src[1];
+        }
         float f[16];
-        if (k0 + 15 < len) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + base + k0);
+        int32_t kmin = 0x7fffffff, kmax = (int32_t)0x80000000;
+        if (b < n_full) {
+            const uint32_t w[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+            short2_v kmn = bf16x2_keys(w[0]), kmx = kmn;
+#pragma unroll
+            for (int q = 1; q < 8; ++q) {
+                const short2_v k = bf16x2_keys(w[q]);
+                kmn = __builtin_elementwise_min(kmn, k);
+                kmx = __builtin_elementwise_max(kmx, k);
+            }
+            kmin = key16_to_key32(min((int32_t)kmn.x, (int32_t)kmn.y));
+            kmax = key16_to_key32(max((int32_t)kmx.x, (int32_t)kmx.y));
             float lo[8], hi[8];
-            unpack8(src[0], lo);
-            unpack8(src[1], hi);
+            unpack8(h0, lo);
+            unpack8(h1, hi);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 f[q] = lo[q];
@@ -179,14 +216,12 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) f[q] = (k0 + q < len) ? bf16_bits_to_float(a.x[base + k0 + q]) : 0.0f;
-        }
-        int32_t kmin = 0x7fffffff, kmax = (int32_t)0x80000000;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            if (k0 + q < len) {
-                kmin = min(kmin, order_key(f[q]));
-                kmax = max(kmax, order_key(f[q]));
+            for (int q = 0; q < 16; ++q) {
+                f[q] = (k0 + q < len) ? bf16_bits_to_float(a.x[base + k0 + q]) : 0.0f;
+                if (k0 + q < len) {
+                    kmin = min(kmin, order_key(f[q]));
+                    kmax = max(kmax, order_key(f[q]));
+                }
             }
         }
         kmin = wave_min_i(kmin);
@@ -208,9 +243,11 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
             code[4 * g + 2] = sr_code<BITS>(f[4 * g + 2], mn, delta, rdelta, r.c);
             code[4 * g + 3] = sr_code<BITS>(f[4 * g + 3], mn, delta, rdelta, r.d);
         }
+        if (b >= n_full) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-            if (k0 + q >= len) code[q] = 0;
+            for (int q = 0; q < 16; ++q)
+                if (k0 + q >= len) code[q] = 0;
+        }
         if (BITS == 4) {
             uint2 pk;
             pk.x = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12) | (code[4] << 16) | (code[5] << 20) |
