@@ -228,6 +228,30 @@ def test_bert_small_three_steps():
     run_steps(wl.chunk_off, 3, init=init, grads=grads, tensor_off=wl.tensor_off, tensor_keep=wl.tensor_keep)
 
 
+def test_forty_steps_with_masks_no_drift():
+    """40 compressed steps over a mixed chunk table (one-pass chunks of many lengths,
+    masked tensors sharing chunks with kept ones, bf16 copy of x), fresh gradients of
+    changing scale each step; after every step bits, scales, m and e equal the oracle's
+    and x is within tolerance, so nothing drifts as e and m evolve."""
+    lengths = [1, 33, 4097, 65541, 1000, 131072, 7, 70000, 64, 2048 * 5 + 3]
+    c_off = W.offsets_from_sizes(lengths)
+    n = int(c_off[-1])
+    t_off = np.array([0, 20, 4131, 60000, 140000, 201113, 270000, n], np.int64)
+    keep = np.array([1, 0, 1, 1, 0, 1, 1], np.uint8)
+    rng = np.random.default_rng(4040)
+    init = rand_state(n, rng)
+    scale = 10.0 ** rng.uniform(-4, -2, len(lengths))
+    per = np.repeat(scale, np.diff(c_off))
+
+    def grads(s):
+        g = np.random.default_rng(9000 + s).standard_normal(n) * per * (1.0 + 0.5 * np.sin(s))
+        g[np.repeat(keep == 0, np.diff(t_off))] = 0.0
+        return g.astype(np.float32)
+    say(f"forty steps n={n}")
+    _, nonexact = run_steps(c_off, 40, init=init, grads=grads, tensor_off=t_off, tensor_keep=keep, x_bf16=True)
+    assert nonexact == 0
+
+
 def test_repeat_is_bit_identical_and_workspace_shared_across_plans():
     rng = np.random.default_rng(26)
     offs = [W.offsets_from_sizes([70000, 4097, 1 << 20]), W.offsets_from_sizes([33, 9000])]
