@@ -5,7 +5,9 @@ A full W-worker step (W = 3 compress-only workers with fp16 gradients, the serve
 stage, the masked finish) over a plan with a two-pass chunk is captured once on one
 set of buffers; the same step runs eagerly on a copy.  Four rounds: new gradients
 are copied into both sets (eager work between replays), the graph is replayed, the
-eager step is run, and every buffer is compared bit for bit.
+eager step is run, and every buffer is compared bit for bit.  The quantizers (QSDP
+quantize and dequantize, three workers' QSGD streams and their decode-and-average, a
+LoCo step whose error average carries over) are checked the same way.
 """
 import numpy as np
 import pytest
@@ -78,3 +80,67 @@ def test_graph_replays_match_eager_steps():
             assert torch.equal(a, b), f"round {t}: buffer {k} differs between the replay and the eager step"
         say(f"  graph replay {t}: all buffers identical to the eager step")
     assert ob.onebit_workspace_status(A.ws) == 0 and ob.onebit_workspace_status(B.ws) == 0
+
+
+class QuantState:
+    """Inputs and outputs of one round of the quantizers: QSDP quantize + dequantize
+    of bf16 weights (4- and 8-bit), QSGD quantize of three workers' bf16 gradients and
+    the decode-and-average of their streams, and a LoCo step whose error average
+    carries over from round to round."""
+
+    def __init__(self, n, workers):
+        self.n, self.workers = n, workers
+        nb = (n + 1023) // 1024
+        self.x = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+        self.g = torch.zeros((workers, (n + 15) // 16 * 16), dtype=torch.bfloat16, device=DEV)   # rows 32-byte aligned
+        self.codes = {b: torch.zeros(n if b == 8 else (n + 1) // 2, dtype=torch.uint8, device=DEV) for b in (4, 8)}
+        self.bmin = {b: torch.zeros(nb, device=DEV) for b in (4, 8)}
+        self.bmax = {b: torch.zeros(nb, device=DEV) for b in (4, 8)}
+        self.y = {b: torch.zeros(n, dtype=torch.bfloat16, device=DEV) for b in (4, 8)}
+        stride = ((n + 1) // 2 + 15) // 16 * 16
+        self.qc = torch.zeros((workers, stride), dtype=torch.uint8, device=DEV)
+        self.qn = torch.zeros((workers, nb), device=DEV)
+        self.avg = torch.zeros(n, device=DEV)
+        self.err = torch.zeros(n, device=DEV)
+        self.lc = torch.zeros((n + 1) // 2, dtype=torch.uint8, device=DEV)
+        self.ln = torch.zeros(nb, device=DEV)
+
+    def run(self, stream=None):
+        n = self.n
+        for b in (4, 8):
+            ob.qsdp_quantize(self.x, 1024, b, 17 + b, self.codes[b], self.bmin[b], self.bmax[b], stream=stream)
+            ob.qsdp_dequantize(self.codes[b], self.bmin[b], self.bmax[b], n, 1024, b, self.y[b], stream=stream)
+        for w in range(self.workers):
+            ob.qsgd_quantize(self.g[w, :n], 1024, 4, 300 + w, self.qc[w], self.qn[w], stream=stream)
+        ob.qsgd_reduce(self.qc, self.qn, n, 1024, 4, out_f32=self.avg, stream=stream)
+        ob.loco_quantize(self.g[0, :n], self.err, 1024, 4, 0.9, 5, self.lc, self.ln, stream=stream)
+
+    def buffers(self):
+        return ([self.codes[b] for b in (4, 8)] + [self.bmin[b] for b in (4, 8)] + [self.bmax[b] for b in (4, 8)] +
+                [self.y[b] for b in (4, 8)] + [self.qc, self.qn, self.avg, self.err, self.lc, self.ln])
+
+
+def test_quantizer_graph_replays_match_eager_calls():
+    n, workers = 3 * 1024 * 7 + 333, 3
+    A, B = QuantState(n, workers), QuantState(n, workers)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        A.run(stream=s)
+    torch.cuda.synchronize()
+    for t in range(4):
+        rng = np.random.default_rng(500 + t)
+        x = torch.from_numpy((rng.standard_normal(n) * 0.02).astype(np.float32)).to(DEV).to(torch.bfloat16)
+        g = torch.from_numpy((rng.standard_normal((workers, n)) * 1e-3).astype(np.float32)).to(DEV).to(torch.bfloat16)
+        for S in (A, B):
+            S.x.copy_(x)
+            S.g[:, :n].copy_(g)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        B.run()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(A.buffers(), B.buffers())):
+            assert torch.equal(a, b), f"round {t}: quantizer buffer {k} differs between the replay and the eager calls"
+        say(f"  quantizer graph replay {t}: all buffers identical to the eager calls")
