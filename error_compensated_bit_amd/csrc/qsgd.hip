@@ -260,19 +260,22 @@ __device__ __forceinline__ double qsgd_accumulate(double acc, uint32_t w, double
     return __fma_rn(slv, step, acc);
 }
 
-// The E codes of one 16-byte word, unrolled with compile-time bit positions.
+// The 16 codes of one load (8 bytes of 4-bit codes, 16 bytes of 8-bit codes),
+// unrolled with compile-time bit positions.
+constexpr int kReduceE = 16;
 template <int BITS, int K = 0>
 struct Accumulate16 {
     static constexpr int PER = 32 / BITS;
-    static constexpr int E = 128 / BITS;
-    __device__ __forceinline__ static void run(double (&acc)[E], const uint32_t (&ws)[4], const double (&step)[E]) {
+    static constexpr int NW = BITS / 2;
+    __device__ __forceinline__ static void run(double (&acc)[kReduceE], const uint32_t (&ws)[NW],
+                                               const double (&step)[kReduceE]) {
         acc[K] = qsgd_accumulate<BITS, BITS * (K % PER)>(acc[K], ws[K / PER], step[K]);
         Accumulate16<BITS, K + 1>::run(acc, ws, step);
     }
 };
 template <>
-struct Accumulate16<4, 32> {
-    __device__ __forceinline__ static void run(double (&)[32], const uint32_t (&)[4], const double (&)[32]) {}
+struct Accumulate16<4, 16> {
+    __device__ __forceinline__ static void run(double (&)[16], const uint32_t (&)[2], const double (&)[16]) {}
 };
 template <>
 struct Accumulate16<8, 16> {
@@ -291,15 +294,16 @@ __device__ __forceinline__ void store_out(const RArgs &a, int64_t i, float y) {
     if (a.out_bf16) a.out_bf16[i] = (uint16_t)float_to_bf16_bits(y);
 }
 
-// One 16-byte word of every worker's row per thread and iteration: E = 32
-// consecutive elements (4-bit) or 16 (8-bit), so each load moves 16 bytes.  With
+// E = 16 consecutive elements per thread and iteration: one 8-byte (4-bit codes) or
+// 16-byte (8-bit) load of every worker's row, 16 fp64 sums live per thread.  With
 // the bucket a multiple of E the E elements share one norm (one level spacing) per
 // worker.  Sum over workers in fp64, in worker order.
 constexpr int kBatch = 4;
 
 template <int BITS, bool SHARED_NORM, bool POW2>
 __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
-    constexpr int E = 128 / BITS;
+    constexpr int E = kReduceE;
+    constexpr int NW = BITS / 2;   // 32-bit words per load
     const int64_t groups = a.n / E;
     const double Wd = (double)a.W;
     for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < groups;
@@ -312,19 +316,32 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
         // workers in batches of kBatch: every load of a batch is issued before its
         // words are decoded, so each thread keeps kBatch 16-byte loads in flight
         for (int w0 = 0; w0 < a.W; w0 += kBatch) {
-            uint4 word[kBatch];
+            uint32_t word[kBatch][NW];
             float nm[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 if (w0 + j < a.W) {
-                    word[j] = *reinterpret_cast<const uint4 *>(a.codes + (int64_t)(w0 + j) * a.code_stride + 16 * q);
+                    const uint8_t *src = a.codes + (int64_t)(w0 + j) * a.code_stride + (int64_t)(E * BITS / 8) * q;
+                    if (BITS == 4) {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(src);
+                        word[j][0] = v.x;
+                        word[j][NW > 1 ? 1 : 0] = v.y;
+                    } else {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                        word[j][0] = v.x;
+                        word[j][NW > 1 ? 1 : 0] = v.y;
+                        word[j][NW > 2 ? 2 : 0] = v.z;
+                        word[j][NW > 3 ? 3 : 0] = v.w;
+                    }
                     nm[j] = SHARED_NORM ? a.norms[(int64_t)(w0 + j) * a.norm_stride + b0] : 0.0f;
                 }
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 if (w0 + j >= a.W) break;
-                const uint32_t ws[4] = {word[j].x, word[j].y, word[j].z, word[j].w};
+                uint32_t ws[NW];
+#pragma unroll
+                for (int h = 0; h < NW; ++h) ws[h] = word[j][h];
                 double sk[E];
                 if (SHARED_NORM) {
                     const double st = (double)level_step<BITS>(nm[j]);
@@ -495,13 +512,13 @@ extern "C" onebit_status_t qsgd_reduce(int W, const uint8_t *codes, int64_t code
     a.W = W;
     a.out_f32 = out_f32;
     a.out_bf16 = out_bf16;
-    int64_t blocks = (n / (128 / bits) + 255) / 256;
+    int64_t blocks = (n / kReduceE + 255) / 256;
     const int64_t cap = (int64_t)device_cus() * 16;
     if (blocks > cap) blocks = cap;
     const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks);
     hipStream_t s = static_cast<hipStream_t>(stream);
     a.invW = 1.0 / (double)W;
-    const bool shared = bucket % (128 / bits) == 0;
+    const bool shared = bucket % kReduceE == 0;
     const bool pow2 = (W & (W - 1)) == 0;
     prof_before(kProfQsgdReduce, s);
     if (bits == 4)
