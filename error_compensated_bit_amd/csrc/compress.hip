@@ -98,19 +98,19 @@ __device__ __forceinline__ uint32_t lane_k0(int r) { return 4u * (threadIdx.x + 
 template <int GT>
 __device__ __forceinline__ void load_g4(const void *g, int64_t start, uint32_t k0, float (&g4)[4]) {
     if (GT != kGradF32) {
-        const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + start + k0);
+        const uint2 h = ld_stream(reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + start + k0));
         g4[0] = half_bits_to_float<GT>(h.x & 0xffffu);
         g4[1] = half_bits_to_float<GT>(h.x >> 16);
         g4[2] = half_bits_to_float<GT>(h.y & 0xffffu);
         g4[3] = half_bits_to_float<GT>(h.y >> 16);
     } else {
-        const float4 h = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + start + k0);
+        const float4 h = ld_stream(reinterpret_cast<const float4 *>(static_cast<const float *>(g) + start + k0));
         g4[0] = h.x; g4[1] = h.y; g4[2] = h.z; g4[3] = h.w;
     }
 }
 
 __device__ __forceinline__ void load4(const float *base, uint32_t k0, float (&v)[4]) {
-    const float4 h = *reinterpret_cast<const float4 *>(base + k0);
+    const float4 h = ld_stream(reinterpret_cast<const float4 *>(base + k0));
     v[0] = h.x; v[1] = h.y; v[2] = h.z; v[3] = h.w;
 }
 
@@ -440,7 +440,7 @@ __device__ float wait_scale(const CompressArgs &a, int chunk, const Posted &r, u
 
 
 __device__ __forceinline__ void store4(float *base, uint32_t k0, const float (&v)[4]) {
-    *reinterpret_cast<float4 *>(base + k0) = make_float4(v[0], v[1], v[2], v[3]);
+    st_stream(reinterpret_cast<float4 *>(base + k0), make_float4(v[0], v[1], v[2], v[3]));
 }
 
 // ------------------------------------------------------- tile: finish
@@ -515,7 +515,7 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
                     uint2 pk;
                     pk.x = float_to_bf16_bits(xn[0]) | (float_to_bf16_bits(xn[1]) << 16);
                     pk.y = float_to_bf16_bits(xn[2]) | (float_to_bf16_bits(xn[3]) << 16);
-                    *reinterpret_cast<uint2 *>(a.xb + t.start + k0) = pk;
+                    st_stream(reinterpret_cast<uint2 *>(a.xb + t.start + k0), pk);
                 }
             } else {
 #pragma unroll
@@ -555,7 +555,7 @@ __device__ __forceinline__ void tile_load_c(const CompressArgs &a, const TileDes
     for (int r = 0; r < kGroups; ++r) {
         const uint32_t k0 = lane_k0(r);
         if (full) {
-            const float4 cc = *reinterpret_cast<const float4 *>(eb + k0);
+            const float4 cc = ld_stream(reinterpret_cast<const float4 *>(eb + k0));
             c[4 * r] = cc.x; c[4 * r + 1] = cc.y; c[4 * r + 2] = cc.z; c[4 * r + 3] = cc.w;
         } else {
 #pragma unroll

@@ -42,6 +42,30 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
     return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
 }
 
+// ------------------------------------------------- streaming accesses
+// State that is read once and written once per call goes through nontemporal
+// loads and stores (the streaming cache policy): on this GPU a kernel with five
+// fp32 read streams and three write streams moves about 6% more bytes per second
+// with both than with neither (either alone gives 1-2%).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 ld_stream(const float4 *p) {
+    const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 ld_stream(const uint2 *p) {
+    const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ void st_stream(float4 *p, float4 v) {
+    const f32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t *>(p));
+}
+__device__ __forceinline__ void st_stream(uint2 *p, uint2 v) {
+    const u32x2_t t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t *>(p));
+}
+
 // --------------------------------------------------------- double-double
 // Error-free transformation a + b = s + err (Knuth's TwoSum); needs unfused fp64.
 struct DD {
