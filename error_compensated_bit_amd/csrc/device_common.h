@@ -46,7 +46,10 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
 // State that is read once and written once per call goes through nontemporal
 // loads and stores (the streaming cache policy): on this GPU a kernel with five
 // fp32 read streams and three write streams moves about 6% more bytes per second
-// with both than with neither (either alone gives 1-2%).
+// with both than with neither (either alone gives 1-2%).  Only where each access
+// instruction of a wave covers whole contiguous cache lines: where the lanes of
+// an instruction leave gaps (each thread owning 32 or 64 consecutive bytes and
+// writing them 16 bytes at a time), streaming stores are far slower.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float4 ld_stream(const float4 *p) {
@@ -56,6 +59,16 @@ __device__ __forceinline__ float4 ld_stream(const float4 *p) {
 __device__ __forceinline__ uint2 ld_stream(const uint2 *p) {
     const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
     return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ uint32_t ld_stream(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t *>(p));
 }
 __device__ __forceinline__ void st_stream(float4 *p, float4 v) {
     const f32x4_t t = {v.x, v.y, v.z, v.w};

@@ -4,12 +4,17 @@
 // frozen-variance step x -= lr * (m / (sqrt(v) + eps) + weight_decay * x).
 // Streaming; per element 12 bytes read and 4 written (x) without a mask, 13 read
 // and 8 written with one (the masked momentum is stored back), plus 2 written for
-// the optional bf16 copy of x.  Eight elements per thread and iteration: two
-// 128-bit accesses for each fp32 array, one 64-bit mask load, one 128-bit bf16 store.
+// the optional bf16 copy of x.  Per group of four elements: one 128-bit access for
+// each fp32 array, one 32-bit mask load, one 64-bit bf16 store.
 #include "device_common.h"
 #include "internal.h"
 
 namespace onebit {
+
+// Groups of four elements per thread and iteration; group h of the threads of a
+// workgroup covers 256 consecutive groups, so every access instruction of a wave
+// covers whole contiguous cache lines (which the streaming cache policy needs).
+constexpr int kUpdGroups = 2;
 
 struct UpdateArgs {
     float *m;
@@ -29,48 +34,49 @@ __device__ __forceinline__ float finish_one(const UpdateArgs &a, float &m, uint3
 
 template <bool MASK, bool XB>
 __global__ __launch_bounds__(256) void k_momentum_update(UpdateArgs a) {
-    const int64_t groups = a.n / 8;
-    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < groups;
-         q += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = 8 * q;
-        float4 m4[2], v4[2], x4[2];
-        uint2 mk = make_uint2(0xffffffffu, 0xffffffffu);
+    const int64_t groups = a.n / 4;
+    const int64_t span = (int64_t)blockDim.x * kUpdGroups;
+    for (int64_t base = blockIdx.x * span; base < groups; base += (int64_t)gridDim.x * span) {
+        float4 m4[kUpdGroups], v4[kUpdGroups], x4[kUpdGroups];
+        uint32_t mk[kUpdGroups];
+        bool in[kUpdGroups];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            m4[h] = *reinterpret_cast<const float4 *>(a.m + i + 4 * h);
-            v4[h] = *reinterpret_cast<const float4 *>(a.v + i + 4 * h);
-            x4[h] = *reinterpret_cast<const float4 *>(a.x + i + 4 * h);
-        }
-        if (MASK) mk = *reinterpret_cast<const uint2 *>(a.mask + i);
-        float xn[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t w = h ? mk.y : mk.x;
-            xn[4 * h + 0] = finish_one(a, m4[h].x, w & 0xffu, v4[h].x, x4[h].x);
-            xn[4 * h + 1] = finish_one(a, m4[h].y, (w >> 8) & 0xffu, v4[h].y, x4[h].y);
-            xn[4 * h + 2] = finish_one(a, m4[h].z, (w >> 16) & 0xffu, v4[h].z, x4[h].z);
-            xn[4 * h + 3] = finish_one(a, m4[h].w, w >> 24, v4[h].w, x4[h].w);
+        for (int h = 0; h < kUpdGroups; ++h) {
+            const int64_t q = base + h * (int64_t)blockDim.x + threadIdx.x;
+            in[h] = q < groups;
+            mk[h] = 0xffffffffu;
+            if (in[h]) {
+                m4[h] = ld_stream(reinterpret_cast<const float4 *>(a.m + 4 * q));
+                v4[h] = ld_stream(reinterpret_cast<const float4 *>(a.v + 4 * q));
+                x4[h] = ld_stream(reinterpret_cast<const float4 *>(a.x + 4 * q));
+                if (MASK) mk[h] = ld_stream(reinterpret_cast<const uint32_t *>(a.mask + 4 * q));
+            }
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (MASK) *reinterpret_cast<float4 *>(a.m + i + 4 * h) = m4[h];
-            *reinterpret_cast<float4 *>(a.x + i + 4 * h) =
-                make_float4(xn[4 * h], xn[4 * h + 1], xn[4 * h + 2], xn[4 * h + 3]);
-        }
-        if (XB) {
-            uint4 pk;
-            pk.x = float_to_bf16_bits(xn[0]) | (float_to_bf16_bits(xn[1]) << 16);
-            pk.y = float_to_bf16_bits(xn[2]) | (float_to_bf16_bits(xn[3]) << 16);
-            pk.z = float_to_bf16_bits(xn[4]) | (float_to_bf16_bits(xn[5]) << 16);
-            pk.w = float_to_bf16_bits(xn[6]) | (float_to_bf16_bits(xn[7]) << 16);
-            *reinterpret_cast<uint4 *>(a.xb + i) = pk;
+        for (int h = 0; h < kUpdGroups; ++h) {
+            if (!in[h]) continue;
+            const int64_t q = base + h * (int64_t)blockDim.x + threadIdx.x;
+            const uint32_t w = mk[h];
+            float xn[4];
+            xn[0] = finish_one(a, m4[h].x, w & 0xffu, v4[h].x, x4[h].x);
+            xn[1] = finish_one(a, m4[h].y, (w >> 8) & 0xffu, v4[h].y, x4[h].y);
+            xn[2] = finish_one(a, m4[h].z, (w >> 16) & 0xffu, v4[h].z, x4[h].z);
+            xn[3] = finish_one(a, m4[h].w, w >> 24, v4[h].w, x4[h].w);
+            if (MASK) st_stream(reinterpret_cast<float4 *>(a.m + 4 * q), m4[h]);
+            st_stream(reinterpret_cast<float4 *>(a.x + 4 * q), make_float4(xn[0], xn[1], xn[2], xn[3]));
+            if (XB) {
+                uint2 pk;
+                pk.x = float_to_bf16_bits(xn[0]) | (float_to_bf16_bits(xn[1]) << 16);
+                pk.y = float_to_bf16_bits(xn[2]) | (float_to_bf16_bits(xn[3]) << 16);
+                st_stream(reinterpret_cast<uint2 *>(a.xb + 4 * q), pk);
+            }
         }
     }
-    // ragged tail (n % 8 elements), one thread each
-    const int64_t tail = a.n - 8 * groups;
+    // ragged tail (n % 4 elements), one thread each
+    const int64_t tail = a.n - 4 * groups;
     const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (gid < tail) {
-        const int64_t i = 8 * groups + gid;
+        const int64_t i = 4 * groups + gid;
         float m = a.m[i];
         const float xn = finish_one(a, m, MASK ? a.mask[i] : 1u, a.v[i], a.x[i]);
         if (MASK) a.m[i] = m;
@@ -118,8 +124,8 @@ __global__ __launch_bounds__(256) void k_momentum_update_packed(PackedUpdateArgs
                 m4[q] = mul_rn(((nib >> q) & 1u) ? -s : s, keep ? 1.0f : 0.0f);
             }
             if (full) {
-                const float4 vv = *reinterpret_cast<const float4 *>(a.v + i0);
-                const float4 xx = *reinterpret_cast<const float4 *>(a.x + i0);
+                const float4 vv = ld_stream(reinterpret_cast<const float4 *>(a.v + i0));
+                const float4 xx = ld_stream(reinterpret_cast<const float4 *>(a.x + i0));
                 v4[0] = vv.x; v4[1] = vv.y; v4[2] = vv.z; v4[3] = vv.w;
                 x4[0] = xx.x; x4[1] = xx.y; x4[2] = xx.z; x4[3] = xx.w;
             } else {
@@ -136,12 +142,12 @@ __global__ __launch_bounds__(256) void k_momentum_update_packed(PackedUpdateArgs
                 xn[q] = sub_rn(x4[q], mul_rn(a.lr, upd));
             }
             if (full) {
-                *reinterpret_cast<float4 *>(a.x + i0) = make_float4(xn[0], xn[1], xn[2], xn[3]);
+                st_stream(reinterpret_cast<float4 *>(a.x + i0), make_float4(xn[0], xn[1], xn[2], xn[3]));
                 if (XB) {
                     uint2 pk;
                     pk.x = float_to_bf16_bits(xn[0]) | (float_to_bf16_bits(xn[1]) << 16);
                     pk.y = float_to_bf16_bits(xn[2]) | (float_to_bf16_bits(xn[3]) << 16);
-                    *reinterpret_cast<uint2 *>(a.xb + i0) = pk;
+                    st_stream(reinterpret_cast<uint2 *>(a.xb + i0), pk);
                 }
             } else {
 #pragma unroll
@@ -226,8 +232,8 @@ extern "C" onebit_status_t onebit_momentum_update(float *m, const uint8_t *mask,
         if (hipDeviceGetAttribute(&v_cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v_cus > 0)
             cus = v_cus;
     }
-    const int64_t groups = n / 8;
-    int64_t blocks = (groups + 255) / 256;
+    const int64_t groups = n / 4;
+    int64_t blocks = (groups + 256 * kUpdGroups - 1) / (256 * kUpdGroups);
     const int64_t cap = (int64_t)cus * 8;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;

@@ -31,13 +31,13 @@ __device__ __forceinline__ void warm_one(const WarmupArgs &a, float g, float &x,
 template <int GT>
 __device__ __forceinline__ void load_g4w(const void *g, int64_t i, float (&gg)[4]) {
     if (GT != kGradF32) {
-        const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + i);
+        const uint2 h = ld_stream(reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + i));
         gg[0] = half_bits_to_float<GT>(h.x & 0xffffu);
         gg[1] = half_bits_to_float<GT>(h.x >> 16);
         gg[2] = half_bits_to_float<GT>(h.y & 0xffffu);
         gg[3] = half_bits_to_float<GT>(h.y >> 16);
     } else {
-        const float4 h = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + i);
+        const float4 h = ld_stream(reinterpret_cast<const float4 *>(static_cast<const float *>(g) + i));
         gg[0] = h.x; gg[1] = h.y; gg[2] = h.z; gg[3] = h.w;
     }
 }
@@ -60,9 +60,9 @@ __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
             in[u] = q < groups;
             if (in[u]) {
                 load_g4w<GT>(a.g, 4 * q, gg[u]);
-                xx[u] = *reinterpret_cast<const float4 *>(a.x + 4 * q);
-                mm[u] = *reinterpret_cast<const float4 *>(a.m + 4 * q);
-                vv[u] = *reinterpret_cast<const float4 *>(a.v + 4 * q);
+                xx[u] = ld_stream(reinterpret_cast<const float4 *>(a.x + 4 * q));
+                mm[u] = ld_stream(reinterpret_cast<const float4 *>(a.m + 4 * q));
+                vv[u] = ld_stream(reinterpret_cast<const float4 *>(a.v + 4 * q));
             }
         }
 #pragma unroll
@@ -73,9 +73,9 @@ __global__ __launch_bounds__(256) void k_adam_warmup(WarmupArgs a) {
             warm_one<GT>(a, gg[u][1], xx[u].y, mm[u].y, vv[u].y);
             warm_one<GT>(a, gg[u][2], xx[u].z, mm[u].z, vv[u].z);
             warm_one<GT>(a, gg[u][3], xx[u].w, mm[u].w, vv[u].w);
-            *reinterpret_cast<float4 *>(a.x + 4 * q) = xx[u];
-            *reinterpret_cast<float4 *>(a.m + 4 * q) = mm[u];
-            *reinterpret_cast<float4 *>(a.v + 4 * q) = vv[u];
+            st_stream(reinterpret_cast<float4 *>(a.x + 4 * q), xx[u]);
+            st_stream(reinterpret_cast<float4 *>(a.m + 4 * q), mm[u]);
+            st_stream(reinterpret_cast<float4 *>(a.v + 4 * q), vv[u]);
         }
     }
     // ragged tail (n % 4 elements), one thread each

@@ -72,6 +72,10 @@ def load():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                               "(hipcc --offload-arch=gfx950); there is no fallback implementation")
+        # torch ships its own HIP runtime; loading it first makes the library bind to
+        # that same runtime (loaded the other way round, the process would hold two
+        # runtimes and the library's first HIP call would fail)
+        import torch  # noqa: F401
         lib = C.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(lib, name)

@@ -112,3 +112,27 @@ def test_forced_wait_timeouts_are_reported_and_recoverable():
     assert_exact("bits after re-initialization", host(bits).view(np.uint32), rb)
     assert check_scales("scales after re-initialization", host(sc), rs) == 0
     assert_exact("e after re-initialization", host(ed), er)
+
+
+def test_library_loaded_before_torch_shares_its_runtime():
+    """A fresh process that loads the library before it imports torch: the binding
+    brings torch's HIP runtime in first, so plan creation and a warmup step work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import numpy as np\n"
+            "from error_compensated_bit_amd import onebit as ob\n"
+            "ob.load()\n"
+            "p = ob.onebit_plan_create(np.array([0, 4096], np.int64))\n"
+            "import torch\n"
+            "z = torch.zeros(4096, device='cuda:0')\n"
+            "g = torch.ones(4096, device='cuda:0')\n"
+            "ob.onebit_adam_warmup_step(z, z.clone(), z.clone(), g, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,"
+            " weight_decay=0.0, bias_correction=True, step=1)\n"
+            "torch.cuda.synchronize()\n"
+            "assert abs(float(z[0]) + 1e-3) < 1e-6, float(z[0])\n"
+            "print('ok')\n")
+    say("library loaded before torch, fresh process")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
