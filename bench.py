@@ -670,7 +670,7 @@ def stream_ceiling(dev, n=335_544_320):
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     best = {}
     for name, ins, outs, bpe in (("5r3w", bufs[:5], bufs[5:], 32.0),):
-        for mult in (1, 2, 3, 6):
+        for mult in (1, 2, 3, 6, 16, 32):
             keep = ob.onebit_stream_probe(ins, outs, cus * mult)           # warm
             times = []
             for _ in range(4):

@@ -1,8 +1,9 @@
 // probe.hip -- a plain streaming kernel that measures what HBM delivers for a given
 // mix of fp32 read and write streams on this device (diagnostics: the compression
 // kernels are compared against it).  Each thread moves four 16-byte vectors of
-// every stream per iteration, grid-stride; out_k = sum of the inputs + k, so no
-// stream can be elided.
+// every stream per iteration, grid-stride, through the streaming cache policy the
+// compression kernels use; out_k = sum of the inputs + k, so no stream can be
+// elided.
 #include "device_common.h"
 #include "internal.h"
 
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(256) void k_stream_probe(const float4 *const *in, f
             for (int u = 0; u < kProbeU; ++u) {
                 const int64_t i = base + u * (int64_t)blockDim.x + threadIdx.x;
                 if (i < n4) {
-                    const float4 v = src[r][i];
+                    const float4 v = ld_stream(src[r] + i);
                     acc[u].x += v.x; acc[u].y += v.y; acc[u].z += v.z; acc[u].w += v.w;
                 }
             }
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void k_stream_probe(const float4 *const *in, f
             for (int u = 0; u < kProbeU; ++u) {
                 const int64_t i = base + u * (int64_t)blockDim.x + threadIdx.x;
                 const float k = (float)w;
-                if (i < n4) dst[w][i] = make_float4(acc[u].x + k, acc[u].y + k, acc[u].z + k, acc[u].w + k);
+                if (i < n4) st_stream(dst[w] + i, make_float4(acc[u].x + k, acc[u].y + k, acc[u].z + k, acc[u].w + k));
             }
         }
     }
