@@ -67,3 +67,52 @@ def test_server_ragged_chunks(Wn):
 def test_server_two_pass_chunk():
     off = W.offsets_from_sizes([max(ob.onebit_onepass_max_elements(), 1) + 4097, 5000])
     run_allreduce(off, 2, 2, seed=77)
+
+
+def _scale_cases(rng, Wn):
+    """Worker scales per chunk: a common exponent field (the exact integer sum applies),
+    mixed exponents, zeros, subnormals next to the smallest normals, a negative and a
+    negative-zero scale, very large scales."""
+    f32 = np.float32
+    cases = [
+        (2.0 ** -10 * rng.uniform(1, 2, Wn)).astype(f32),                      # one exponent
+        (2.0 ** -10 * rng.uniform(0.5, 2, Wn)).astype(f32),                    # mixed
+        np.where(rng.random(Wn) < 0.3, 0.0, 2.0 ** -7 * rng.uniform(1, 2, Wn)).astype(f32),
+        np.zeros(Wn, f32),
+        (rng.integers(1, 1 << 24, Wn) * 2.0 ** -149).astype(f32),              # subnormal and smallest normal binade
+        (2.0 ** 100 * rng.uniform(1, 2, Wn)).astype(f32),
+        (2.0 ** -3 * rng.uniform(1, 2, Wn)).astype(f32),
+        (2.0 ** -3 * rng.uniform(1, 2, Wn)).astype(f32),
+    ]
+    cases[6][Wn // 2] = -cases[6][Wn // 2]
+    cases[7][0] = -0.0
+    return cases
+
+
+@pytest.mark.parametrize("Wn", [1, 3, 16, 17])
+def test_server_scale_exponent_cases(Wn):
+    sizes = [4096, 2048 * 3 + 5, 31, 4096 + 64, 8192, 2053, 4096, 999]
+    off = W.offsets_from_sizes(sizes)
+    buf = CompressBuffers(off)
+    n, words, nch = buf.n, buf.words, buf.n_chunks
+    rng = np.random.default_rng(900 + Wn)
+    wb = rng.integers(0, 1 << 32, size=(Wn, words), dtype=np.uint64).astype(np.uint32)
+    sc = np.stack(_scale_cases(rng, Wn), axis=1)  # [Wn, nch]
+    assert sc.shape == (Wn, nch)
+    es = (rng.standard_normal(n) * 1e-5).astype(np.float32)
+    say(f"server scale cases W={Wn}")
+    wbd = torch.from_numpy(wb.view(np.int32).copy()).to(DEV)
+    scd = torch.from_numpy(sc.copy()).to(DEV)
+    esd = torch.from_numpy(es.copy()).to(DEV)
+    sbits = torch.zeros(words, dtype=torch.int32, device=DEV)
+    sscales = torch.zeros(nch, dtype=torch.float32, device=DEV)
+    md = torch.zeros(n, dtype=torch.float32, device=DEV)
+    for step in range(2):
+        ob.onebit_server_reduce(buf.plan, wbd, scd, esd, sbits, sscales, md, buf.ws)
+        rb, rs, m_out = oracle.server_reduce(off, wb, sc, es)
+        torch.cuda.synchronize()
+        assert_bits_exact(f"server bits step {step}", host(sbits).view(np.uint32), rb)
+        assert check_scales(f"server scales step {step}", host(sscales), rs) == 0
+        assert_exact(f"server e step {step}", host(esd), es)
+        assert_exact(f"server m step {step}", host(md), m_out)
+        assert ob.onebit_workspace_status(buf.ws) == 0
