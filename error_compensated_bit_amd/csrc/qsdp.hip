@@ -279,44 +279,37 @@ __global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
 // Buckets of 1024, kDeqBatch buckets per wave and iteration: the codes and bucket
 // bounds of all of them are loaded before any is decoded, so each wave keeps
 // several loads in flight while it writes (the stores outweigh the loads 4:1 or
-// 2:1 and need no wait).
+// 2:1 and need no wait).  A lane takes eight consecutive elements at 8*lane and
+// at 512 + 8*lane of the bucket, so every store instruction of a wave writes one
+// contiguous 1 KiB run of bf16 outputs (whole cache lines), with the streaming
+// cache policy.
 constexpr int kDeqBatch = 4;
+constexpr int kDeqWords = 2;  // code words per lane and half-bucket (4-bit uses one)
 
 template <int BITS>
-__device__ __forceinline__ void dequant16_store(const QArgs &a, int64_t base, int32_t len, int k0, float mn,
-                                               float delta, const uint32_t (&wv)[4]) {
-    uint32_t code[16];
-    if (BITS == 4) {
+__device__ __forceinline__ void dequant8_store(const QArgs &a, int64_t base, int32_t len, int k0, float mn,
+                                              float delta, const uint32_t (&wv)[kDeqWords]) {
+    uint32_t code[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            code[q] = (wv[0] >> (4 * q)) & 15u;
-            code[8 + q] = (wv[1] >> (4 * q)) & 15u;
-        }
-    } else {
+    for (int q = 0; q < 8; ++q)
+        code[q] = BITS == 4 ? (wv[0] >> (4 * q)) & 15u : (wv[q >> 2] >> (8 * (q & 3))) & 255u;
+    float y[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) code[q] = (wv[q >> 2] >> (8 * (q & 3))) & 255u;
-    }
-    float y[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) y[q] = add_rn(mn, mul_rn((float)code[q], delta));
+    for (int q = 0; q < 8; ++q) y[q] = add_rn(mn, mul_rn((float)code[q], delta));
     const int64_t i0 = base + k0;
-    if (k0 + 15 < len) {
+    if (k0 + 7 < len) {
         if (a.out_f32) {
             float4 *o = reinterpret_cast<float4 *>(a.out_f32 + i0);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) o[g] = make_float4(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]);
+            o[0] = make_float4(y[0], y[1], y[2], y[3]);
+            o[1] = make_float4(y[4], y[5], y[6], y[7]);
         }
         if (a.out_bf16) {
-            uint4 *o = reinterpret_cast<uint4 *>(a.out_bf16 + i0);
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                uint4 pk;
-                pk.x = float_to_bf16_bits(y[8 * g + 0]) | (float_to_bf16_bits(y[8 * g + 1]) << 16);
-                pk.y = float_to_bf16_bits(y[8 * g + 2]) | (float_to_bf16_bits(y[8 * g + 3]) << 16);
-                pk.z = float_to_bf16_bits(y[8 * g + 4]) | (float_to_bf16_bits(y[8 * g + 5]) << 16);
-                pk.w = float_to_bf16_bits(y[8 * g + 6]) | (float_to_bf16_bits(y[8 * g + 7]) << 16);
-                o[g] = pk;
-            }
+            uint4 pk;
+            pk.x = float_to_bf16_bits(y[0]) | (float_to_bf16_bits(y[1]) << 16);
+            pk.y = float_to_bf16_bits(y[2]) | (float_to_bf16_bits(y[3]) << 16);
+            pk.z = float_to_bf16_bits(y[4]) | (float_to_bf16_bits(y[5]) << 16);
+            pk.w = float_to_bf16_bits(y[6]) | (float_to_bf16_bits(y[7]) << 16);
+            st_stream(reinterpret_cast<uint4 *>(a.out_bf16 + i0), pk);
         }
     } else {
         for (int q = 0; q < len - k0; ++q) {
@@ -332,36 +325,39 @@ __global__ __launch_bounds__(256) void k_qsdp_dequantize_1024(QArgs a) {
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     constexpr float L = (float)((1 << BITS) - 1);
-    const int k0 = 16 * lane;
     for (int64_t b0 = wave * kDeqBatch; b0 < a.n_buckets; b0 += nwaves * kDeqBatch) {
-        uint32_t wv[kDeqBatch][4];
+        uint32_t wv[kDeqBatch][2][kDeqWords];
         float mn[kDeqBatch], mx[kDeqBatch];
 #pragma unroll
         for (int u = 0; u < kDeqBatch; ++u) {
             const int64_t b = b0 + u;
-            wv[u][0] = wv[u][1] = wv[u][2] = wv[u][3] = 0u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) wv[u][h][0] = wv[u][h][1] = 0u;
             mn[u] = mx[u] = 0.0f;
             if (b < a.n_buckets) {
                 const int64_t base = b * 1024;
                 const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
                 mn[u] = a.in_min[b];
                 mx[u] = a.in_max[b];
-                if (k0 + 15 < len) {
-                    if (BITS == 4) {
-                        const uint2 w = *reinterpret_cast<const uint2 *>(a.in_codes + ((base + k0) >> 1));
-                        wv[u][0] = w.x;
-                        wv[u][1] = w.y;
-                    } else {
-                        const uint4 w = *reinterpret_cast<const uint4 *>(a.in_codes + base + k0);
-                        wv[u][0] = w.x; wv[u][1] = w.y; wv[u][2] = w.z; wv[u][3] = w.w;
-                    }
-                } else if (k0 < len) {
-                    if (BITS == 4) {
-                        const uint8_t *src = a.in_codes + ((base + k0) >> 1);
-                        for (int q = 0; 2 * q < len - k0; ++q) wv[u][q >> 2] |= (uint32_t)src[q] << (8 * (q & 3));
-                    } else {
-                        const uint8_t *src = a.in_codes + base + k0;
-                        for (int q = 0; q < len - k0; ++q) wv[u][q >> 2] |= (uint32_t)src[q] << (8 * (q & 3));
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k0 = 8 * lane + 512 * h;
+                    if (k0 + 7 < len) {
+                        if (BITS == 4) {
+                            wv[u][h][0] = *reinterpret_cast<const uint32_t *>(a.in_codes + ((base + k0) >> 1));
+                        } else {
+                            const uint2 w = *reinterpret_cast<const uint2 *>(a.in_codes + base + k0);
+                            wv[u][h][0] = w.x;
+                            wv[u][h][1] = w.y;
+                        }
+                    } else if (k0 < len) {
+                        if (BITS == 4) {
+                            const uint8_t *src = a.in_codes + ((base + k0) >> 1);
+                            for (int q = 0; 2 * q < len - k0; ++q) wv[u][h][0] |= (uint32_t)src[q] << (8 * q);
+                        } else {
+                            const uint8_t *src = a.in_codes + base + k0;
+                            for (int q = 0; q < len - k0; ++q) wv[u][h][q >> 2] |= (uint32_t)src[q] << (8 * (q & 3));
+                        }
                     }
                 }
             }
@@ -372,9 +368,12 @@ __global__ __launch_bounds__(256) void k_qsdp_dequantize_1024(QArgs a) {
             if (b >= a.n_buckets) break;
             const int64_t base = b * 1024;
             const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
-            if (k0 >= len) continue;
             const float delta = __fdiv_rn(sub_rn(mx[u], mn[u]), L);
-            dequant16_store<BITS>(a, base, len, k0, mn[u], delta, wv[u]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k0 = 8 * lane + 512 * h;
+                if (k0 < len) dequant8_store<BITS>(a, base, len, k0, mn[u], delta, wv[u][h]);
+            }
         }
     }
 }
