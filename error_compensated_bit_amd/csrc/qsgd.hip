@@ -297,22 +297,30 @@ __device__ __forceinline__ void store_out(const RArgs &a, int64_t i, float y) {
 // E = 16 consecutive elements per thread and iteration: one 8-byte (4-bit codes) or
 // 16-byte (8-bit) load of every worker's row, 16 fp64 sums live per thread.  With
 // the bucket a multiple of E the E elements share one norm (one level spacing) per
-// worker.  Sum over workers in fp64, in worker order.
+// worker.  Sum over workers in fp64, in worker order.  The results of a wave (1024
+// consecutive elements) pass through LDS so that every store instruction writes one
+// contiguous run (1 KiB of fp32 or bf16), with the streaming cache policy; the waves
+// step through the vector together, so every lane takes part in the exchange.
 constexpr int kBatch = 4;
 
 template <int BITS, bool SHARED_NORM, bool POW2>
 __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
     constexpr int E = kReduceE;
     constexpr int NW = BITS / 2;   // 32-bit words per load
+    __shared__ float4 s_out[4][64 * E / 4];
+    float4 *const sw = s_out[threadIdx.x >> 6];
+    const int lane = threadIdx.x & 63;
     const int64_t groups = a.n / E;
     const double Wd = (double)a.W;
-    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < groups;
-         q += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t q0 = blockIdx.x * (int64_t)blockDim.x + (threadIdx.x & ~63); q0 < groups;
+         q0 += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t q = q0 + lane;
         const int64_t i0 = E * q;
         double acc[E];
 #pragma unroll
         for (int k = 0; k < E; ++k) acc[k] = 0.0;
         const int64_t b0 = i0 / a.bucket;
+        if (q < groups) {
         // workers in batches of kBatch: every load of a batch is issued before its
         // words are decoded, so each thread keeps kBatch 16-byte loads in flight
         for (int w0 = 0; w0 < a.W; w0 += kBatch) {
@@ -355,16 +363,24 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
                 Accumulate16<BITS>::run(acc, ws, sk);
             }
         }
+        }
         float y[E];
 #pragma unroll
         for (int k = 0; k < E; ++k) y[k] = mean_of<POW2>(acc[k], Wd, a.invW);
+        // store h of a lane covers the wave's elements 4 (64 h + lane) .. +3 (fp32) or
+        // 8 (64 h + lane) .. +7 (bf16), computed by lane 16 h + lane / 4 or 32 h + lane / 2
         if (a.out_f32) {
-            float4 *o = reinterpret_cast<float4 *>(a.out_f32 + i0);
 #pragma unroll
-            for (int h = 0; h < E / 4; ++h) o[h] = make_float4(y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]);
+            for (int h = 0; h < E / 4; ++h) sw[4 * lane + h] = make_float4(y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]);
+            __builtin_amdgcn_wave_barrier();
+            float4 *o = reinterpret_cast<float4 *>(a.out_f32 + E * q0);
+#pragma unroll
+            for (int h = 0; h < E / 4; ++h)
+                if (q0 + 16 * h + (lane >> 2) < groups) st_stream(o + 64 * h + lane, sw[64 * h + lane]);
+            __builtin_amdgcn_wave_barrier();
         }
         if (a.out_bf16) {
-            uint4 *o = reinterpret_cast<uint4 *>(a.out_bf16 + i0);
+            uint4 *su = reinterpret_cast<uint4 *>(sw);
 #pragma unroll
             for (int h = 0; h < E / 8; ++h) {
                 uint4 pk;
@@ -372,8 +388,14 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
                 pk.y = float_to_bf16_bits(y[8 * h + 2]) | (float_to_bf16_bits(y[8 * h + 3]) << 16);
                 pk.z = float_to_bf16_bits(y[8 * h + 4]) | (float_to_bf16_bits(y[8 * h + 5]) << 16);
                 pk.w = float_to_bf16_bits(y[8 * h + 6]) | (float_to_bf16_bits(y[8 * h + 7]) << 16);
-                o[h] = pk;
+                su[2 * lane + h] = pk;
             }
+            __builtin_amdgcn_wave_barrier();
+            uint4 *o = reinterpret_cast<uint4 *>(a.out_bf16 + E * q0);
+#pragma unroll
+            for (int h = 0; h < E / 8; ++h)
+                if (q0 + 32 * h + (lane >> 1) < groups) st_stream(o + 64 * h + lane, su[64 * h + lane]);
+            __builtin_amdgcn_wave_barrier();
         }
     }
     // ragged tail (n % E elements), one thread each
