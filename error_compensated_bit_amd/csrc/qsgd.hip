@@ -70,19 +70,76 @@ __device__ __forceinline__ float norm_of(DD acc) {
 }
 
 // Buckets of 1024: one wave per bucket, lane l owns the 16 consecutive elements
-// 16l..16l+15 (two or four 16-byte loads), kept in registers between the norm and
-// the codes; four Philox calls per lane; one 8- or 16-byte store of codes.
+// 16l..16l+15, kept in registers between the norm and the codes; four Philox calls
+// per lane; one 8- or 16-byte store of codes.  In whole buckets the gradient (and
+// LoCo's error average, both ways) moves between HBM and the lanes through LDS:
+// every load or store instruction of the wave covers one contiguous 1 KiB run
+// (streaming cache policy), and each lane then reads its own 16 elements.
 template <int BITS, int GT, bool LOCO>
 __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
+    __shared__ float4 s_g[4][256];
+    __shared__ float4 s_e[4][LOCO ? 256 : 1];
+    float4 *const wg = s_g[threadIdx.x >> 6];
+    float4 *const we = s_e[threadIdx.x >> 6];
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
         const int64_t base = b * 1024;
         const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
+        const bool whole = len == 1024;  // uniform over the wave
         const int k0 = 16 * lane;
         float f[16];
-        if (k0 + 15 < len) {
+        float ea[LOCO ? 16 : 1];
+        if (whole) {
+            if (GT == kGradF32) {
+                const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + base);
+                float4 v[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) v[h] = ld_stream(src + 64 * h + lane);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) wg[64 * h + lane] = v[h];
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float4 t = wg[4 * lane + h];
+                    f[4 * h] = t.x; f[4 * h + 1] = t.y; f[4 * h + 2] = t.z; f[4 * h + 3] = t.w;
+                }
+            } else {
+                const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.g) + base);
+                uint4 *wu = reinterpret_cast<uint4 *>(wg);
+                uint4 v[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) v[h] = ld_stream(src + 64 * h + lane);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) wu[64 * h + lane] = v[h];
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 t = wu[2 * lane + h];
+                    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f[8 * h + 2 * q] = half_bits_to_float<GT>(w[q] & 0xffffu);
+                        f[8 * h + 2 * q + 1] = half_bits_to_float<GT>(w[q] >> 16);
+                    }
+                }
+            }
+            if (LOCO) {
+                const float4 *src = reinterpret_cast<const float4 *>(a.err + base);
+                float4 v[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) v[h] = ld_stream(src + 64 * h + lane);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) we[64 * h + lane] = v[h];
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float4 t = we[4 * lane + h];
+                    ea[4 * h] = t.x; ea[4 * h + 1] = t.y; ea[4 * h + 2] = t.z; ea[4 * h + 3] = t.w;
+                }
+            }
+        } else if (k0 + 15 < len) {
             if (GT == kGradF32) {
                 const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + base + k0);
 #pragma unroll
@@ -107,8 +164,7 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) f[q] = (k0 + q < len) ? load_grad<GT>(a.g, base + k0 + q) : 0.0f;
         }
-        float ea[LOCO ? 16 : 1];
-        if (LOCO) {
+        if (LOCO && !whole) {
             if (k0 + 15 < len) {
                 const float4 *src = reinterpret_cast<const float4 *>(a.err + base + k0);
 #pragma unroll
@@ -120,6 +176,8 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) ea[q] = (k0 + q < len) ? a.err[base + k0 + q] : 0.0f;
             }
+        }
+        if (LOCO) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) f[q] = add_rn(f[q], ea[q]);     // compensated gradient h
         }
@@ -146,7 +204,15 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
             const float st = __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
 #pragma unroll
             for (int q = 0; q < 16; ++q) ea[q] = loco_update<BITS>(a, ea[q], f[q], code[q], st);
-            if (k0 + 15 < len) {
+            if (whole) {
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int h = 0; h < 4; ++h) we[4 * lane + h] = make_float4(ea[4 * h], ea[4 * h + 1], ea[4 * h + 2], ea[4 * h + 3]);
+                __builtin_amdgcn_wave_barrier();
+                float4 *dst = reinterpret_cast<float4 *>(a.err + base);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) st_stream(dst + 64 * h + lane, we[64 * h + lane]);
+            } else if (k0 + 15 < len) {
                 float4 *dst = reinterpret_cast<float4 *>(a.err + base + k0);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) dst[h] = make_float4(ea[4 * h], ea[4 * h + 1], ea[4 * h + 2], ea[4 * h + 3]);
