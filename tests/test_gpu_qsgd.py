@@ -119,8 +119,10 @@ def test_extreme_exponents(bucket, bits):
 
 @pytest.mark.parametrize("workers", [1, 2, 3, 8])
 @pytest.mark.parametrize("bucket,bits", [(1024, 4), (1000, 8), (30, 4), (2, 8), (4096, 4)])
-def test_reduce_parity(workers, bucket, bits):
-    n = 3 * 4096 + 13
+@pytest.mark.parametrize("n", [3 * 4096 + 13, 16 * 1000 + 7, 16 * 63 + 5])
+def test_reduce_parity(workers, bucket, bits, n):
+    """n: whole waves of 64 x 16 elements plus a ragged tail, then a partly filled
+    last wave (1000 and 63 groups of 16) plus a tail."""
     nb = (n + bucket - 1) // bucket
     stride = (code_bytes(n, bits) + 15) // 16 * 16 + 32      # padded worker rows
     codes = torch.zeros((workers, stride), dtype=torch.uint8, device=DEV)
@@ -138,7 +140,7 @@ def test_reduce_parity(workers, bucket, bits):
     ob.qsgd_reduce(codes, norms, n, bucket, bits, out_f32=y, out_bf16=yb)
     ry, ryb = oracle.qsgd_reduce(np.stack(rcs), np.stack(rns), n, bucket=bucket, bits=bits, want_bf16=True)
     torch.cuda.synchronize()
-    tag = f"W={workers} bucket {bucket} bits {bits}"
+    tag = f"W={workers} bucket {bucket} bits {bits} n {n}"
     assert_exact(f"{tag} codes", host(codes), np.stack(rcs))
     assert_exact(f"{tag} mean", host(y), ry)
     check_bf16(f"{tag} mean bf16", host(yb), ryb)
