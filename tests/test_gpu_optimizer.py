@@ -1,0 +1,100 @@
+"""GPU parity of the 1-bit Adam driver (error_compensated_bit_amd.optimizer) against the
+oracle run through the same phases: full-precision warmup up to freeze_step, then
+compressed steps with v frozen; a checkpoint reload in the compressed phase (m, v and
+the step kept, the error restarted from zero); masked tensors pinned at zero."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from error_compensated_bit_amd import workloads as W
+from error_compensated_bit_amd.optimizer import OneBitAdam
+from gpu_helpers import DEV, host
+from parity import assert_bits_exact, assert_exact, check_scales, check_x, say
+
+pytestmark = pytest.mark.gpu
+
+
+class OracleAdam:
+    """The oracle driven through the same phases on host arrays."""
+
+    def __init__(self, x, chunk_off, tensor_off, tensor_keep, hp, freeze_step):
+        self.x, self.m, self.v, self.e = x.copy(), np.zeros_like(x), np.zeros_like(x), np.zeros_like(x)
+        self.off, self.to, self.tk, self.hp, self.freeze = chunk_off, tensor_off, tensor_keep, hp, freeze_step
+        self.t = 0
+        self.bits = self.scales = None
+
+    def step(self, g):
+        self.t += 1
+        hp = self.hp
+        if self.t <= self.freeze:
+            oracle.adam_warmup_step(self.x, self.m, self.v, g, lr=hp["lr"], beta1=hp["beta1"], beta2=hp["beta2"],
+                                    eps=hp["eps"], weight_decay=hp["weight_decay"],
+                                    bias_correction=hp["bias_correction"], step=self.t)
+        else:
+            self.bits, self.scales, _ = oracle.compress_update(
+                self.off, g, self.m, self.e, self.v, self.x, tensor_off=self.to, tensor_keep=self.tk, lr=hp["lr"],
+                beta1=hp["beta1"], eps=hp["eps"], weight_decay=hp["weight_decay"])
+
+
+def check(tag, o, r, x_prev):
+    torch.cuda.synchronize()
+    say(f"  {tag}")
+    assert_exact(f"{tag} m", host(o.m), r.m)
+    assert_exact(f"{tag} v", host(o.v), r.v)
+    check_x(f"{tag} x", host(o.x), r.x, x_prev)
+    if r.bits is not None and o.frozen:
+        assert_bits_exact(f"{tag} bits", host(o.bits)[:r.bits.size].view(np.uint32), r.bits)
+        assert check_scales(f"{tag} scales", host(o.scales)[:r.scales.size], r.scales) == 0
+        assert_exact(f"{tag} e", host(o.e), r.e)
+
+
+@pytest.mark.parametrize("bias_correction", [False, True])
+def test_tiny_workload_through_the_driver(bias_correction):
+    """1,048,576 params, one chunk: 5 warmup steps, then compressed steps; at step 7 a
+    checkpoint is saved and loaded into a fresh driver, which continues to step 10."""
+    wl = W.tiny()
+    hp = dict(W.HYPER, bias_correction=bias_correction)
+    x0 = W.init_state(wl)[0].numpy().copy()
+    o = OneBitAdam(torch.from_numpy(x0.copy()).to(DEV), lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]),
+                   eps=hp["eps"], weight_decay=hp["weight_decay"], bias_correction=bias_correction, freeze_step=5)
+    r = OracleAdam(x0, wl.chunk_off, None, None, hp, 5)
+    for t in range(1, 11):
+        g = W.gradient(wl, t).numpy()
+        x_prev = r.x.copy()
+        o.step(torch.from_numpy(g).to(DEV))
+        r.step(g)
+        check(f"bias_correction={bias_correction} step {t}", o, r, x_prev)
+        if t == 7:
+            sd = o.state_dict()
+            o = OneBitAdam(o.x, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                           weight_decay=hp["weight_decay"], bias_correction=bias_correction, freeze_step=5)
+            o.e.fill_(1.0)
+            o.load_state_dict(sd)
+            r.e[:] = 0.0
+            assert o.frozen and torch.count_nonzero(o.e) == 0
+
+
+def test_masked_tensors_through_the_driver():
+    sizes = [1000, 2000, 1099, 4096 + 3]
+    to = W.offsets_from_sizes(sizes)
+    keep = np.array([1, 0, 1, 0], np.uint8)
+    n = int(to[-1])
+    rng = np.random.default_rng(11)
+    x0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hp = dict(W.HYPER)
+    o = OneBitAdam(torch.from_numpy(x0.copy()).to(DEV), tensor_offsets=to, tensor_keep=keep, lr=hp["lr"],
+                   betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=0.0,
+                   bias_correction=hp["bias_correction"], freeze_step=2)
+    r = OracleAdam(x0, to, to, keep, dict(hp, weight_decay=0.0), 2)
+    masked = np.repeat(keep == 0, np.diff(to))
+    for t in range(1, 6):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        g[masked] = 0.0
+        x_prev = r.x.copy()
+        o.step(torch.from_numpy(g).to(DEV))
+        r.step(g)
+        check(f"masked tensors step {t}", o, r, x_prev)
+        if t > 2:
+            assert np.all(host(o.m)[masked] == 0) and np.all(host(o.e)[masked] == 0)
+            assert np.array_equal(host(o.x)[masked], x_prev[masked])

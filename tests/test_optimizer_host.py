@@ -1,0 +1,88 @@
+"""Host logic of the 1-bit Adam driver (no GPU): which library call each step makes,
+the freeze boundary, the step numbers handed to the warmup, and the error reset on
+checkpoint load.  The library calls are replaced by recorders; the tensors are CPU
+tensors that no kernel touches."""
+import numpy as np
+import pytest
+import torch
+
+from error_compensated_bit_amd import onebit as ob
+from error_compensated_bit_amd import optimizer as opt
+
+
+@pytest.fixture
+def calls(monkeypatch):
+    log = []
+    monkeypatch.setattr(ob, "onebit_plan_create", lambda co, to=None, tk=None: ("plan", np.asarray(co).tolist()))
+    monkeypatch.setattr(ob, "onebit_plan_words", lambda p: 3)
+    monkeypatch.setattr(ob, "onebit_plan_chunks", lambda p: 2)
+    monkeypatch.setattr(ob, "onebit_plan_workspace_bytes", lambda p: 64)
+
+    def warm(x, m, v, g, **k):
+        log.append(("warmup", k["step"], k["bias_correction"], k["beta2"]))
+
+    def comp(plan, g, m, e, v, x, xb, bits, scales, **k):
+        assert e is not None and v is not None and x is not None and xb is None
+        log.append(("compress", plan[1], k["beta1"], k["lr"]))
+
+    monkeypatch.setattr(ob, "onebit_adam_warmup_step", warm)
+    monkeypatch.setattr(ob, "onebit_compress_update", comp)
+    return log
+
+
+def test_warmup_then_compressed_steps(calls):
+    x = torch.zeros(10)
+    o = opt.OneBitAdam(x, chunk_offsets=[0, 4, 10], lr=2e-3, betas=(0.8, 0.99), freeze_step=3,
+                       bias_correction=False)
+    assert not o.frozen
+    for _ in range(5):
+        o.step(torch.zeros(10))
+    assert o.frozen and o.step_count == 5
+    assert calls == [("warmup", 1, False, 0.99), ("warmup", 2, False, 0.99), ("warmup", 3, False, 0.99),
+                     ("compress", [0, 4, 10], 0.8, 2e-3), ("compress", [0, 4, 10], 0.8, 2e-3)]
+    assert o.bits.numel() == 3 and o.scales.numel() == 2 and o.workspace.numel() == 8
+
+
+def test_default_chunks_follow_tensors_then_whole_vector(calls):
+    o = opt.OneBitAdam(torch.zeros(6), tensor_offsets=[0, 2, 6], tensor_keep=[1, 0], freeze_step=0)
+    o.step(torch.zeros(6))
+    assert calls == [("compress", [0, 2, 6], 0.9, 1e-3)]
+    calls.clear()
+    o = opt.OneBitAdam(torch.zeros(6), freeze_step=0)
+    o.step(torch.zeros(6))
+    assert calls == [("compress", [0, 6], 0.9, 1e-3)]
+
+
+def test_checkpoint_keeps_moments_and_resets_error(calls):
+    o = opt.OneBitAdam(torch.zeros(4), freeze_step=2)
+    for _ in range(3):
+        o.step(torch.zeros(4))
+    o.m.fill_(1.0)
+    o.v.fill_(2.0)
+    o.e.fill_(3.0)
+    sd = o.state_dict()
+    assert set(sd) == {"step", "exp_avg", "exp_avg_sq"} and sd["step"] == 3
+    p = opt.OneBitAdam(torch.zeros(4), freeze_step=2)
+    p.e.fill_(5.0)
+    p.load_state_dict(sd)
+    assert p.step_count == 3 and p.frozen
+    assert torch.equal(p.m, torch.ones(4)) and torch.equal(p.v, torch.full((4,), 2.0))
+    assert torch.equal(p.e, torch.zeros(4))
+    calls.clear()
+    p.step(torch.zeros(4))
+    assert calls[0][0] == "compress"
+
+
+def test_rejects_bad_arguments(calls):
+    with pytest.raises(TypeError):
+        opt.OneBitAdam(torch.zeros(4, dtype=torch.float64))
+    with pytest.raises(TypeError):
+        opt.OneBitAdam(torch.zeros(2, 2))
+    with pytest.raises(ValueError):
+        opt.OneBitAdam(torch.zeros(4), chunk_offsets=[0, 3])
+    with pytest.raises(ValueError):
+        opt.OneBitAdam(torch.zeros(4), freeze_step=-1)
+    o = opt.OneBitAdam(torch.zeros(4))
+    with pytest.raises(ValueError):
+        o.step(torch.zeros(5))
+    assert calls == []
