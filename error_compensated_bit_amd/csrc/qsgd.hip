@@ -387,48 +387,48 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
         for (int k = 0; k < E; ++k) acc[k] = 0.0;
         const int64_t b0 = i0 / a.bucket;
         if (q < groups) {
-        // workers in batches of kBatch: every load of a batch is issued before its
-        // words are decoded, so each thread keeps kBatch 16-byte loads in flight
-        for (int w0 = 0; w0 < a.W; w0 += kBatch) {
-            uint32_t word[kBatch][NW];
-            float nm[kBatch];
+            // workers in batches of kBatch: every load of a batch is issued before its
+            // words are decoded, so each thread keeps kBatch 16-byte loads in flight
+            for (int w0 = 0; w0 < a.W; w0 += kBatch) {
+                uint32_t word[kBatch][NW];
+                float nm[kBatch];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (w0 + j < a.W) {
-                    const uint8_t *src = a.codes + (int64_t)(w0 + j) * a.code_stride + (int64_t)(E * BITS / 8) * q;
-                    if (BITS == 4) {
-                        const uint2 v = *reinterpret_cast<const uint2 *>(src);
-                        word[j][0] = v.x;
-                        word[j][NW > 1 ? 1 : 0] = v.y;
-                    } else {
-                        const uint4 v = *reinterpret_cast<const uint4 *>(src);
-                        word[j][0] = v.x;
-                        word[j][NW > 1 ? 1 : 0] = v.y;
-                        word[j][NW > 2 ? 2 : 0] = v.z;
-                        word[j][NW > 3 ? 3 : 0] = v.w;
+                for (int j = 0; j < kBatch; ++j) {
+                    if (w0 + j < a.W) {
+                        const uint8_t *src = a.codes + (int64_t)(w0 + j) * a.code_stride + (int64_t)(E * BITS / 8) * q;
+                        if (BITS == 4) {
+                            const uint2 v = *reinterpret_cast<const uint2 *>(src);
+                            word[j][0] = v.x;
+                            word[j][NW > 1 ? 1 : 0] = v.y;
+                        } else {
+                            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                            word[j][0] = v.x;
+                            word[j][NW > 1 ? 1 : 0] = v.y;
+                            word[j][NW > 2 ? 2 : 0] = v.z;
+                            word[j][NW > 3 ? 3 : 0] = v.w;
+                        }
+                        nm[j] = SHARED_NORM ? a.norms[(int64_t)(w0 + j) * a.norm_stride + b0] : 0.0f;
                     }
-                    nm[j] = SHARED_NORM ? a.norms[(int64_t)(w0 + j) * a.norm_stride + b0] : 0.0f;
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    if (w0 + j >= a.W) break;
+                    uint32_t ws[NW];
+#pragma unroll
+                    for (int h = 0; h < NW; ++h) ws[h] = word[j][h];
+                    double sk[E];
+                    if (SHARED_NORM) {
+                        const double st = (double)level_step<BITS>(nm[j]);
+#pragma unroll
+                        for (int k = 0; k < E; ++k) sk[k] = st;
+                    } else {
+                        const float *nrow = a.norms + (int64_t)(w0 + j) * a.norm_stride;
+#pragma unroll
+                        for (int k = 0; k < E; ++k) sk[k] = (double)level_step<BITS>(nrow[(i0 + k) / a.bucket]);
+                    }
+                    Accumulate16<BITS>::run(acc, ws, sk);
                 }
             }
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (w0 + j >= a.W) break;
-                uint32_t ws[NW];
-#pragma unroll
-                for (int h = 0; h < NW; ++h) ws[h] = word[j][h];
-                double sk[E];
-                if (SHARED_NORM) {
-                    const double st = (double)level_step<BITS>(nm[j]);
-#pragma unroll
-                    for (int k = 0; k < E; ++k) sk[k] = st;
-                } else {
-                    const float *nrow = a.norms + (int64_t)(w0 + j) * a.norm_stride;
-#pragma unroll
-                    for (int k = 0; k < E; ++k) sk[k] = (double)level_step<BITS>(nrow[(i0 + k) / a.bucket]);
-                }
-                Accumulate16<BITS>::run(acc, ws, sk);
-            }
-        }
         }
         float y[E];
 #pragma unroll
