@@ -167,9 +167,10 @@ __device__ __forceinline__ U4 philox4x32_10(U4 ctr, uint32_t k0, uint32_t k1) {
         const uint64_t p = (uint64_t)ctr.a * 0xD2511F53u;
         const uint64_t q = (uint64_t)ctr.c * 0xCD9E8D57u;
         U4 nx;
-        nx.a = (uint32_t)(q >> 32) ^ ctr.b ^ k0;
+        // three-input xors as one v_bitop3_b32 each (truth table 0x96 = odd parity)
+        nx.a = __builtin_amdgcn_bitop3_b32((uint32_t)(q >> 32), ctr.b, k0, 0x96);
         nx.b = (uint32_t)q;
-        nx.c = (uint32_t)(p >> 32) ^ ctr.d ^ k1;
+        nx.c = __builtin_amdgcn_bitop3_b32((uint32_t)(p >> 32), ctr.d, k1, 0x96);
         nx.d = (uint32_t)p;
         ctr = nx;
         k0 += 0x9E3779B9u;
