@@ -273,6 +273,33 @@ def test_repeat_is_bit_identical_and_workspace_shared_across_plans():
             assert_exact("repeat", a, b)
 
 
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+def test_warmup_kernel_several_grid_passes(gdt):
+    """13 * 2^20 + 5 elements: more than one pass of the grid-stride loop (at most
+    six workgroups per CU x 4096 elements each per pass), plus a ragged tail."""
+    n = (13 << 20) + 5
+    rng = np.random.default_rng(5)
+    x, m, _, v = rand_state(n, rng)
+    xd, md, vd = (torch.from_numpy(a.copy()).to(DEV) for a in (x, m, v))
+    for t in range(1, 3):
+        g32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        gt = torch.from_numpy(g32).to(DEV)
+        if gdt == "bf16":
+            gt = gt.to(torch.bfloat16)
+            g = host(gt)
+        else:
+            g = g32
+        hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, bias_correction=True, step=t)
+        say(f"warmup n={n} {gdt} step {t}")
+        x_prev = x.copy()
+        ob.onebit_adam_warmup_step(xd, md, vd, gt, **hp)
+        oracle.adam_warmup_step(x, m, v, g, **hp)
+        torch.cuda.synchronize()
+        assert_exact(f"n={n} m", host(md), m)
+        assert_exact(f"n={n} v", host(vd), v)
+        check_x(f"n={n} x", host(xd), x, x_prev)
+
+
 def test_warmup_kernel_edge_sizes():
     for n in (1, 3, 4, 5, 4099, (1 << 20) + 3):
         for gdt in ("f32", "bf16", "f16"):

@@ -31,7 +31,7 @@ def rand_state(n, rng):
     return m, v, x
 
 
-@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4099, (1 << 20) + 3])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4099, (1 << 20) + 3, (9 << 20) + 5])  # the last: several grid passes
 @pytest.mark.parametrize("with_mask,x_bf16", [(False, False), (True, False), (False, True), (True, True)])
 def test_momentum_update_parity(n, with_mask, x_bf16):
     rng = np.random.default_rng(n + 17)
