@@ -170,7 +170,8 @@ __device__ __forceinline__ void unpack8(uint4 h, float (&f)[8]) {
 }
 
 template <int BITS>
-__global__ __launch_bounds__(256) void k_qsdp_quantize_1024(QArgs a) {
+// six waves per SIMD (at most 80 VGPRs): the 4-bit variant otherwise takes 82 and runs five
+__global__ __launch_bounds__(256, 6) void k_qsdp_quantize_1024(QArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
