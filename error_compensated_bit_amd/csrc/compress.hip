@@ -375,6 +375,12 @@ __device__ __forceinline__ float scale_of(double S, int64_t len) {
     return len > 0 ? (float)__ddiv_rn(__dsqrt_rn(S), __dsqrt_rn((double)len)) : 0.0f;
 }
 
+// Slot loads in flight per thread when a tile of the one-pass kernel finalizes its
+// chunk.  This path is inlined into every tile, so its registers count for the
+// whole kernel: with 8 (16 VGPRs of slot words) it set the kernel's peak, and
+// the update and packed-momentum variants spilled; with 4 they do not.
+constexpr int kFinalizeBatch = 4;
+
 // What a workgroup knows about a tile it has posted.
 struct Posted {
     uint32_t epoch;  // publish epoch of the chunk read before posting
@@ -404,7 +410,7 @@ __device__ Posted post_tile(const CompressArgs &a, int tile_id, int chunk, doubl
         const ChunkDesc ch = a.chunks[chunk];
         if (tile_id == ch.first_tile + ch.ntiles - 1) {
             r.mine = 1u;
-            r.scale = scale_of(chunk_sum(a, ch, s_red, s_total), ch.len);
+            r.scale = scale_of(chunk_sum<kBlock, kFinalizeBatch>(a, ch, s_red, s_total), ch.len);
             if (threadIdx.x == 0) {
                 a.scales[chunk] = r.scale;
                 st_agent(a.publish + chunk,
