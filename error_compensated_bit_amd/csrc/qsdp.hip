@@ -287,9 +287,12 @@ __global__ __launch_bounds__(256, 6) void k_qsdp_quantize_1024(QArgs a) {
 constexpr int kDeqBatch = 4;
 constexpr int kDeqWords = 2;  // code words per lane and half-bucket (4-bit uses one)
 
+// The fp32 output of a whole half-bucket passes through the wave's LDS buffer `wl`
+// (128 16-byte slots), so that its stores are contiguous 1 KiB runs too.
 template <int BITS>
 __device__ __forceinline__ void dequant8_store(const QArgs &a, int64_t base, int32_t len, int k0, float mn,
-                                              float delta, const uint32_t (&wv)[kDeqWords]) {
+                                              float delta, const uint32_t (&wv)[kDeqWords], float4 *wl,
+                                              bool half_whole, int64_t half_base) {
     uint32_t code[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -298,8 +301,18 @@ __device__ __forceinline__ void dequant8_store(const QArgs &a, int64_t base, int
 #pragma unroll
     for (int q = 0; q < 8; ++q) y[q] = add_rn(mn, mul_rn((float)code[q], delta));
     const int64_t i0 = base + k0;
+    if (a.out_f32 && half_whole) {
+        const int lane = threadIdx.x & 63;
+        wl[2 * lane] = make_float4(y[0], y[1], y[2], y[3]);
+        wl[2 * lane + 1] = make_float4(y[4], y[5], y[6], y[7]);
+        __builtin_amdgcn_wave_barrier();
+        float4 *o = reinterpret_cast<float4 *>(a.out_f32 + half_base);
+        st_stream(o + lane, wl[lane]);
+        st_stream(o + 64 + lane, wl[64 + lane]);
+        __builtin_amdgcn_wave_barrier();
+    }
     if (k0 + 7 < len) {
-        if (a.out_f32) {
+        if (a.out_f32 && !half_whole) {
             float4 *o = reinterpret_cast<float4 *>(a.out_f32 + i0);
             o[0] = make_float4(y[0], y[1], y[2], y[3]);
             o[1] = make_float4(y[4], y[5], y[6], y[7]);
@@ -322,6 +335,8 @@ __device__ __forceinline__ void dequant8_store(const QArgs &a, int64_t base, int
 
 template <int BITS>
 __global__ __launch_bounds__(256) void k_qsdp_dequantize_1024(QArgs a) {
+    __shared__ float4 s_y[4][128];
+    float4 *const wl = s_y[threadIdx.x >> 6];
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
@@ -373,7 +388,9 @@ __global__ __launch_bounds__(256) void k_qsdp_dequantize_1024(QArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int k0 = 8 * lane + 512 * h;
-                if (k0 < len) dequant8_store<BITS>(a, base, len, k0, mn[u], delta, wv[u][h]);
+                if (k0 < len)
+                    dequant8_store<BITS>(a, base, len, k0, mn[u], delta, wv[u][h], wl, len >= 512 * (h + 1),
+                                         base + 512 * h);
             }
         }
     }
@@ -488,15 +505,61 @@ __device__ __forceinline__ double block_sum_d(double v, double *s_red) {
 
 // partials[2b] = sum (y - x), partials[2b+1] = sum (y - x)^2 over block b's share;
 // ysum += y when given.
+// Two consecutive elements per thread and access, so that every access
+// instruction of a wave covers whole contiguous lines (256 B of weights, 512 B of
+// y, 1 KiB of ysum), with kStatU pairs per thread in flight; fp64 running sums in a
+// fixed order (bitwise reproducible).  An odd last element is taken by thread 0.
+constexpr int kStatU = 4;
+
+__device__ __forceinline__ void ld_f64x2(const double *p, double &a, double &b) {
+    const uint4 w = ld_stream(reinterpret_cast<const uint4 *>(p));
+    a = __hiloint2double((int)w.y, (int)w.x);
+    b = __hiloint2double((int)w.w, (int)w.z);
+}
+__device__ __forceinline__ void st_f64x2(double *p, double a, double b) {
+    const uint64_t ua = (uint64_t)__double_as_longlong(a), ub = (uint64_t)__double_as_longlong(b);
+    st_stream(reinterpret_cast<uint4 *>(p), make_uint4((uint32_t)ua, (uint32_t)(ua >> 32), (uint32_t)ub, (uint32_t)(ub >> 32)));
+}
+
+__device__ __forceinline__ void stat_add(double &s1, double &s2, float yv, uint32_t xbits) {
+    const double d = (double)yv - (double)bf16_bits_to_float(xbits);
+    s1 += d;
+    s2 += d * d;
+}
+
 __global__ __launch_bounds__(256) void k_qsdp_stats(const uint16_t *x, const float *y, int64_t n, double *ysum,
                                                      double *partials) {
     __shared__ double s_red[4];
     double s1 = 0.0, s2 = 0.0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
-        const double d = (double)y[i] - (double)bf16_bits_to_float(x[i]);
-        s1 += d;
-        s2 += d * d;
+    const int64_t pairs = n / 2;
+    const int64_t span = (int64_t)blockDim.x * kStatU;
+    for (int64_t base = blockIdx.x * span; base < pairs; base += (int64_t)gridDim.x * span) {
+        uint32_t xx[kStatU];
+        uint2 yy[kStatU];
+        double ya[kStatU], yb[kStatU];
+#pragma unroll
+        for (int u = 0; u < kStatU; ++u) {
+            const int64_t p = base + u * (int64_t)blockDim.x + threadIdx.x;
+            if (p < pairs) {
+                xx[u] = ld_stream(reinterpret_cast<const uint32_t *>(x + 2 * p));
+                yy[u] = ld_stream(reinterpret_cast<const uint2 *>(y + 2 * p));
+                if (ysum) ld_f64x2(ysum + 2 * p, ya[u], yb[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStatU; ++u) {
+            const int64_t p = base + u * (int64_t)blockDim.x + threadIdx.x;
+            if (p < pairs) {
+                const float y0 = __uint_as_float(yy[u].x), y1 = __uint_as_float(yy[u].y);
+                stat_add(s1, s2, y0, xx[u] & 0xffffu);
+                stat_add(s1, s2, y1, xx[u] >> 16);
+                if (ysum) st_f64x2(ysum + 2 * p, ya[u] + (double)y0, yb[u] + (double)y1);
+            }
+        }
+    }
+    if ((n & 1) && blockIdx.x == 0 && threadIdx.x == 0) {
+        const int64_t i = n - 1;
+        stat_add(s1, s2, y[i], x[i]);
         if (ysum) ysum[i] += (double)y[i];
     }
     const double t1 = block_sum_d(s1, s_red);
@@ -507,14 +570,35 @@ __global__ __launch_bounds__(256) void k_qsdp_stats(const uint16_t *x, const flo
     }
 }
 
-// partials[b] = sum |ysum / seeds - x| over block b's share
+// partials[b] = sum |ysum / seeds - x| over block b's share (same access pattern)
 __global__ __launch_bounds__(256) void k_qsdp_mae(const uint16_t *x, const double *ysum, int64_t n, double inv_seeds,
                                                    double *partials) {
     __shared__ double s_red[4];
     double s = 0.0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
-        s += fabs(ysum[i] * inv_seeds - (double)bf16_bits_to_float(x[i]));
+    const int64_t pairs = n / 2;
+    const int64_t span = (int64_t)blockDim.x * kStatU;
+    for (int64_t base = blockIdx.x * span; base < pairs; base += (int64_t)gridDim.x * span) {
+        uint32_t xx[kStatU];
+        double ya[kStatU], yb[kStatU];
+#pragma unroll
+        for (int u = 0; u < kStatU; ++u) {
+            const int64_t p = base + u * (int64_t)blockDim.x + threadIdx.x;
+            if (p < pairs) {
+                xx[u] = ld_stream(reinterpret_cast<const uint32_t *>(x + 2 * p));
+                ld_f64x2(ysum + 2 * p, ya[u], yb[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStatU; ++u) {
+            const int64_t p = base + u * (int64_t)blockDim.x + threadIdx.x;
+            if (p < pairs) {
+                s += fabs(ya[u] * inv_seeds - (double)bf16_bits_to_float(xx[u] & 0xffffu));
+                s += fabs(yb[u] * inv_seeds - (double)bf16_bits_to_float(xx[u] >> 16));
+            }
+        }
+    }
+    if ((n & 1) && blockIdx.x == 0 && threadIdx.x == 0)
+        s += fabs(ysum[n - 1] * inv_seeds - (double)bf16_bits_to_float(x[n - 1]));
     const double t = block_sum_d(s, s_red);
     if (threadIdx.x == 0) partials[blockIdx.x] = t;
 }
@@ -623,7 +707,8 @@ extern "C" onebit_status_t qsdp_error_stats(const uint16_t *x_bf16, const float 
                                             double *sums, double *partials, void *stream) {
     if (n < 0 || !sums || !partials) return ONEBIT_ERR_INVALID;
     if (n > 0 && (!x_bf16 || !y)) return ONEBIT_ERR_INVALID;
-    if (!aligned_to(sums, 8) || !aligned_to(partials, 8) || (ysum && !aligned_to(ysum, 8))) return ONEBIT_ERR_ALIGN;
+    if (!aligned_to(sums, 8) || !aligned_to(partials, 8) || (ysum && !aligned16(ysum))) return ONEBIT_ERR_ALIGN;
+    if (n > 0 && (!aligned16(x_bf16) || !aligned16(y))) return ONEBIT_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     prof_before(kProfFinalize, s);
     hipLaunchKernelGGL(k_qsdp_stats, dim3(kStatBlocks), dim3(256), 0, s, x_bf16, y, n, ysum, partials);
@@ -635,7 +720,7 @@ extern "C" onebit_status_t qsdp_error_stats(const uint16_t *x_bf16, const float 
 extern "C" onebit_status_t qsdp_mean_abs_error(const uint16_t *x_bf16, const double *ysum, int64_t n, int seeds,
                                                double *out, double *partials, void *stream) {
     if (n < 1 || seeds < 1 || !x_bf16 || !ysum || !out || !partials) return ONEBIT_ERR_INVALID;
-    if (!aligned_to(ysum, 8) || !aligned_to(out, 8) || !aligned_to(partials, 8)) return ONEBIT_ERR_ALIGN;
+    if (!aligned16(ysum) || !aligned16(x_bf16) || !aligned_to(out, 8) || !aligned_to(partials, 8)) return ONEBIT_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(k_qsdp_mae, dim3(kStatBlocks), dim3(256), 0, s, x_bf16, ysum, n, 1.0 / (double)seeds, partials);
     hipLaunchKernelGGL(k_reduce_partials, dim3(1), dim3(256), 0, s, (const double *)partials, 1, out, 0);

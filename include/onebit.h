@@ -318,13 +318,15 @@ onebit_status_t qsdp_dequantize(const uint8_t *codes, const float *bucket_min,
  * the weight):  sums[0] += sum_i (y_i - x_i),  sums[1] += sum_i (y_i - x_i)^2,
  * both fp64 (device [2]); ysum (device fp64 [n], nullable): ysum_i += y_i.
  * partials: device scratch of 2 * QSDP_STATS_PARTIALS doubles.  The reduction
- * order is fixed, so results are bitwise reproducible. */
+ * order is fixed, so results are bitwise reproducible.  x_bf16, y and ysum must be
+ * 16-byte aligned (ONEBIT_ERR_ALIGN otherwise). */
 #define QSDP_STATS_PARTIALS 1024
 onebit_status_t qsdp_error_stats(const uint16_t *x_bf16, const float *y, int64_t n, double *ysum,
                                  double *sums, double *partials, void *stream);
 
 /* *out (device fp64) = sum_i | ysum_i / seeds - x_i |: with the mean abs error of
- * the seed-averaged quantizer, divide by n.  Same partials scratch. */
+ * the seed-averaged quantizer, divide by n.  Same partials scratch; x_bf16 and
+ * ysum 16-byte aligned. */
 onebit_status_t qsdp_mean_abs_error(const uint16_t *x_bf16, const double *ysum, int64_t n, int seeds,
                                     double *out, double *partials, void *stream);
 
