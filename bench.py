@@ -49,6 +49,8 @@ B_WORKER_F16 = 14.125        # read g fp16 (2), m, e; write e; bits
 B_FINISH_MASK = 21.0         # read m, mask (1), v, x; write m, x
 B_FINISH_PACKED = 13.125     # read 1/8 B of server words, mask (1), v, x; write x
 B_QSDP4, B_QSDP8 = 2.0 + 0.5 + 8.0 / 1024, 2.0 + 1.0 + 8.0 / 1024
+B_QSDP_STAT = 22.0           # the statistic: read x bf16 (2), y fp32 (4), ysum fp64 (8); write ysum (8)
+B_QSDP_MAE = 10.0            # mean abs error of the seed average: read x bf16 (2), ysum fp64 (8)
 
 
 def log(*a):
@@ -225,6 +227,17 @@ def cpu_row_baselines(rows, budget_s=1.0):
         r, c = _oracle_rate(lambda: oracle.qsdp_dequantize(codes, bmin, bmax, n, bucket=q.bucket, bits=bits), n,
                             budget_s)
         put(f"qsdp{bits}_dequantize", r, "elems/s", f"{n} bf16 weights, buckets of {q.bucket}", c)
+
+    # one seed of the 64-seed statistic: oracle quantize, dequantize to fp32, fp64 sums
+    xf = oracle.bf16_bits_to_f32(xb).astype(np.float64)
+
+    def stat_seed():
+        cds, mn_, mx_ = oracle.qsdp_quantize(xb, bucket=q.bucket, bits=4, seed=1)
+        _, yf = oracle.qsdp_dequantize(cds, mn_, mx_, n, bucket=q.bucket, bits=4, want_f32=True)
+        d = yf.astype(np.float64) - xf
+        return d.sum(), (d * d).sum()
+    r, c = _oracle_rate(stat_seed, n, budget_s)
+    put("qsdp4_seed_statistic", r, "elems/s", f"one seed over {n} bf16 weights (oracle draws, numpy fp64 sums)", c)
 
     # QSGD / LoCo on bf16 gradients with per-block scales
     qg = W.QsgdWorkload()
@@ -745,6 +758,31 @@ def secondary_rows(dev, args):
         rows[f"qsdp{bits}_dequantize"] = dict(elems_per_s=q.n / td, gbps=bpe * q.n / td / 1e9)
         rows[f"qsdp{bits}_dequantize"]["roofline"] = roof(bpe * q.n / td / 1e9)
         del codes, out
+    # one seed of the 64-seed error statistic (4-bit): quantize, dequantize to fp32,
+    # then the statistic (sums of y - x and (y - x)^2, ysum += y); the mean absolute
+    # error of the seed average runs once after the 64 seeds
+    codes = torch.zeros((q.n + 1) // 2, dtype=torch.uint8, device=dev)
+    y = torch.zeros(q.n, device=dev)
+    ysum = torch.zeros(q.n, dtype=torch.float64, device=dev)
+    sums = torch.zeros(2, dtype=torch.float64, device=dev)
+    part = torch.zeros(2 * ob.QSDP_STATS_PARTIALS, dtype=torch.float64, device=dev)
+    mae = torch.zeros(1, dtype=torch.float64, device=dev)
+    seed = [0]
+
+    def one_seed():
+        ob.qsdp_quantize(xq, q.bucket, 4, seed[0], codes, bmin, bmax)
+        ob.qsdp_dequantize(codes, bmin, bmax, q.n, q.bucket, 4, None, y)
+        ob.qsdp_error_stats(xq, y, ysum, sums, part)
+        seed[0] += 1
+    ts, kts = timed(one_seed, steps, 1)
+    tm, _ = timed(lambda: ob.qsdp_mean_abs_error(xq, ysum, q.seeds, mae, part), steps, 1)
+    st_ms = kts.mean_ms("finalize")
+    rows["qsdp4_seed_statistic"] = dict(
+        ms_per_seed=ts * 1e3, elems_per_s=q.n / ts, ms_64_seeds=(q.seeds * ts + tm) * 1e3,
+        statistic_kernel_gbps=B_QSDP_STAT * q.n / (st_ms * 1e-3) / 1e9,
+        mean_abs_error_gbps=B_QSDP_MAE * q.n / tm / 1e9,
+        roofline=roof(B_QSDP_STAT * q.n / (st_ms * 1e-3) / 1e9))
+    del codes, y, ysum
     del xq, bmin, bmax
     torch.cuda.empty_cache()
     log(f"[bench] qsdp {[(k, v) for k, v in rows.items() if 'qsdp' in k]}")

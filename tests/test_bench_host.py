@@ -40,7 +40,7 @@ def test_quantizer_valu_summary_parses():
 
 def test_every_row_gets_a_cpu_oracle_timing():
     keys = ["warmup_adam_bert_large", "qsdp4_quantize", "qsdp4_dequantize", "qsdp8_quantize", "qsdp8_dequantize",
-            "qsgd4_quantize", "qsgd8_quantize", "loco4_quantize", "allreduce_16x64M", "full_step_16x64M_f16_mask",
+            "qsgd4_quantize", "qsgd8_quantize", "loco4_quantize", "qsdp4_seed_statistic", "allreduce_16x64M", "full_step_16x64M_f16_mask",
             "full_step_16x64M_f16_mask_packed_m", "gpu_share_of_16_64M_f16_mask",
             "gpu_share_of_16_64M_f16_mask_packed_m", "compress_bert_large_packed_m", "compress_gpt2_xl_bf16"]
     from error_compensated_bit_amd import workloads as W
