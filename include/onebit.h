@@ -152,7 +152,9 @@ onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
  * HBM delivers for that mix on this device.  in / out: DEVICE arrays of `reads` /
  * `writes` device pointers, each 16-byte aligned; n a multiple of 4.  Supported
  * mixes: 5 reads + 3 writes (the compression kernel's), 1 + 1 (a copy); others
- * return ONEBIT_ERR_UNSUPPORTED.  grid: workgroups of 256 threads. */
+ * return ONEBIT_ERR_UNSUPPORTED.  grid: workgroups of 256 threads.  Loads and
+ * stores use the streaming (nontemporal) cache policy, as the compression
+ * kernels do. */
 onebit_status_t onebit_stream_probe(const float *const *in, int reads, float *const *out, int writes,
                                     int64_t n, int grid, void *stream);
 
