@@ -58,6 +58,29 @@ def test_stats_match_numpy_on_oracle_draws():
     np.testing.assert_allclose(host(mae)[0], np.abs(ref_ysum / S - xf).sum(), rtol=1e-12)
 
 
+def test_stats_without_the_seed_sum():
+    """ysum is optional: the sums alone, on an odd length (the last element is taken
+    apart from the pairs)."""
+    n, bucket, bits = 4099, 1024, 8
+    x = torch.from_numpy((np.random.default_rng(8).standard_normal(n) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    xd = x.to(DEV)
+    xh = x.view(torch.int16).numpy().view(np.uint16)
+    codes, bmin, bmax = _buffers(n, bucket, bits)
+    y = torch.zeros(n, device=DEV)
+    sums = torch.zeros(2, dtype=torch.float64, device=DEV)
+    part = torch.zeros(2 * ob.QSDP_STATS_PARTIALS, dtype=torch.float64, device=DEV)
+    ob.qsdp_quantize(xd, bucket, bits, 5, codes, bmin, bmax)
+    ob.qsdp_dequantize(codes, bmin, bmax, n, bucket, bits, None, y)
+    ob.qsdp_error_stats(xd, y, None, sums, part)
+    rc, rmn, rmx = oracle.qsdp_quantize(xh, bucket=bucket, bits=bits, seed=5)
+    _, ry = oracle.qsdp_dequantize(rc, rmn, rmx, n, bucket=bucket, bits=bits, want_f32=True)
+    d = ry.astype(np.float64) - oracle.bf16_bits_to_f32(xh).astype(np.float64)
+    torch.cuda.synchronize()
+    got = host(sums)
+    assert abs(got[0] - d.sum()) <= 1e-12 * np.abs(ry).sum() + 1e-15
+    np.testing.assert_allclose(got[1], (d * d).sum(), rtol=1e-12)
+
+
 def test_64_seed_statistic_full_size():
     q = W.QsdpWorkload()
     bits, S = 4, q.seeds
