@@ -683,22 +683,23 @@ def stream_ceiling(dev, n=335_544_320):
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     best = {}
     for name, ins, outs, bpe in (("5r3w", bufs[:5], bufs[5:], 32.0),):
-        for mult in (1, 2, 3, 6, 16, 32):
-            keep = ob.onebit_stream_probe(ins, outs, cus * mult)           # warm
-            times = []
-            for _ in range(4):
-                ev0.record()
-                keep = ob.onebit_stream_probe(ins, outs, cus * mult)
-                ev1.record()
-                ev1.synchronize()
-                times.append(ev0.elapsed_time(ev1))
-            del keep
-            gbps = bpe * n / (min(times) * 1e-3) / 1e9
-            if gbps > best.get(name, (0.0, 0))[0]:
-                best[name] = (gbps, cus * mult)
+        for block, mults in ((256, (1, 2, 3, 6, 16, 32)), (1024, (1, 2, 4, 6, 8))):
+            for mult in mults:
+                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block)    # warm
+                times = []
+                for _ in range(4):
+                    ev0.record()
+                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block)
+                    ev1.record()
+                    ev1.synchronize()
+                    times.append(ev0.elapsed_time(ev1))
+                del keep
+                gbps = bpe * n / (min(times) * 1e-3) / 1e9
+                if gbps > best.get(name, (0.0, 0, 0))[0]:
+                    best[name] = (gbps, cus * mult, block)
     del bufs
-    return {"gbps_5r3w": best["5r3w"][0], "grid_5r3w": best["5r3w"][1], "elements": n,
-            "kernel": "onebit_stream_probe"}
+    return {"gbps_5r3w": best["5r3w"][0], "grid_5r3w": best["5r3w"][1], "block_5r3w": best["5r3w"][2],
+            "elements": n, "kernel": "onebit_stream_probe"}
 
 
 def roof(gbps, elems_per_s=None, label=None, valu=None):

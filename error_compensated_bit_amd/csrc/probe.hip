@@ -12,7 +12,7 @@ namespace onebit {
 constexpr int kProbeU = 4;
 
 template <int R, int WR>
-__global__ __launch_bounds__(256) void k_stream_probe(const float4 *const *in, float4 *const *out, int64_t n4) {
+__global__ __launch_bounds__(1024) void k_stream_probe(const float4 *const *in, float4 *const *out, int64_t n4) {
     const float4 *src[R];
     float4 *dst[WR];
 #pragma unroll
@@ -52,8 +52,9 @@ __global__ __launch_bounds__(256) void k_stream_probe(const float4 *const *in, f
 using namespace onebit;
 
 extern "C" onebit_status_t onebit_stream_probe(const float *const *in, int reads, float *const *out, int writes,
-                                               int64_t n, int grid, void *stream) {
+                                               int64_t n, int grid, int block, void *stream) {
     if (n < 0 || grid < 1 || !in || !out) return ONEBIT_ERR_INVALID;
+    if (block != 256 && block != 512 && block != 1024) return ONEBIT_ERR_INVALID;
     if (n % 4 != 0) return ONEBIT_ERR_ALIGN;
     const bool five_three = reads == 5 && writes == 3, one_one = reads == 1 && writes == 1;
     if (!five_three && !one_one) return ONEBIT_ERR_UNSUPPORTED;
@@ -62,8 +63,8 @@ extern "C" onebit_status_t onebit_stream_probe(const float *const *in, int reads
     const auto *i4 = reinterpret_cast<const float4 *const *>(in);
     auto *o4 = reinterpret_cast<float4 *const *>(out);
     if (five_three)
-        hipLaunchKernelGGL((k_stream_probe<5, 3>), dim3(grid), dim3(256), 0, s, i4, o4, n / 4);
+        hipLaunchKernelGGL((k_stream_probe<5, 3>), dim3(grid), dim3(block), 0, s, i4, o4, n / 4);
     else
-        hipLaunchKernelGGL((k_stream_probe<1, 1>), dim3(grid), dim3(256), 0, s, i4, o4, n / 4);
+        hipLaunchKernelGGL((k_stream_probe<1, 1>), dim3(grid), dim3(block), 0, s, i4, o4, n / 4);
     return hip_status(hipGetLastError());
 }

@@ -43,7 +43,7 @@ _SIGS = {
     "onebit_compress_update_packed": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
     "onebit_momentum_update_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _P]),
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
-    "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _P]),
+    "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _I, _P]),
     "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
     "qsgd_quantize": (_I, [_P, _I, _I64, _I, _I, _U64, _P, _P, _P]),
     "qsgd_reduce": (_I, [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P, _P]),
@@ -293,14 +293,15 @@ def onebit_server_reduce(plan, worker_bits, worker_scales, server_error, server_
                                        _stream(stream)), "onebit_server_reduce")
 
 
-def onebit_stream_probe(inputs, outputs, grid, stream=None):
-    """inputs / outputs: lists of equally long fp32 device tensors (5 + 3 or 1 + 1)."""
+def onebit_stream_probe(inputs, outputs, grid, block=256, stream=None):
+    """inputs / outputs: lists of equally long fp32 device tensors (5 + 3 or 1 + 1);
+    block: threads per workgroup (256, 512 or 1024)."""
     import torch
     dev = inputs[0].device
     pin = torch.tensor([t.data_ptr() for t in inputs], dtype=torch.int64, device=dev)
     pout = torch.tensor([t.data_ptr() for t in outputs], dtype=torch.int64, device=dev)
     _check(load().onebit_stream_probe(_ptr(pin), len(inputs), _ptr(pout), len(outputs), inputs[0].numel(), int(grid),
-                                      _stream(stream)), "onebit_stream_probe")
+                                      int(block), _stream(stream)), "onebit_stream_probe")
     return pin, pout           # keep the pointer arrays alive until the launch has run
 
 

@@ -152,11 +152,11 @@ onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
  * HBM delivers for that mix on this device.  in / out: DEVICE arrays of `reads` /
  * `writes` device pointers, each 16-byte aligned; n a multiple of 4.  Supported
  * mixes: 5 reads + 3 writes (the compression kernel's), 1 + 1 (a copy); others
- * return ONEBIT_ERR_UNSUPPORTED.  grid: workgroups of 256 threads.  Loads and
- * stores use the streaming (nontemporal) cache policy, as the compression
- * kernels do. */
+ * return ONEBIT_ERR_UNSUPPORTED.  grid: number of workgroups; block: threads per
+ * workgroup, 256, 512 or 1024 (ONEBIT_ERR_INVALID otherwise).  Loads and stores
+ * use the streaming (nontemporal) cache policy, as the compression kernels do. */
 onebit_status_t onebit_stream_probe(const float *const *in, int reads, float *const *out, int writes,
-                                    int64_t n, int grid, void *stream);
+                                    int64_t n, int grid, int block, void *stream);
 
 /* Warmup step t (1-based) of full-precision Adam over n elements ([DSG] sec. 4,
  * phase one; [1BA]):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
