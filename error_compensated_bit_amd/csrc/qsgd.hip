@@ -69,13 +69,120 @@ __device__ __forceinline__ float norm_of(DD acc) {
     return (float)__dsqrt_rn(t.hi);
 }
 
-// Buckets of 1024: one wave per bucket, lane l owns the 16 consecutive elements
-// 16l..16l+15, kept in registers between the norm and the codes; four Philox calls
-// per lane; one 8- or 16-byte store of codes.  In whole buckets the gradient (and
-// LoCo's error average, both ways) moves between HBM and the lanes through LDS:
-// every load or store instruction of the wave covers one contiguous 1 KiB run
-// (streaming cache policy), and each lane then reads its own 16 elements.
+// Group j (four elements) of this lane's sixteen in a whole bucket staged in LDS:
+// the value that is quantized (g, or with LoCo h = g + err) and, with LoCo, err.
+template <int GT, bool LOCO>
+__device__ __forceinline__ void staged_group(const float4 *wg, const float4 *we, int lane, int j, float (&h)[4],
+                                             float (&e)[4]) {
+    if (GT == kGradF32) {
+        const float4 t = wg[4 * lane + j];
+        h[0] = t.x; h[1] = t.y; h[2] = t.z; h[3] = t.w;
+    } else {
+        const uint2 t = reinterpret_cast<const uint2 *>(wg)[4 * lane + j];
+        h[0] = half_bits_to_float<GT>(t.x & 0xffffu);
+        h[1] = half_bits_to_float<GT>(t.x >> 16);
+        h[2] = half_bits_to_float<GT>(t.y & 0xffffu);
+        h[3] = half_bits_to_float<GT>(t.y >> 16);
+    }
+    if (LOCO) {
+        const float4 t = we[4 * lane + j];
+        e[0] = t.x; e[1] = t.y; e[2] = t.z; e[3] = t.w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = add_rn(h[q], e[q]);     // compensated gradient h
+    }
+}
+
+// The lane's sixteen codes (element 16l + q of the bucket at code[q]): one 8-byte
+// (4-bit) or 16-byte (8-bit) store, bytewise at a ragged end.
+template <int BITS>
+__device__ __forceinline__ void store_codes(const GArgs &a, int64_t base, int k0, int32_t len,
+                                            const uint32_t (&code)[16]) {
+    if (BITS == 4) {
+        uint2 pk;
+        pk.x = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12) | (code[4] << 16) | (code[5] << 20) |
+               (code[6] << 24) | (code[7] << 28);
+        pk.y = code[8] | (code[9] << 4) | (code[10] << 8) | (code[11] << 12) | (code[12] << 16) |
+               (code[13] << 20) | (code[14] << 24) | (code[15] << 28);
+        uint8_t *dst = a.codes + ((base + k0) >> 1);
+        if (k0 + 15 < len) {
+            *reinterpret_cast<uint2 *>(dst) = pk;
+        } else {
+            for (int q = 0; 2 * q < len - k0; ++q) dst[q] = (uint8_t)(((q < 4 ? pk.x : pk.y) >> (8 * (q & 3))) & 0xffu);
+        }
+    } else {
+        uint4 pk;
+        pk.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+        pk.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+        pk.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
+        pk.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
+        uint8_t *dst = a.codes + base + k0;
+        if (k0 + 15 < len) {
+            *reinterpret_cast<uint4 *>(dst) = pk;
+        } else {
+            for (int q = 0; q < len - k0; ++q) dst[q] = (uint8_t)code[q];
+        }
+    }
+}
+
+// A whole bucket of 1024 staged in LDS (g in wg, LoCo's err in we): pass 1 sums the
+// squares of the lane's sixteen values in order (the norm), pass 2 codes them and
+// updates the error average group by group, writing it back to the lane's own LDS
+// slots; then the error average leaves as contiguous 1 KiB runs and the codes as
+// one store per lane.  Every value is formed by the same operations, in the same
+// order, as for a bucket held in registers.
 template <int BITS, int GT, bool LOCO>
+__device__ __forceinline__ void quantize_whole_bucket(const GArgs &a, int64_t b, int64_t base, int lane, float4 *wg,
+                                                      float4 *we) {
+    const int k0 = 16 * lane;
+    DD acc{0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float h[4], e[4];
+        staged_group<GT, LOCO>(wg, we, lane, j, h, e);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dd_add_term(acc, (double)h[q] * (double)h[q]);   // each square exact
+    }
+    const float norm = norm_of(acc);
+    const double rnorm = recip_rn64(norm);
+    if (lane == 0) a.norms[b] = norm;
+    const float st = __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
+    uint32_t code[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float h[4], e[4];
+        staged_group<GT, LOCO>(wg, we, lane, j, h, e);
+        const uint64_t blk = (uint64_t)(base + k0 + 4 * j) >> 2;
+        const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, a.k0, a.k1);
+        code[4 * j + 0] = qsgd_code<BITS>(h[0], norm, rnorm, r.a);
+        code[4 * j + 1] = qsgd_code<BITS>(h[1], norm, rnorm, r.b);
+        code[4 * j + 2] = qsgd_code<BITS>(h[2], norm, rnorm, r.c);
+        code[4 * j + 3] = qsgd_code<BITS>(h[3], norm, rnorm, r.d);
+        if (LOCO) {
+            float en[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) en[q] = loco_update<BITS>(a, e[q], h[q], code[4 * j + q], st);
+            we[4 * lane + j] = make_float4(en[0], en[1], en[2], en[3]);
+        }
+    }
+    if (LOCO) {
+        __builtin_amdgcn_wave_barrier();
+        float4 *dst = reinterpret_cast<float4 *>(a.err + base);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) st_stream(dst + 64 * h + lane, we[64 * h + lane]);
+    }
+    store_codes<BITS>(a, base, k0, 1024, code);
+    __builtin_amdgcn_wave_barrier();   // the staged bucket is read before the next one overwrites it
+}
+
+// Buckets of 1024: one wave per bucket, lane l owns the 16 consecutive elements
+// 16l..16l+15; four Philox calls per lane; one 8- or 16-byte store of codes.
+// TAIL = false takes the whole buckets: the gradient (and LoCo's error average, both
+// ways) moves between HBM and LDS as contiguous 1 KiB runs per wave instruction
+// (streaming cache policy) and the lanes read their elements from LDS in both passes
+// (quantize_whole_bucket).  TAIL = true takes only the ragged last bucket, its
+// elements kept in registers between the norm and the codes; it is a launch of its
+// own so that its registers do not set the occupancy of the whole-bucket kernel.
+template <int BITS, int GT, bool LOCO, bool TAIL>
 __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
     __shared__ float4 s_g[4][256];
     __shared__ float4 s_e[4][LOCO ? 256 : 1];
@@ -84,14 +191,16 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
-    for (int64_t b = wave; b < a.n_buckets; b += nwaves) {
+    const int64_t n_whole = a.n / 1024;
+    for (int64_t b = (TAIL ? n_whole : 0) + wave; b < (TAIL ? a.n_buckets : n_whole); b += nwaves) {
         const int64_t base = b * 1024;
         const int32_t len = (int32_t)min((int64_t)1024, a.n - base);
-        const bool whole = len == 1024;  // uniform over the wave
         const int k0 = 16 * lane;
         float f[16];
         float ea[LOCO ? 16 : 1];
-        if (whole) {
+        if (!TAIL) {
+            // the bucket goes to LDS only; the lanes read their elements from there in
+            // both passes below, so nothing of it stays live in registers
             if (GT == kGradF32) {
                 const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + base);
                 float4 v[4];
@@ -99,12 +208,6 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
                 for (int h = 0; h < 4; ++h) v[h] = ld_stream(src + 64 * h + lane);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) wg[64 * h + lane] = v[h];
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const float4 t = wg[4 * lane + h];
-                    f[4 * h] = t.x; f[4 * h + 1] = t.y; f[4 * h + 2] = t.z; f[4 * h + 3] = t.w;
-                }
             } else {
                 const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.g) + base);
                 uint4 *wu = reinterpret_cast<uint4 *>(wg);
@@ -113,17 +216,6 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
                 for (int h = 0; h < 2; ++h) v[h] = ld_stream(src + 64 * h + lane);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) wu[64 * h + lane] = v[h];
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint4 t = wu[2 * lane + h];
-                    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        f[8 * h + 2 * q] = half_bits_to_float<GT>(w[q] & 0xffffu);
-                        f[8 * h + 2 * q + 1] = half_bits_to_float<GT>(w[q] >> 16);
-                    }
-                }
             }
             if (LOCO) {
                 const float4 *src = reinterpret_cast<const float4 *>(a.err + base);
@@ -132,13 +224,10 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
                 for (int h = 0; h < 4; ++h) v[h] = ld_stream(src + 64 * h + lane);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) we[64 * h + lane] = v[h];
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const float4 t = we[4 * lane + h];
-                    ea[4 * h] = t.x; ea[4 * h + 1] = t.y; ea[4 * h + 2] = t.z; ea[4 * h + 3] = t.w;
-                }
             }
+            __builtin_amdgcn_wave_barrier();
+            quantize_whole_bucket<BITS, GT, LOCO>(a, b, base, lane, wg, we);
+            continue;
         } else if (k0 + 15 < len) {
             if (GT == kGradF32) {
                 const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + base + k0);
@@ -164,7 +253,7 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) f[q] = (k0 + q < len) ? load_grad<GT>(a.g, base + k0 + q) : 0.0f;
         }
-        if (LOCO && !whole) {
+        if (LOCO) {
             if (k0 + 15 < len) {
                 const float4 *src = reinterpret_cast<const float4 *>(a.err + base + k0);
 #pragma unroll
@@ -204,15 +293,7 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
             const float st = __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
 #pragma unroll
             for (int q = 0; q < 16; ++q) ea[q] = loco_update<BITS>(a, ea[q], f[q], code[q], st);
-            if (whole) {
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int h = 0; h < 4; ++h) we[4 * lane + h] = make_float4(ea[4 * h], ea[4 * h + 1], ea[4 * h + 2], ea[4 * h + 3]);
-                __builtin_amdgcn_wave_barrier();
-                float4 *dst = reinterpret_cast<float4 *>(a.err + base);
-#pragma unroll
-                for (int h = 0; h < 4; ++h) st_stream(dst + 64 * h + lane, we[64 * h + lane]);
-            } else if (k0 + 15 < len) {
+            if (k0 + 15 < len) {
                 float4 *dst = reinterpret_cast<float4 *>(a.err + base + k0);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) dst[h] = make_float4(ea[4 * h], ea[4 * h + 1], ea[4 * h + 2], ea[4 * h + 3]);
@@ -220,31 +301,7 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
                 for (int q = 0; q < len - k0; ++q) a.err[base + k0 + q] = ea[q];
             }
         }
-        if (BITS == 4) {
-            uint2 pk;
-            pk.x = code[0] | (code[1] << 4) | (code[2] << 8) | (code[3] << 12) | (code[4] << 16) | (code[5] << 20) |
-                   (code[6] << 24) | (code[7] << 28);
-            pk.y = code[8] | (code[9] << 4) | (code[10] << 8) | (code[11] << 12) | (code[12] << 16) |
-                   (code[13] << 20) | (code[14] << 24) | (code[15] << 28);
-            uint8_t *dst = a.codes + ((base + k0) >> 1);
-            if (k0 + 15 < len) {
-                *reinterpret_cast<uint2 *>(dst) = pk;
-            } else {
-                for (int q = 0; 2 * q < len - k0; ++q) dst[q] = (uint8_t)(((q < 4 ? pk.x : pk.y) >> (8 * (q & 3))) & 0xffu);
-            }
-        } else {
-            uint4 pk;
-            pk.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-            pk.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-            pk.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
-            pk.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
-            uint8_t *dst = a.codes + base + k0;
-            if (k0 + 15 < len) {
-                *reinterpret_cast<uint4 *>(dst) = pk;
-            } else {
-                for (int q = 0; q < len - k0; ++q) dst[q] = (uint8_t)code[q];
-            }
-        }
+        store_codes<BITS>(a, base, k0, len, code);
     }
 }
 
@@ -491,9 +548,11 @@ static int device_cus() {
 
 template <int BITS, int GT, bool LOCO>
 static void launch_quantize(const GArgs &a, unsigned grid, hipStream_t s) {
-    if (a.bucket == 1024)
-        hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO>), dim3(grid), dim3(256), 0, s, a);
-    else
+    if (a.bucket == 1024) {
+        // grid covers the whole buckets; one more workgroup takes a ragged last one
+        if (a.n >= 1024) hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO, false>), dim3(grid), dim3(256), 0, s, a);
+        if (a.n % 1024) hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO, true>), dim3(1), dim3(256), 0, s, a);
+    } else
         hipLaunchKernelGGL((k_qsgd_quantize_generic<BITS, GT, LOCO>), dim3(grid), dim3(256), 0, s, a);
 }
 

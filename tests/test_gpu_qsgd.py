@@ -55,7 +55,7 @@ def to_device(g, dt):
 @pytest.mark.parametrize("bits", [4, 8])
 def test_quantize_parity(bucket, bits):
     for dt in ("f32", "bf16", "f16"):
-        for n in (1, 2 * bucket + 7, 9 * 1024 + 333):
+        for n in (1, 2 * bucket + 7, 9 * 1024 + 333, 4 * 1024):    # 4096: no ragged bucket at 1024
             if bits == 4 and n % 2 == 1 and n > 1:
                 pass                                       # odd n: pad nibble
             rng = np.random.default_rng(n * 7 + bucket + bits)
@@ -210,8 +210,8 @@ def test_full_size_eight_workers(bits):
 
 @pytest.mark.parametrize("bucket,bits", [(1024, 4), (1024, 8), (30, 4), (1000, 8)])
 @pytest.mark.parametrize("beta", [0.0, 0.5, 0.9])
-def test_loco_parity(bucket, bits, beta):
-    n = 5 * 1024 + 77
+@pytest.mark.parametrize("n", [5 * 1024 + 77, 3 * 1024, 500])
+def test_loco_parity(bucket, bits, beta, n):
     rng = np.random.default_rng(bucket + bits)
     e0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
     for dt in ("f32", "bf16"):
