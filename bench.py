@@ -388,11 +388,11 @@ def quantizer_calls(dev):
     return [
         ("k_qsdp_quantize_1024<4>", "qsdp4_quantize", q.n, lambda: ob.qsdp_quantize(xq, q.bucket, 4, 0, codes, f1, f2)),
         ("k_qsdp_quantize_1024<8>", "qsdp8_quantize", q.n, lambda: ob.qsdp_quantize(xq, q.bucket, 8, 0, codes, f1, f2)),
-        ("k_qsgd_quantize_1024<4, 1, false>", "qsgd4_quantize", q.n,
+        ("k_qsgd_quantize_1024<4, 1, false, false>", "qsgd4_quantize", q.n,
          lambda: ob.qsgd_quantize(gq, q.bucket, 4, 0, codes, f1)),
-        ("k_qsgd_quantize_1024<8, 1, false>", "qsgd8_quantize", q.n,
+        ("k_qsgd_quantize_1024<8, 1, false, false>", "qsgd8_quantize", q.n,
          lambda: ob.qsgd_quantize(gq, q.bucket, 8, 0, codes, f1)),
-        ("k_qsgd_quantize_1024<4, 1, true>", "loco4_quantize", q.n,
+        ("k_qsgd_quantize_1024<4, 1, true, false>", "loco4_quantize", q.n,
          lambda: ob.loco_quantize(gq, err, q.bucket, 4, 0.9, 0, codes, f1)),
     ]
 
@@ -429,7 +429,9 @@ def summarize_quantizers(kt_dir, pmc_dir):
     out.append("")
     out.append(f"Issue-rate bound: {VALU_LANE_OPS_PER_S / 1e12:.2f} T VALU lane-instructions/s (256 CUs x 4 SIMD16 x "
                f"one wave64 instruction per 4 clocks x 2.4 GHz); elements/s bound = that / (SQ_INSTS_VALU x 64 / "
-               f"elements).  Transcendental and fp64 instructions issue at lower rates, so the bound is optimistic.")
+               f"elements).  Transcendental and fp64 instructions issue at lower rates, so the bound is optimistic.  "
+               f"The QSGD rows are the whole-bucket kernel; the one-workgroup launch for the ragged last bucket "
+               f"(256 elements) is not counted.")
     out.append("")
     out.append("| kernel | elements | average ns | SQ_INSTS_VALU per dispatch | VALU lane-instr per element | "
                "bound G elem/s | achieved G elem/s | fraction |")
@@ -452,9 +454,9 @@ def summarize_quantizers(kt_dir, pmc_dir):
 def quantizer_calls_meta():
     n = 1_300_000_000
     return [("k_qsdp_quantize_1024<4>", "qsdp4_quantize", n, None), ("k_qsdp_quantize_1024<8>", "qsdp8_quantize", n, None),
-            ("k_qsgd_quantize_1024<4, 1, false>", "qsgd4_quantize", n, None),
-            ("k_qsgd_quantize_1024<8, 1, false>", "qsgd8_quantize", n, None),
-            ("k_qsgd_quantize_1024<4, 1, true>", "loco4_quantize", n, None)]
+            ("k_qsgd_quantize_1024<4, 1, false, false>", "qsgd4_quantize", n, None),
+            ("k_qsgd_quantize_1024<8, 1, false, false>", "qsgd8_quantize", n, None),
+            ("k_qsgd_quantize_1024<4, 1, true, false>", "loco4_quantize", n, None)]
 
 
 def summarize_kernels(kt_dir, command):
