@@ -623,7 +623,12 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
     __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
     __shared__ uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int G = (int)gridDim.x;
-    const int b = (int)blockIdx.x;
+    // Workgroups are dispatched to the eight XCDs in turn; outside the server stage
+    // the ones on one XCD take consecutive list positions (one-pass BERT-Large step
+    // 1.80 -> 1.78 ms; the server tiles were 3% slower with it).  Any bijection of
+    // the workgroup ids keeps the progress argument above.
+    const bool xcd_runs = MODE != kServer && (G & 7) == 0;
+    const int b = xcd_runs ? (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
     const int mine = a.list_len > b ? (a.list_len - b + G - 1) / G : 0;  // tiles of this workgroup
     // prologue: post the first kDepth-1 tiles
     for (int i = 0; i < kDepth - 1 && i < mine; ++i) {
