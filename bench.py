@@ -21,6 +21,8 @@ Profiling (rocprofv3 runs the program itself, so these modes only do the work):
   python bench.py --profile            headline workload, a few steps, then a
                                        1 GiB device-to-device copy used to
                                        calibrate the FETCH_SIZE/WRITE_SIZE counters
+  python bench.py --profile-allreduce  the same for the 16-worker simulated all-reduce
+  python bench.py --summarize-allreduce KT FETCH WRITE
   python bench.py --summarize-profile KT FETCH WRITE
                                        turn three rocprofv3 CSV output directories
                                        (kernel trace+stats, --pmc FETCH_SIZE,
@@ -503,6 +505,89 @@ def _rows(dirname, suffix):
         return list(csv.DictReader(f))
 
 
+def profile_allreduce(steps):
+    """Work for rocprofv3: `steps` simulated all-reduce steps (16 workers x 64M), then a plain 1 GiB copy."""
+    import torch
+    ensure_built()
+    from error_compensated_bit_amd import onebit as ob
+    from error_compensated_bit_amd import workloads as W
+    dev = "cuda:0"
+    a = W.AllreduceWorkload()
+    plan = ob.onebit_plan_create(a.chunk_off)
+    words, nch = ob.onebit_plan_words(plan), ob.onebit_plan_chunks(plan)
+    m = torch.zeros(a.n, device=dev)
+    e = torch.zeros((a.W, a.n), device=dev)
+    es = torch.zeros(a.n, device=dev)
+    grads = torch.randn((a.W, a.n), device=dev) * a.grad_std
+    wbits = torch.zeros((a.W, words), dtype=torch.int32, device=dev)
+    wsc = torch.zeros((a.W, nch), device=dev)
+    sbits = torch.zeros(words, dtype=torch.int32, device=dev)
+    ssc = torch.zeros(nch, device=dev)
+    wsp = torch.zeros(ob.onebit_plan_workspace_bytes(plan) // 8, dtype=torch.int64, device=dev)
+    for _ in range(steps):
+        for w in range(a.W):
+            ob.onebit_compress_update(plan, grads[w], m, e[w], None, None, None, wbits[w], wsc[w], lr=0.0,
+                                      beta1=0.9, eps=1e-8, weight_decay=0.0, workspace=wsp)
+        ob.onebit_server_reduce(plan, wbits, wsc, es, sbits, ssc, m, wsp)
+    torch.cuda.synchronize()
+    assert ob.onebit_workspace_status(wsp) == 0, "a cross-workgroup wait timed out"
+    del e, grads
+    src = torch.ones(CALIBRATION_FLOATS, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[profile] {steps} all-reduce steps of {a.W} x {a.n} and one {CALIBRATION_FLOATS * 4} B copy done")
+
+
+def summarize_allreduce(kt_dir, fetch_dir, write_dir):
+    """Kernel time and HBM traffic of the worker (compress-only) and server launches."""
+    import numpy as np
+    from error_compensated_bit_amd import workloads as W
+    a = W.AllreduceWorkload()
+    stats = {_short(r["Name"]): r for r in _rows(kt_dir, "kernel_stats.csv")}
+    per = {}
+    for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in _rows(d, "counter_collection.csv"):
+            if r.get("Counter_Name") == key:
+                per.setdefault((key, _short(r["Kernel_Name"])), []).append(float(r["Counter_Value"]))
+    def counter(key, frag, how=np.median):
+        vals = [v for (k, name), vs in per.items() if k == key and frag in name for v in vs]
+        return float(how(vals)) if vals else None
+    cal = CALIBRATION_FLOATS * 4
+    f_scale = cal / (counter("FETCH_SIZE", "neg_kernel", np.max) * 1024.0)
+    w_scale = cal / (counter("WRITE_SIZE", "neg_kernel", np.max) * 1024.0)
+    out = [f"# Worker and server launches of the simulated all-reduce ({a.W} workers x {a.n} fp32, "
+           f"{len(a.chunk_off) - 1} chunks)", ""]
+    out.append("Commands (from the repository root, on one MI355X):")
+    out.append("```")
+    for d, extra in ((kt_dir, "--kernel-trace --stats"), (fetch_dir, "--pmc FETCH_SIZE"), (write_dir, "--pmc WRITE_SIZE")):
+        out.append(f"rocprofv3 {extra} --output-format csv -d {d} -o bench -- python3 bench.py --profile-allreduce")
+    out.append(f"python bench.py --summarize-allreduce {kt_dir} {fetch_dir} {write_dir}")
+    out.append("```")
+    out.append(f"Library source digest: {source_digest()}")
+    out.append("")
+    out.append(f"Counter scale from the plain {cal} B copy: FETCH_SIZE x{f_scale:.4f}, WRITE_SIZE x{w_scale:.4f}.  "
+               f"Algorithmic bytes per element: worker 16.125 (read g, m, e; write e, sign bits), server "
+               f"{a.W / 8 + 12.125:.3f} (read {a.W} workers' sign bits and the server error; write the server "
+               f"error, the decompressed momentum and the server's sign bits).")
+    out.append("")
+    out.append("| launch | calls | average ns | read bytes | written bytes | traffic / algorithmic | "
+               "algorithmic GB/s |")
+    out.append("|---|---|---|---|---|---|---|")
+    for label, frag, bpe in (("worker (compress-only)", "k_compress_onepass<1, ", 16.125),
+                             ("server", "k_compress_onepass<2, ", a.W / 8 + 12.125)):
+        key = next((k for k in stats if frag in k), None)
+        if key is None:
+            continue
+        ns = float(stats[key]["AverageNs"])
+        rd = counter("FETCH_SIZE", frag) * 1024.0 * f_scale
+        wr = counter("WRITE_SIZE", frag) * 1024.0 * w_scale
+        alg = bpe * a.n
+        out.append(f"| {label} | {stats[key]['Calls']} | {ns:.0f} | {rd:.0f} | {wr:.0f} | {(rd + wr) / alg:.4f} | "
+                   f"{alg / ns:.0f} |")
+    return "\n".join(out) + "\n"
+
+
 def _short(name):
     return name.split("(")[0].replace("void ", "").strip()
 
@@ -586,6 +671,8 @@ def main():
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-quantizers", action="store_true")
+    ap.add_argument("--profile-allreduce", action="store_true")
+    ap.add_argument("--summarize-allreduce", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-quantizers", nargs=2, metavar=("KT_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("KT_DIR", "COMMAND"))
     args = ap.parse_args()
@@ -598,8 +685,14 @@ def main():
     if args.summarize_quantizers:
         sys.stdout.write(summarize_quantizers(*args.summarize_quantizers))
         return
+    if args.summarize_allreduce:
+        sys.stdout.write(summarize_allreduce(*args.summarize_allreduce))
+        return
     if args.profile_quantizers:
         profile_quantizers()
+        return
+    if args.profile_allreduce:
+        profile_allreduce(max(1, min(args.steps, 3)))
         return
     if args.profile:
         profile_mode(max(1, min(args.steps, 5)))
