@@ -141,7 +141,9 @@ void onebit_set_spin_limit(uint32_t limit);
  * ONEBIT_PROFILE_CLASSES entries, nullable).  Classes: 0 warmup, 1/2/3 worker
  * compression pass 1 / one-pass / pass 2, 4 quantize, 5 dequantize, 6/7/8 server
  * pass 1 / one-pass / pass 2, 9 chunk-norm finalization of two-pass chunks, 10
- * momentum update, 11 QSGD quantize, 12 QSGD reduce, 13 LoCo quantize.  Not
+ * momentum update, 11 QSGD quantize, 12 QSGD reduce, 13 LoCo quantize.  A QSGD or
+ * LoCo call with buckets of 1024 and a ragged last bucket launches two kernels (whole
+ * buckets, then the last one) inside one bracket, counted as one launch.  Not
  * thread-safe; diagnostics only. */
 #define ONEBIT_PROFILE_CLASSES 14
 void onebit_profile_begin(void);
