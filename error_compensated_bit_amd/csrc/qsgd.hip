@@ -546,24 +546,31 @@ static int device_cus() {
     return cus;
 }
 
+// The launch status of the call's kernels (the first failure, if any).
 template <int BITS, int GT, bool LOCO>
-static void launch_quantize(const GArgs &a, unsigned grid, hipStream_t s) {
-    if (a.bucket == 1024) {
-        // grid covers the whole buckets; one more workgroup takes a ragged last one
-        if (a.n >= 1024) hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO, false>), dim3(grid), dim3(256), 0, s, a);
-        if (a.n % 1024) hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO, true>), dim3(1), dim3(256), 0, s, a);
-    } else
+static hipError_t launch_quantize(const GArgs &a, unsigned grid, hipStream_t s) {
+    if (a.bucket != 1024) {
         hipLaunchKernelGGL((k_qsgd_quantize_generic<BITS, GT, LOCO>), dim3(grid), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    // grid covers the whole buckets; one more workgroup takes a ragged last one
+    if (a.n >= 1024) {
+        hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO, false>), dim3(grid), dim3(256), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.n % 1024) {
+        hipLaunchKernelGGL((k_qsgd_quantize_1024<BITS, GT, LOCO, true>), dim3(1), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 template <int BITS, bool LOCO>
-static void launch_quantize_dt(const GArgs &a, onebit_dtype_t dt, unsigned grid, hipStream_t s) {
-    if (dt == ONEBIT_BF16)
-        launch_quantize<BITS, kGradBF16, LOCO>(a, grid, s);
-    else if (dt == ONEBIT_F16)
-        launch_quantize<BITS, kGradF16, LOCO>(a, grid, s);
-    else
-        launch_quantize<BITS, kGradF32, LOCO>(a, grid, s);
+static hipError_t launch_quantize_dt(const GArgs &a, onebit_dtype_t dt, unsigned grid, hipStream_t s) {
+    if (dt == ONEBIT_BF16) return launch_quantize<BITS, kGradBF16, LOCO>(a, grid, s);
+    if (dt == ONEBIT_F16) return launch_quantize<BITS, kGradF16, LOCO>(a, grid, s);
+    return launch_quantize<BITS, kGradF32, LOCO>(a, grid, s);
 }
 
 // Validation and launch shared by the plain and the LoCo quantizer.
@@ -595,16 +602,17 @@ static onebit_status_t quantize_entry(const void *g, onebit_dtype_t g_dtype, flo
     const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks);
     hipStream_t s = static_cast<hipStream_t>(stream);
     prof_before(err ? kProfLocoQuantize : kProfQsgdQuantize, s);
+    hipError_t e;
     if (bits == 4 && err)
-        launch_quantize_dt<4, true>(a, g_dtype, grid, s);
+        e = launch_quantize_dt<4, true>(a, g_dtype, grid, s);
     else if (bits == 4)
-        launch_quantize_dt<4, false>(a, g_dtype, grid, s);
+        e = launch_quantize_dt<4, false>(a, g_dtype, grid, s);
     else if (err)
-        launch_quantize_dt<8, true>(a, g_dtype, grid, s);
+        e = launch_quantize_dt<8, true>(a, g_dtype, grid, s);
     else
-        launch_quantize_dt<8, false>(a, g_dtype, grid, s);
+        e = launch_quantize_dt<8, false>(a, g_dtype, grid, s);
     prof_after(s);
-    return hip_status(hipGetLastError());
+    return hip_status(e);
 }
 
 template <int BITS>
