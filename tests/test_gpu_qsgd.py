@@ -231,6 +231,37 @@ def test_loco_parity(bucket, bits, beta, n):
             assert_exact(f"{tag} err_avg", host(ed), er)
 
 
+@pytest.mark.parametrize("n", [1023, 1024, 1025, 2048, 2049])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_bucket_1024_whole_and_last(n, bits):
+    """Buckets of 1024 go to two kernels (whole buckets, then a ragged last one):
+    sizes with only a last bucket, only whole ones, and both; plain and LoCo."""
+    rng = np.random.default_rng(n + bits)
+    for dt in ("f32", "bf16", "f16"):
+        g = special_gradient(n, rng)
+        if dt == "f16":
+            g = np.clip(g, -6e4, 6e4)
+        gd, gh = to_device(g, dt)
+        nb = (n + 1023) // 1024
+        codes = torch.full((code_bytes(n, bits) + 16,), 0xAB, dtype=torch.uint8, device=DEV)
+        norms = torch.zeros(nb, device=DEV)
+        ob.qsgd_quantize(gd, 1024, bits, 77 + n, codes, norms)
+        rc, rn = oracle.qsgd_quantize(gh, bucket=1024, bits=bits, seed=77 + n)
+        torch.cuda.synchronize()
+        tag = f"n {n} bits {bits} {dt}"
+        assert_exact(f"{tag} codes", host(codes)[:rc.size], rc)
+        assert (host(codes)[rc.size:] == 0xAB).all(), f"{tag}: bytes past the codes written"
+        assert_exact(f"{tag} norms", host(norms), rn)
+        e0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        ed, er = torch.from_numpy(e0.copy()).to(DEV), e0.copy()
+        ob.loco_quantize(gd, ed, 1024, bits, 0.5, 91 + n, codes, norms)
+        rc, rn = oracle.loco_quantize(gh, er, bucket=1024, bits=bits, beta=0.5, seed=91 + n)
+        torch.cuda.synchronize()
+        assert_exact(f"{tag} loco codes", host(codes)[:rc.size], rc)
+        assert_exact(f"{tag} loco norms", host(norms), rn)
+        assert_exact(f"{tag} loco err_avg", host(ed), er)
+
+
 def test_loco_argument_errors():
     g = torch.zeros(64, device=DEV)
     e = torch.zeros(64, device=DEV)
