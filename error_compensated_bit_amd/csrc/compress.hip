@@ -134,9 +134,19 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
         __syncthreads();  // previous batch fully consumed
         for (int w = threadIdx.x; w < wn; w += kBlock)
             s_wscale_d[w] = (double)a.wscales[(int64_t)(w0 + w) * a.n_chunks + t.chunk];
-        for (int k = threadIdx.x; k < wn * kTileWords; k += kBlock) {
-            const int w = k / kTileWords, i = k % kTileWords;
-            s_words[k] = i < nwords ? a.wbits[(int64_t)(w0 + w) * a.plan_words + t.word + i] : 0u;
+        // a full batch of a full tile with 16-byte aligned rows: one 16-byte load per
+        // thread (thread k takes words 4k..4k+3 of the batch), else one word each
+        const bool vec = kWBatch * kTileWords == 4 * kBlock && full && wn == kWBatch &&
+                         (((uintptr_t)a.wbits | (uintptr_t)a.plan_words * 4u | (uintptr_t)t.word * 4u) & 15u) == 0;
+        if (vec) {
+            const int w = threadIdx.x / (kTileWords / 4), i = 4 * (threadIdx.x % (kTileWords / 4));
+            reinterpret_cast<uint4 *>(s_words)[threadIdx.x] =
+                *reinterpret_cast<const uint4 *>(a.wbits + (int64_t)(w0 + w) * a.plan_words + t.word + i);
+        } else {
+            for (int k = threadIdx.x; k < wn * kTileWords; k += kBlock) {
+                const int w = k / kTileWords, i = k % kTileWords;
+                s_words[k] = i < nwords ? a.wbits[(int64_t)(w0 + w) * a.plan_words + t.word + i] : 0u;
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -621,7 +631,7 @@ __global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepa
     __shared__ uint32_t s_u32[2];
     __shared__ double s_total;
     __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
-    __shared__ uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
+    __shared__ __align__(16) uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int G = (int)gridDim.x;
     // Workgroups are dispatched to the eight XCDs in turn; outside the server stage
     // the ones on one XCD take consecutive list positions (one-pass BERT-Large step
@@ -672,7 +682,7 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     __shared__ uint32_t s_u32[2];
     __shared__ double s_total;
     __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
-    __shared__ uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
+    __shared__ __align__(16) uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int tile_id = a.list[blockIdx.x];
     const TileDesc t = a.tiles[tile_id];
     float c[kPerThread];
