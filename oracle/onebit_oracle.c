@@ -62,10 +62,15 @@
  *  - QSGD: per bucket the L2 norm (same fp64 sum, sqrt in fp64, one rounding to
  *    fp32); s = 2^(bits-1) - 1 levels of |g| / norm; code = sign bit (top bit of
  *    the code, set iff g < 0) and the level below it; same Philox stream layout as
- *    the weights (the caller picks a different seed); dequantized value
- *    level * fl32(norm / s) (exact in fp64), negated for a set sign bit; several
- *    workers' values are averaged as the server stage does (fp64 sum in worker
- *    order, fp64 divide by W, one rounding to fp32).
+ *    the weights (the caller picks a different seed); the dequantized value is
+ *    the real number +-level * norm / s, and the average of W workers' values is
+ *    (sum_w +-level_w * norm_w) / (s * W): each product level * norm is exact in
+ *    fp64 (7 + 24 significant bits), the products are summed in fp64 in worker
+ *    order, divided once by s * W in fp64 and rounded once to fp32.  Whenever
+ *    that fp64 sum is exact the result is the exact average rounded once to fp32
+ *    (the fp64 quotient cannot straddle a binary32 rounding boundary); the sum is
+ *    exact for W = 1, and whenever W * 2^(31 + d) <= 2^53 with d the spread of the
+ *    exponents of the W norms of the bucket (e.g. W <= 16 and d <= 18).
  */
 #include <math.h>
 #include <stddef.h>
@@ -614,22 +619,22 @@ int oracle_qsgd_quantize(const void *g, int g_dtype, int64_t n, int bucket, int 
     return ORACLE_OK;
 }
 
-/* The value worker w sent for element i: level times the bucket's level spacing,
- * exact in fp64 (at most 7 + 24 significant bits). */
-static double qsgd_value(const uint8_t *codes, const float *norms, int64_t i, int bucket, int nbits)
+/* The value worker w sent for element i, times s: +-level * norm, exact in fp64
+ * (at most 7 + 24 significant bits). */
+static double qsgd_value_times_s(const uint8_t *codes, const float *norms, int64_t i, int bucket, int nbits)
 {
     const uint32_t s = (1u << (nbits - 1)) - 1u;
     const uint32_t code = nbits == 8 ? codes[i] : (uint32_t)((codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu);
     const uint32_t level = code & s;
-    const float step = norms[i / bucket] / (float)s; /* the bucket's level spacing */
-    const double y = (double)level * (double)step;
+    const double y = (double)level * (double)norms[i / bucket];
     return (code >> (nbits - 1)) ? -y : y;
 }
 
-/* [QSGD] decoding (value = level * norm / s, formed exactly as level times the
- * bucket's level spacing fl32(norm / s)), averaged over W workers' streams (the reduce half of a quantized
- * gradient reduce-scatter): out_i = fl32( (sum_w y_{w,i}) / W ), fp64 sum in worker
- * order.  Worker w's codes start at codes + w * code_stride bytes, its norms at
+/* [QSGD] sec. 3.1 decoding: worker w's value is +-level_w * norm_w / s, averaged
+ * over W workers' streams (the reduce half of a quantized gradient
+ * reduce-scatter): out_i = fl32( (sum_w +-level_w * norm_w) / (s * W) ), the exact
+ * products summed in fp64 in worker order, one fp64 division, one rounding to
+ * fp32.  Worker w's codes start at codes + w * code_stride bytes, its norms at
  * norms + w * norm_stride.  W = 1 is plain dequantization. */
 int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const float *norms, int64_t norm_stride,
                        int64_t n, int bucket, int nbits, float *out_f32, uint16_t *out_bf16)
@@ -640,12 +645,13 @@ int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const f
         return ORACLE_OK;
     if (!codes || !norms || (!out_f32 && !out_bf16))
         return ORACLE_ERR_INVALID;
+    const double sW = (double)((1u << (nbits - 1)) - 1u) * (double)W;
     for (int64_t i = 0; i < n; ++i) {
         double acc = 0.0;
         for (int w = 0; w < W; ++w)
-            acc += qsgd_value(codes + (int64_t)w * code_stride, norms + (int64_t)w * norm_stride, i, bucket,
+            acc += qsgd_value_times_s(codes + (int64_t)w * code_stride, norms + (int64_t)w * norm_stride, i, bucket,
                                       nbits);
-        const float y = (float)(acc / (double)W);
+        const float y = (float)(acc / sW);
         if (out_f32)
             out_f32[i] = y;
         if (out_bf16)
@@ -659,7 +665,7 @@ int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const f
  * average of past errors, add it to the gradient, compress the sum.  Reading
  * (binary32, unfused; beta and 1 - beta formed in binary64, rounded once):
  *   h = fl32(g + err_avg);  (codes, norms) = QSGD of h, as O7;  y = decoded h as
- *   the W = 1 decode of O7;  err_avg = fl32( fl32(beta * err_avg) + fl32((1 - beta) * (h - y)) ).
+ *   the W = 1 decode of O7 (fl32(+-level * norm / s));  err_avg = fl32( fl32(beta * err_avg) + fl32((1 - beta) * (h - y)) ).
  * beta = 0 is plain error feedback (err_avg = h - y).  err_avg: fp32 [n] in place.
  * first_index: global index of g[0], as in O7.
  */

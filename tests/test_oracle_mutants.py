@@ -60,6 +60,9 @@ def _qsgd():
     TG.test_norm_is_the_rounded_exact_norm()
     TG.test_unbiased_and_variance_closed_form(4)
     TG.test_average_of_workers()
+    TG.test_decode_is_exact_average_rounded_once(8, 1, 0)
+    TG.test_decode_is_exact_average_rounded_once(4, 3, 18)
+    TG.test_lone_value_decodes_to_itself_over_the_whole_range()
 
 
 def _loco():
@@ -107,13 +110,18 @@ MUTANTS = [
     ("qsgd s + 1 levels", "const float u = t * (float)s;", "const float u = t * (float)(s + 1);", _qsgd),
     ("qsgd norm not square-rooted", "const float norm = (float)sqrt(bucket_sum_squares(v, len));",
      "const float norm = (float)bucket_sum_squares(v, len);", _qsgd),
-    ("qsgd decode scale", "const float step = norms[i / bucket] / (float)s;",
-     "const float step = norms[i / bucket] / (float)(s + 1);", _qsgd),
+    ("qsgd decode scale", "const double sW = (double)((1u << (nbits - 1)) - 1u) * (double)W;",
+     "const double sW = (double)(1u << (nbits - 1)) * (double)W;", _qsgd),
+    ("qsgd level spacing rounded to fp32 first", "(double)level * (double)norms[i / bucket];",
+     "(double)level * (double)(norms[i / bucket] / (float)s) * (double)s;", _qsgd),
+    ("qsgd level times norm rounded to fp32", "            acc += qsgd_value_times_s(",
+     "            acc += (double)(float)qsgd_value_times_s(", _qsgd),
     ("qsgd pack nibble order", "codes[i >> 1] |= (uint8_t)((i & 1) ? code << 4 : code);",
      "codes[i >> 1] |= (uint8_t)((i & 1) ? code : code << 4);", _qsgd),
     ("qsgd decode nibble order", "(uint32_t)((codes[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xfu)",
      "(uint32_t)((codes[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xfu)", _qsgd),
-    ("qsgd average not divided", "const float y = (float)(acc / (double)W);", "const float y = (float)acc;", _qsgd),
+    ("qsgd average not divided", "const float y = (float)(acc / sW);", "const float y = (float)(acc / (sW / (double)W));",
+     _qsgd),
     ("loco compensation sign", "h[i] = gi + err_avg[i];", "h[i] = gi - err_avg[i];", _loco),
     ("loco weights swapped", "err_avg[i] = beta * err_avg[i] + one_minus_beta * (h[i] - y[i]);",
      "err_avg[i] = one_minus_beta * err_avg[i] + beta * (h[i] - y[i]);", _loco),

@@ -6,14 +6,22 @@ sec. 3.1: Q_s(v_i) = ||v||_2 sgn(v_i) xi_i / s with xi_i in {l, l + 1}, rounding
 with probability |v_i| s / ||v||_2 - l, so E[Q_s(v)] = v and the variance of one
 coordinate is (||v|| / s)^2 p (1 - p).
 
+Decoding reading: a code stands for the real number +-level * ||v|| / s, and the
+average of W workers' values is the real number (sum_w +-level_w ||v_w||) / (s W);
+the decoded fp32 value is that number rounded once (round to nearest even).
+
 Pinned without retyping the oracle's steps: buckets whose ratios |v_i| s / ||v|| are
 integers (Pythagorean-style vectors) must come out exactly and independently of the
-seed; a lone non-zero goes to the top level; the norm equals math.fsum in exact
-arithmetic; over 4096 seeds the decoded mean is within 6 sigma of v and the mean
-squared error matches the closed form; the round-up frequency of each element
-matches its p; averaging a stream with its sign-flipped copy gives exactly 0.
+seed; a lone non-zero goes to the top level and decodes to itself, for values over
+the whole binary32 range; arbitrary codes and norms decode (W = 1) and average
+(W = 2 ... 16) to the exact rational value rounded once to binary32, computed with
+fractions.Fraction; the norm equals math.fsum in exact arithmetic; over 4096 seeds
+the decoded mean is within 6 sigma of v and the mean squared error matches the
+closed form; the round-up frequency of each element matches its p; averaging a
+stream with its sign-flipped copy gives exactly 0.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -30,6 +38,37 @@ def unpack4(codes, n):
 
 def to_bf16_bits(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def rn32(q):
+    """The binary32 number nearest the rational q (ties to even), as float32."""
+    if q == 0:
+        return np.float32(0.0)
+    neg, a = q < 0, abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()      # 2^e <= a < 2^(e+2)
+    if a >= Fraction(2) ** (e + 1):
+        e += 1
+    if a < Fraction(2) ** e:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, -126) - 23)                        # subnormal spacing below 2^-126
+    m, rem = divmod(a, ulp)
+    m = int(m)
+    if rem > ulp / 2 or (rem == ulp / 2 and m % 2 == 1):
+        m += 1
+    v = Fraction(m) * ulp
+    if v >= Fraction(2) ** 128:
+        return np.float32(-np.inf if neg else np.inf)
+    return np.float32(-float(v) if neg else float(v))
+
+
+def test_rn32_helper_against_numpy_on_exact_doubles():
+    # on fp64 inputs numpy's float32 conversion is a single rounding: the helper must agree
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(4000) * 2.0 ** rng.integers(-160, 127, 4000)
+    for v in x[np.abs(x) < 2.0 ** 127]:
+        assert rn32(Fraction(float(v))) == np.float32(v)
+    assert rn32(Fraction(3, 2 ** 150)) == np.float32(2.0 ** -148)   # tie between 1 and 2 subnormal steps: even
+    assert rn32(Fraction(1, 2 ** 150)) == np.float32(0.0)             # half the smallest step: ties to 0
 
 
 @pytest.mark.parametrize("as_bf16", [False, True])
@@ -70,6 +109,52 @@ def test_lone_value_zero_bucket_signed_zero_and_padding():
         ref[2], ref[12] = big, tiny
         np.testing.assert_array_equal(y, ref)
         assert not np.signbit(y[8]) and not np.signbit(y[10])     # -0 is sent as +0
+
+
+def random_norms(rng, W, nb, spread):
+    """[W, nb] float32 norms: per bucket a base exponent over the binary32 range, each
+    worker within `spread` binary orders of it (subnormal norms included)."""
+    base = rng.integers(-150, 100, nb)
+    e = base[None, :] + rng.integers(0, spread + 1, (W, nb))
+    sig = rng.uniform(1.0, 2.0, (W, nb))
+    return np.ldexp(sig, e).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("W,spread", [(1, 0), (1, 200), (2, 18), (3, 18), (5, 18), (8, 18), (16, 18)])
+def test_decode_is_exact_average_rounded_once(bits, W, spread):
+    rng = np.random.default_rng(100 * W + bits + spread)
+    s = 2 ** (bits - 1) - 1
+    bucket, nb = 16, 24
+    n = bucket * nb - 5                                   # ragged last bucket, odd n
+    nbytes = (n + 1) // 2 if bits == 4 else n
+    codes = rng.integers(0, 256, (W, nbytes), dtype=np.uint8)   # every byte is a valid code (pair)
+    if bits == 4:
+        codes[:, -1] &= 0x0F                               # pad nibble
+    norms = random_norms(rng, W, nb, min(spread, 60))
+    y, _ = oracle.qsgd_reduce(codes, norms, n, bucket=bucket, bits=bits)
+    lv = np.stack([(unpack4(c, n) if bits == 4 else c[:n]) for c in codes]).astype(np.int64)
+    for i in range(n):
+        exact = sum(((-1) ** int(lv[w, i] >> (bits - 1))) * int(lv[w, i] & s) * Fraction(float(norms[w, i // bucket]))
+                    for w in range(W)) / (s * W)
+        assert y[i] == rn32(exact), (i, W, y[i], rn32(exact))
+
+
+def test_lone_value_decodes_to_itself_over_the_whole_range():
+    # one non-zero value v in a bucket: norm = |v|, level = s, decoded value s |v| / s = v
+    rng = np.random.default_rng(21)
+    k = 3000
+    v = (rng.choice([-1.0, 1.0], k) * np.ldexp(rng.uniform(1.0, 2.0, k), rng.integers(-149, 127, k))).astype(np.float32)
+    v = v[v != 0]
+    bucket = 4
+    g = np.zeros(bucket * v.size, np.float32)
+    pos = rng.integers(0, bucket, v.size)
+    g[np.arange(v.size) * bucket + pos] = v
+    for bits in (4, 8):
+        codes, norms = oracle.qsgd_quantize(g, bucket=bucket, bits=bits, seed=5)
+        np.testing.assert_array_equal(norms, np.abs(v))
+        y, _ = oracle.qsgd_reduce(codes, norms, g.size, bucket=bucket, bits=bits)
+        np.testing.assert_array_equal(y, g)
 
 
 def test_norm_is_the_rounded_exact_norm():
