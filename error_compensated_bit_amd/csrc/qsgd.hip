@@ -9,6 +9,9 @@
 // fp64 square root, one rounding to fp32); s = 2^(bits-1) - 1 levels of |g|/norm,
 // rounded up at random with probability equal to the fractional part, so the
 // decoded value norm * level / s carries the sign of g and has expectation g.
+// Decoding rounds that real value once: the product level * norm is exact in fp64,
+// W workers' products are summed in fp64 in worker order, divided once by s * W
+// (correctly rounded) and rounded once to fp32.
 // Codes: sign bit on top, level below; 4-bit codes two per byte (even element
 // low).  Random words: Philox4x32-10 keyed by the seed, counter = element index
 // / 4, word = element index % 4 -- the weights' layout; the caller gives the
@@ -53,14 +56,29 @@ __device__ __forceinline__ uint32_t qsgd_code(float g, float norm, double rnorm,
     return (g < 0.0f ? (1u << (BITS - 1)) : 0u) | level;
 }
 
-// LoCo: the new moving average of the compression error, from the old one, the
-// compensated value h, its code and the bucket's level spacing (decode as the
-// W = 1 average: +-fl32(level * spacing)).
-template <int BITS>
-__device__ __forceinline__ float loco_update(const GArgs &a, float ea, float h, uint32_t code, float step) {
+// The decoded value of one code, times s, added to acc: +-level * norm is exact in
+// fp64 (at most 7 + 24 significant bits), so one fused multiply-add is the fp64 sum
+// of the exact product.  The code sits at bit P of the 32-bit word w; its sign bit
+// goes straight into the sign of the converted level (the level's own sign bit is 0).
+template <int BITS, int P>
+__device__ __forceinline__ double qsgd_accumulate(double acc, uint32_t w, double norm) {
     constexpr uint32_t S = (1u << (BITS - 1)) - 1u;
-    const float y = mul_rn((float)(code & S), step);
-    const float err = sub_rn(h, (code >> (BITS - 1)) ? -y : y);
+    constexpr uint32_t SIGN = 1u << (P + BITS - 1);
+    const double lv = (double)((w >> P) & S);
+    const uint32_t hi = (uint32_t)(__double_as_longlong(lv) >> 32) | ((w & SIGN) << (32 - BITS - P));
+    const double slv = __hiloint2double((int)hi, (int)(uint32_t)__double_as_longlong(lv));
+    return __fma_rn(slv, norm, acc);
+}
+
+// LoCo: the new moving average of the compression error, from the old one, the
+// compensated value h, its code and the bucket's norm.  The decode is the W = 1
+// average: fl32((0 + +-level * norm) / s).
+template <int BITS>
+__device__ __forceinline__ float loco_update(const GArgs &a, float ea, float h, uint32_t code, float norm) {
+    constexpr double S = (double)((1u << (BITS - 1)) - 1u);
+    constexpr double RS = 1.0 / S;   // correctly rounded at compile time
+    const float y = (float)div_rn64(qsgd_accumulate<BITS, 0>(0.0, code, (double)norm), S, RS);
+    const float err = sub_rn(h, y);
     return add_rn(mul_rn(a.beta, ea), mul_rn(a.obeta, err));
 }
 
@@ -145,7 +163,6 @@ __device__ __forceinline__ void quantize_whole_bucket(const GArgs &a, int64_t b,
     const float norm = norm_of(acc);
     const double rnorm = recip_rn64(norm);
     if (lane == 0) a.norms[b] = norm;
-    const float st = __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
     uint32_t code[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -160,7 +177,7 @@ __device__ __forceinline__ void quantize_whole_bucket(const GArgs &a, int64_t b,
         if (LOCO) {
             float en[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) en[q] = loco_update<BITS>(a, e[q], h[q], code[4 * j + q], st);
+            for (int q = 0; q < 4; ++q) en[q] = loco_update<BITS>(a, e[q], h[q], code[4 * j + q], norm);
             we[4 * lane + j] = make_float4(en[0], en[1], en[2], en[3]);
         }
     }
@@ -290,9 +307,8 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
         for (int q = 0; q < 16; ++q)
             if (k0 + q >= len) code[q] = 0;
         if (LOCO) {
-            const float st = __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
 #pragma unroll
-            for (int q = 0; q < 16; ++q) ea[q] = loco_update<BITS>(a, ea[q], f[q], code[q], st);
+            for (int q = 0; q < 16; ++q) ea[q] = loco_update<BITS>(a, ea[q], f[q], code[q], norm);
             if (k0 + 15 < len) {
                 float4 *dst = reinterpret_cast<float4 *>(a.err + base + k0);
 #pragma unroll
@@ -331,7 +347,6 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
         const float norm = norm_of(acc);
         const double rnorm = recip_rn64(norm);
         if (lane == 0) a.norms[b] = norm;
-        const float st = LOCO ? __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u)) : 0.0f;
         const int step = BITS == 4 ? 2 : 1;
         for (int k = step * lane; k < len; k += 64 * step) {
             uint32_t byte = 0;
@@ -342,7 +357,7 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_generic(GArgs a) {
                 const uint32_t w = (i & 3) == 0 ? r.a : (i & 3) == 1 ? r.b : (i & 3) == 2 ? r.c : r.d;
                 const float h = value_at<GT, LOCO>(a, i);
                 const uint32_t code = qsgd_code<BITS>(h, norm, rnorm, w);
-                if (LOCO) a.err[i] = loco_update<BITS>(a, a.err[i], h, code, st);
+                if (LOCO) a.err[i] = loco_update<BITS>(a, a.err[i], h, code, norm);
                 byte |= code << (4 * q);
             }
             a.codes[BITS == 4 ? ((base + k) >> 1) : (base + k)] = (uint8_t)byte;
@@ -361,27 +376,8 @@ struct RArgs {
     int32_t W;
     float *out_f32;
     uint16_t *out_bf16;
-    double invW;  // 1 / W, exact when W is a power of two
+    double sw, rsw;  // s * W and RN64(1 / (s * W))
 };
-
-// Level spacing of a bucket.
-template <int BITS>
-__device__ __forceinline__ float level_step(float norm) {
-    return __fdiv_rn(norm, (float)((1u << (BITS - 1)) - 1u));
-}
-// acc + (+-level * step): the product is exact in fp64 (at most 7 + 24 significant
-// bits), so one fused multiply-add is the fp64 sum of the exact decoded value.
-// The code sits at bit P of the 32-bit word w; its sign bit goes straight into the
-// sign of the converted level (the level's own sign bit is 0).
-template <int BITS, int P>
-__device__ __forceinline__ double qsgd_accumulate(double acc, uint32_t w, double step) {
-    constexpr uint32_t S = (1u << (BITS - 1)) - 1u;
-    constexpr uint32_t SIGN = 1u << (P + BITS - 1);
-    const double lv = (double)((w >> P) & S);
-    const uint32_t hi = (uint32_t)(__double_as_longlong(lv) >> 32) | ((w & SIGN) << (32 - BITS - P));
-    const double slv = __hiloint2double((int)hi, (int)(uint32_t)__double_as_longlong(lv));
-    return __fma_rn(slv, step, acc);
-}
 
 // The 16 codes of one load (8 bytes of 4-bit codes, 16 bytes of 8-bit codes),
 // unrolled with compile-time bit positions.
@@ -405,12 +401,8 @@ struct Accumulate16<8, 16> {
     __device__ __forceinline__ static void run(double (&)[16], const uint32_t (&)[4], const double (&)[16]) {}
 };
 
-// The mean over W: a product with the exact reciprocal when W is a power of two
-// (the same value as the quotient), the quotient otherwise.
-template <bool POW2>
-__device__ __forceinline__ float mean_of(double acc, double Wd, double invW) {
-    return (float)(POW2 ? __dmul_rn(acc, invW) : __ddiv_rn(acc, Wd));
-}
+// The mean over W: the fp64 sum of the products divided once by s * W, rounded once.
+__device__ __forceinline__ float mean_of(const RArgs &a, double acc) { return (float)div_rn64(acc, a.sw, a.rsw); }
 
 __device__ __forceinline__ void store_out(const RArgs &a, int64_t i, float y) {
     if (a.out_f32) a.out_f32[i] = y;
@@ -419,14 +411,13 @@ __device__ __forceinline__ void store_out(const RArgs &a, int64_t i, float y) {
 
 // E = 16 consecutive elements per thread and iteration: one 8-byte (4-bit codes) or
 // 16-byte (8-bit) load of every worker's row, 16 fp64 sums live per thread.  With
-// the bucket a multiple of E the E elements share one norm (one level spacing) per
-// worker.  Sum over workers in fp64, in worker order.  The results of a wave (1024
+// the bucket a multiple of E the E elements share one norm per worker.  Sum over workers in fp64, in worker order.  The results of a wave (1024
 // consecutive elements) pass through LDS so that every store instruction writes one
 // contiguous run (1 KiB of fp32 or bf16), with the streaming cache policy; the waves
 // step through the vector together, so every lane takes part in the exchange.
 constexpr int kBatch = 4;
 
-template <int BITS, bool SHARED_NORM, bool POW2>
+template <int BITS, bool SHARED_NORM>
 __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
     constexpr int E = kReduceE;
     constexpr int NW = BITS / 2;   // 32-bit words per load
@@ -434,7 +425,6 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
     float4 *const sw = s_out[threadIdx.x >> 6];
     const int lane = threadIdx.x & 63;
     const int64_t groups = a.n / E;
-    const double Wd = (double)a.W;
     for (int64_t q0 = blockIdx.x * (int64_t)blockDim.x + (threadIdx.x & ~63); q0 < groups;
          q0 += (int64_t)gridDim.x * blockDim.x) {
         const int64_t q = q0 + lane;
@@ -475,13 +465,13 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
                     for (int h = 0; h < NW; ++h) ws[h] = word[j][h];
                     double sk[E];
                     if (SHARED_NORM) {
-                        const double st = (double)level_step<BITS>(nm[j]);
+                        const double st = (double)nm[j];
 #pragma unroll
                         for (int k = 0; k < E; ++k) sk[k] = st;
                     } else {
                         const float *nrow = a.norms + (int64_t)(w0 + j) * a.norm_stride;
 #pragma unroll
-                        for (int k = 0; k < E; ++k) sk[k] = (double)level_step<BITS>(nrow[(i0 + k) / a.bucket]);
+                        for (int k = 0; k < E; ++k) sk[k] = (double)nrow[(i0 + k) / a.bucket];
                     }
                     Accumulate16<BITS>::run(acc, ws, sk);
                 }
@@ -489,7 +479,7 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
         }
         float y[E];
 #pragma unroll
-        for (int k = 0; k < E; ++k) y[k] = mean_of<POW2>(acc[k], Wd, a.invW);
+        for (int k = 0; k < E; ++k) y[k] = mean_of(a, acc[k]);
         // store h of a lane covers the wave's elements 4 (64 h + lane) .. +3 (fp32) or
         // 8 (64 h + lane) .. +7 (bf16), computed by lane 16 h + lane / 4 or 32 h + lane / 2
         if (a.out_f32) {
@@ -530,10 +520,9 @@ __global__ __launch_bounds__(256) void k_qsgd_reduce(RArgs a) {
         for (int w = 0; w < a.W; ++w) {
             const uint8_t *row = a.codes + (int64_t)w * a.code_stride;
             const uint32_t c = BITS == 4 ? (uint32_t)(row[i >> 1] >> ((i & 1) * 4)) & 15u : (uint32_t)row[i];
-            const double st = (double)level_step<BITS>(a.norms[(int64_t)w * a.norm_stride + i / a.bucket]);
-            acc = qsgd_accumulate<BITS, 0>(acc, c, st);
+            acc = qsgd_accumulate<BITS, 0>(acc, c, (double)a.norms[(int64_t)w * a.norm_stride + i / a.bucket]);
         }
-        store_out(a, i, mean_of<POW2>(acc, Wd, a.invW));
+        store_out(a, i, mean_of(a, acc));
     }
 }
 
@@ -616,15 +605,11 @@ static onebit_status_t quantize_entry(const void *g, onebit_dtype_t g_dtype, flo
 }
 
 template <int BITS>
-static void launch_reduce(const RArgs &a, bool shared, bool pow2, unsigned grid, hipStream_t s) {
-    if (shared && pow2)
-        hipLaunchKernelGGL((k_qsgd_reduce<BITS, true, true>), dim3(grid), dim3(256), 0, s, a);
-    else if (shared)
-        hipLaunchKernelGGL((k_qsgd_reduce<BITS, true, false>), dim3(grid), dim3(256), 0, s, a);
-    else if (pow2)
-        hipLaunchKernelGGL((k_qsgd_reduce<BITS, false, true>), dim3(grid), dim3(256), 0, s, a);
+static void launch_reduce(const RArgs &a, bool shared, unsigned grid, hipStream_t s) {
+    if (shared)
+        hipLaunchKernelGGL((k_qsgd_reduce<BITS, true>), dim3(grid), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((k_qsgd_reduce<BITS, false, false>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_qsgd_reduce<BITS, false>), dim3(grid), dim3(256), 0, s, a);
 }
 
 }  // namespace onebit
@@ -672,14 +657,14 @@ extern "C" onebit_status_t qsgd_reduce(int W, const uint8_t *codes, int64_t code
     if (blocks > cap) blocks = cap;
     const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    a.invW = 1.0 / (double)W;
+    a.sw = (double)((1u << (bits - 1)) - 1u) * (double)W;
+    a.rsw = 1.0 / a.sw;
     const bool shared = bucket % kReduceE == 0;
-    const bool pow2 = (W & (W - 1)) == 0;
     prof_before(kProfQsgdReduce, s);
     if (bits == 4)
-        launch_reduce<4>(a, shared, pow2, grid, s);
+        launch_reduce<4>(a, shared, grid, s);
     else
-        launch_reduce<8>(a, shared, pow2, grid, s);
+        launch_reduce<8>(a, shared, grid, s);
     prof_after(s);
     return hip_status(hipGetLastError());
 }

@@ -20,4 +20,16 @@ __device__ __forceinline__ double recip_rn64(float b) { return __ddiv_rn(1.0, (d
 
 __device__ __forceinline__ float div_by_recip(float a, double rb) { return (float)__dmul_rn((double)a, rb); }
 
+// RN64(a / d) for fp64 a and finite d > 0, given rd = RN64(1 / d), with one product
+// and two fused multiply-adds instead of the fp64 division sequence: q = RN(a rd) is
+// within one ulp of a / d, the residual a - d q is exact in one fma, and q + res rd
+// rounded once is the correctly rounded quotient (Markstein's theorem; no fp64
+// underflow or overflow can occur for the decode's finite operands).  An infinite
+// or NaN a gives a NaN residual; q itself (+-inf or NaN) is then the quotient.
+__device__ __forceinline__ double div_rn64(double a, double d, double rd) {
+    const double q = __dmul_rn(a, rd);
+    const double res = __fma_rn(-q, d, a);
+    return __builtin_isfinite(res) ? __fma_rn(res, rd, q) : q;
+}
+
 }  // namespace onebit

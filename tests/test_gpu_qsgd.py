@@ -6,7 +6,8 @@ Small cases cover the 1024-element fast path and the generic path (bucket sizes
 bf16 / fp16 gradients, zero and single-value buckets, signed zeros, buckets whose
 ratios are exact levels, and a wide dynamic range.  The reduce covers W = 1, 2,
 3, 8, buckets that are and are not multiples of 8, n not a multiple of 8, fp32
-and bf16 outputs, padded worker rows.  Full size: the 1.3e9-parameter gradient of
+and bf16 outputs, padded worker rows, and arbitrary codes with norms over the whole
+binary32 range (W = 1, 5, 16, 33).  Full size: the 1.3e9-parameter gradient of
 8 workers, bucket 1024, sampled buckets of every worker and sampled buckets of two
 shards' averages (the first and the ragged last).
 """
@@ -144,6 +145,52 @@ def test_reduce_parity(workers, bucket, bits, n):
     assert_exact(f"{tag} codes", host(codes), np.stack(rcs))
     assert_exact(f"{tag} mean", host(y), ry)
     check_bf16(f"{tag} mean bf16", host(yb), ryb)
+
+
+@pytest.mark.parametrize("workers", [1, 5, 16, 33])
+@pytest.mark.parametrize("bucket,bits", [(1024, 4), (1024, 8), (30, 4), (16, 8)])
+def test_reduce_arbitrary_codes_and_norms(workers, bucket, bits):
+    """Every byte pattern is a valid code (pair); norms span the finite binary32
+    range, subnormals included, with up to 60 binary orders between workers of a
+    bucket: the decode is the fp64 sum of exact level * norm products, one division
+    by s * W, one rounding.  A last run makes one worker's norm of one bucket
+    infinite: +-inf where every worker's level there is non-zero with one sign, NaN
+    where the sum meets opposite infinities or a level 0 meets the infinite norm."""
+    rng = np.random.default_rng(7 * workers + bits + bucket)
+    n = 5 * 1024 + 16 * 37 + 9
+    nb = (n + bucket - 1) // bucket
+    cb = code_bytes(n, bits)
+    stride = (cb + 15) // 16 * 16
+    c = rng.integers(0, 256, (workers, stride), dtype=np.uint8)
+    if bits == 4:
+        c[:, cb - 1] &= 0x0F                               # pad nibble of the odd tail
+    c[:, cb:] = 0
+    base = rng.integers(-150, 67, nb)
+    e = base[None, :] + rng.integers(0, 61, (workers, nb))       # norms below 2^127
+    nm = np.ldexp(rng.uniform(1.0, 2.0, (workers, nb)), e).astype(np.float32)
+    nm[:, 1] = 0.0                                         # a zero bucket
+    codes = torch.from_numpy(c).to(DEV)
+    norms = torch.from_numpy(nm).to(DEV)
+    y = torch.zeros(n, device=DEV)
+    yb = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    ob.qsgd_reduce(codes, norms, n, bucket, bits, out_f32=y, out_bf16=yb)
+    ry, ryb = oracle.qsgd_reduce(c, nm, n, bucket=bucket, bits=bits, want_bf16=True)
+    torch.cuda.synchronize()
+    tag = f"arbitrary codes W={workers} bucket {bucket} bits {bits}"
+    say(tag)
+    assert np.all(np.isfinite(nm))
+    assert_exact(f"{tag} mean", host(y), ry)
+    check_bf16(f"{tag} mean bf16", host(yb), ryb)
+    nm[workers // 2, 2] = np.inf
+    norms.copy_(torch.from_numpy(nm))
+    ob.qsgd_reduce(codes, norms, n, bucket, bits, out_f32=y)
+    ry, _ = oracle.qsgd_reduce(c, nm, n, bucket=bucket, bits=bits)
+    torch.cuda.synchronize()
+    got = host(y)
+    nan = np.isnan(ry)
+    assert np.array_equal(np.isnan(got), nan), f"{tag} infinite norm: NaN positions differ"
+    assert_exact(f"{tag} infinite norm, non-NaN values", got[~nan], ry[~nan])
+    assert np.isinf(ry).any() or nan.any()
 
 
 def test_argument_errors():
