@@ -11,10 +11,11 @@
 // How: the flat vector is cut into tiles of 2048 elements (256 threads x 8).
 // A tile computes its c, writes its sign words, and posts its fp64 partial sum
 // of squares.  The chunk scale needs every tile of the chunk, so
-//  - chunks of at most 2R tiles (R = co-resident workgroups) are done in ONE pass
-//    by a cooperative persistent kernel: each tile parks c in LDS, waits for its
-//    chunk's scale while the next tile streams, then finishes -- HBM sees each
-//    input once and each output once;
+//  - chunks of at most 3R tiles (R = co-resident workgroups) are done in ONE pass
+//    by a persistent kernel whose grid is at most R workgroups, so that every
+//    workgroup is resident: each tile parks c in LDS, waits for its chunk's scale
+//    while the next tiles stream, then finishes -- HBM sees each input once and
+//    each output once;
 //  - larger chunks take two passes: pass 1 stores c in place of e, pass 2 reads it
 //    back with v and x once the chunk scale is known.
 // Cross-workgroup communication uses only single-location relaxed agent-scope
@@ -22,6 +23,8 @@
 // {epoch, scale}); no cache-wide write-back or invalidate is ever needed, and a
 // zeroed workspace is always ready for the next call.
 #include <math.h>
+
+#include <atomic>
 
 #include "device_common.h"
 #include "internal.h"
@@ -77,8 +80,12 @@ struct CompressArgs {
 // of any workgroup spins again, so a kernel always drains in bounded time.
 constexpr uint32_t kSpinLimit = 1u << 20;
 // Limit used by the next launches (diagnostics can lower it to exercise the
-// failure path; a wait that gives up records an error in the workspace).
-static uint32_t g_spin_limit = kSpinLimit;
+// failure path; a wait that gives up records an error in the workspace).  Atomic:
+// any host thread may set it while others launch.
+static std::atomic<uint32_t> g_spin_limit{kSpinLimit};
+// Diagnostic cap on the one-pass grid (0 = none): lets the tests run the chunk-norm
+// exchange with fewer resident workgroups than the device holds.
+static std::atomic<int32_t> g_grid_cap{0};
 
 __device__ __forceinline__ bool give_up(const CompressArgs &a, uint32_t spins) {
     return spins >= a.spin_limit || ((spins & 255u) == 255u && ld_agent(a.err) != 0);
@@ -402,7 +409,7 @@ struct Posted {
 // complete, so it precedes the post), then store the tagged partial in the tile's
 // own slot -- no read-modify-write, so tiles never contend for one word.  The
 // workgroup holding the chunk's last tile then sums all slots and publishes
-// {epoch + 1, scale}.  With at most coop_depth() tiles of a chunk per workgroup,
+// {epoch + 1, scale}.  With at most onepass_depth() tiles of a chunk per workgroup,
 // all earlier tiles of the chunk are posted by workgroups that do not wait on it.
 template <bool FINALIZE>
 __device__ Posted post_tile(const CompressArgs &a, int tile_id, int chunk, double partial, DD *s_red,
@@ -601,7 +608,11 @@ __device__ __forceinline__ void unpark_c(const float4 *s, float (&c)[kPerThread]
 }
 
 // ------------------------------------------------------------- kernels
-// One pass, persistent, cooperative (every workgroup of the grid is resident).
+// One pass, persistent: the grid is at most the number of workgroups the device
+// holds at once (its resident capacity for this kernel), so on an otherwise idle
+// device every workgroup is resident from the start; a workgroup that has to wait
+// for a slot (another stream's kernel holding CUs) becomes resident when that
+// kernel's workgroups retire, since none of them waits on this kernel.
 // Workgroup b takes list positions b, b+G, b+2G, ... and keeps kDepth tiles in
 // flight: it computes and posts tile i+kDepth-1 (c parked in LDS) before it waits
 // for tile i's chunk scale and finishes tile i, so the chunk-norm exchange
@@ -744,15 +755,16 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
         e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e);
     }
-    if (p->n_coop > 0) {
-        a.list = p->d_coop_list;
-        a.list_len = p->n_coop;
+    if (p->n_onepass > 0) {
+        a.list = p->d_onepass_list;
+        a.list_len = p->n_onepass;
         // Each variant runs with its own resident capacity; the plan's one-pass /
         // two-pass split was made for the smallest one, so kDepth * grid still
-        // covers every one-pass chunk.
-        static int32_t cap_cache[64] = {0};
+        // covers every one-pass chunk.  The caches are atomic: concurrent first
+        // calls from several host threads compute and store the same value.
+        static std::atomic<int32_t> cap_cache[64];
         const int dev = p->device;
-        int32_t cap = (dev >= 0 && dev < 64) ? cap_cache[dev] : 0;
+        int32_t cap = (dev >= 0 && dev < 64) ? cap_cache[dev].load(std::memory_order_relaxed) : 0;
         if (cap <= 0) {
             int per_cu = 0, cus = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -760,19 +772,20 @@ static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_
                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
                 return ONEBIT_ERR_HIP;
             cap = per_cu * cus;
-            if (dev >= 0 && dev < 64) cap_cache[dev] = cap;
+            if (dev >= 0 && dev < 64) cap_cache[dev].store(cap, std::memory_order_relaxed);
         }
-        if (cap < p->coop_capacity) return ONEBIT_ERR_HIP;
-        const int grid = p->n_coop < cap ? p->n_coop : cap;
-        void *args[] = {&a};
+        if (cap < p->resident_capacity) return ONEBIT_ERR_HIP;
+        int grid = p->n_onepass < cap ? p->n_onepass : cap;
+        const int32_t user_cap = g_grid_cap.load(std::memory_order_relaxed);
+        if (user_cap > 0 && user_cap < grid) grid = user_cap;
+        // the progress argument needs every one-pass chunk within kDepth * grid
+        // consecutive list positions
+        if ((int64_t)kDepth * grid < (int64_t)p->max_onepass_chunk_tiles) return ONEBIT_ERR_INVALID;
         prof_before(base + 1, stream);
-        hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_compress_onepass<MODE, GT, XB>),
-                                                  dim3(grid), dim3(kBlock), args, 0, stream);
+        hipLaunchKernelGGL((k_compress_onepass<MODE, GT, XB>), dim3(grid), dim3(kBlock), 0, stream, a);
         prof_after(stream);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return hip_status(e);
-        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_status(e);
     }
     return ONEBIT_OK;
 }
@@ -783,14 +796,16 @@ static int occupancy_of(const void *fn) {
     return blocks;
 }
 
-int32_t coop_depth() { return kDepth; }
+int32_t onepass_depth() { return kDepth; }
 
-int32_t coop_capacity(int device) {
-    static int32_t cached[64] = {0};
-    if (device >= 0 && device < 64 && cached[device] > 0) return cached[device];
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
-    if (!prop.cooperativeLaunch) return 0;
+int32_t resident_capacity(int device) {
+    static std::atomic<int32_t> cached[64];
+    if (device >= 0 && device < 64) {
+        const int32_t c = cached[device].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
     const void *fns[] = {
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradF32, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdate, kGradF32, true>),
@@ -817,8 +832,8 @@ int32_t coop_capacity(int device) {
         const int b = occupancy_of(f);
         per_cu = b < per_cu ? b : per_cu;
     }
-    const int32_t cap = per_cu > 0 ? per_cu * prop.multiProcessorCount : 0;
-    if (device >= 0 && device < 64) cached[device] = cap;
+    const int32_t cap = per_cu > 0 ? per_cu * cus : 0;
+    if (device >= 0 && device < 64) cached[device].store(cap, std::memory_order_relaxed);
     return cap;
 }
 
@@ -879,7 +894,7 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     a.err = ws.err;
     a.publish = ws.publish;
     a.slots = ws.slots;
-    a.spin_limit = g_spin_limit;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (packed && !update) {
         switch (g_dtype) {
@@ -969,8 +984,12 @@ extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const
     a.err = ws.err;
     a.publish = ws.publish;
     a.slots = ws.slots;
-    a.spin_limit = g_spin_limit;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     return launch<kServer, kGradF32, false>(plan, a, static_cast<hipStream_t>(stream));
 }
 
-extern "C" void onebit_set_spin_limit(uint32_t limit) { g_spin_limit = limit ? limit : kSpinLimit; }
+extern "C" void onebit_set_spin_limit(uint32_t limit) {
+    g_spin_limit.store(limit ? limit : kSpinLimit, std::memory_order_relaxed);
+}
+
+extern "C" void onebit_set_grid_cap(int32_t cap) { g_grid_cap.store(cap > 0 ? cap : 0, std::memory_order_relaxed); }

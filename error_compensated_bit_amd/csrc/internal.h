@@ -50,13 +50,14 @@ struct onebit_plan_s {
     onebit::TileDesc *d_tiles = nullptr;
     onebit::ChunkDesc *d_chunks = nullptr;
     int64_t *d_mask_iv = nullptr;     // 2*n_mask_iv: [a, b) pairs, sorted, disjoint
-    int32_t *d_coop_list = nullptr;   // tiles of chunks small enough to stay resident
+    int32_t *d_onepass_list = nullptr;  // tiles of chunks the one-pass kernel takes
     int32_t *d_big_list = nullptr;    // tiles of the other chunks (two-pass)
     int32_t *d_big_chunks = nullptr;  // the two-pass chunks
-    int32_t n_coop = 0;
+    int32_t n_onepass = 0;
     int32_t n_big = 0;
     int32_t n_big_chunks = 0;
-    int32_t coop_capacity = 0;        // resident workgroups the split was made for
+    int32_t resident_capacity = 0;    // resident workgroups the split was made for
+    int32_t max_onepass_chunk_tiles = 0;  // tiles of the largest one-pass chunk
 };
 
 namespace onebit {
@@ -67,10 +68,11 @@ bool aligned16(const void *p);
 bool aligned_to(const void *p, uintptr_t bytes);
 onebit_status_t hip_status(hipError_t e);
 
-// Largest number of co-resident workgroups of the compress kernels on this device,
-// and the number of tiles each of them keeps in flight.
-int32_t coop_capacity(int device);
-int32_t coop_depth();
+// Largest number of co-resident workgroups of the one-pass compress kernels on this
+// device (the smallest over their variants), and the number of tiles each
+// workgroup keeps in flight.
+int32_t resident_capacity(int device);
+int32_t onepass_depth();
 
 // Launch timing (diagnostics): while a profiling session is open every kernel
 // launch of the library is bracketed by two events on its stream.

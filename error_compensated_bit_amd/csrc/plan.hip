@@ -109,7 +109,7 @@ extern "C" void onebit_plan_destroy(onebit_plan_t p) {
     (void)hipFree(p->d_tiles);
     (void)hipFree(p->d_chunks);
     (void)hipFree(p->d_mask_iv);
-    (void)hipFree(p->d_coop_list);
+    (void)hipFree(p->d_onepass_list);
     (void)hipFree(p->d_big_list);
     (void)hipFree(p->d_big_chunks);
     if (prev >= 0) (void)hipSetDevice(prev);
@@ -245,26 +245,27 @@ extern "C" onebit_status_t onebit_plan_create(const int64_t *chunk_offsets, int6
     p->aligned = T.aligned;
     p->max_chunk_tiles = T.max_chunk_tiles;
 
-    // one-pass chunks (at most coop_depth() times the resident workgroups: the
+    // one-pass chunks (at most onepass_depth() times the resident workgroups: the
     // one-pass kernel keeps that many tiles in flight per workgroup) and two-pass
     // chunks
-    p->coop_capacity = coop_capacity(p->device);
-    std::vector<int32_t> coop, big, big_chunks;
+    p->resident_capacity = resident_capacity(p->device);
+    std::vector<int32_t> onepass, big, big_chunks;
     for (int64_t j = 0; j < n_chunks; ++j) {
         const ChunkDesc &c = T.chunks[j];
-        const bool one_pass = (int64_t)c.ntiles <= (int64_t)coop_depth() * (int64_t)p->coop_capacity;
-        std::vector<int32_t> &dst = one_pass ? coop : big;
+        const bool one_pass = (int64_t)c.ntiles <= (int64_t)onepass_depth() * (int64_t)p->resident_capacity;
+        std::vector<int32_t> &dst = one_pass ? onepass : big;
         for (int32_t k = 0; k < c.ntiles; ++k) dst.push_back(c.first_tile + k);
         if (!one_pass) big_chunks.push_back((int32_t)j);
+        if (one_pass && c.ntiles > p->max_onepass_chunk_tiles) p->max_onepass_chunk_tiles = c.ntiles;
     }
-    p->n_coop = (int32_t)coop.size();
+    p->n_onepass = (int32_t)onepass.size();
     p->n_big = (int32_t)big.size();
     p->n_big_chunks = (int32_t)big_chunks.size();
 
     hipError_t e = upload(&p->d_tiles, T.tiles);
     if (e == hipSuccess) e = upload(&p->d_chunks, T.chunks);
     if (e == hipSuccess) e = upload(&p->d_mask_iv, T.iv);
-    if (e == hipSuccess) e = upload(&p->d_coop_list, coop);
+    if (e == hipSuccess) e = upload(&p->d_onepass_list, onepass);
     if (e == hipSuccess) e = upload(&p->d_big_list, big);
     if (e == hipSuccess) e = upload(&p->d_big_chunks, big_chunks);
     if (e != hipSuccess) {
@@ -333,24 +334,24 @@ extern "C" onebit_status_t onebit_profile_end(double *total_ms, int64_t *launche
     return st;
 }
 
-extern "C" int32_t onebit_device_coop_capacity(void) {
+extern "C" int32_t onebit_device_resident_capacity(void) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    return coop_capacity(dev);
+    return resident_capacity(dev);
 }
 
 extern "C" int64_t onebit_onepass_max_elements(void) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    return (int64_t)coop_depth() * (int64_t)coop_capacity(dev) * (int64_t)kTile;
+    return (int64_t)onepass_depth() * (int64_t)resident_capacity(dev) * (int64_t)kTile;
 }
 
 extern "C" void onebit_plan_stats(onebit_plan_t p, int64_t *out6) {
     if (!p || !out6) return;
     out6[0] = p->n_tiles;
-    out6[1] = p->n_coop;
+    out6[1] = p->n_onepass;
     out6[2] = p->n_big;
-    out6[3] = p->coop_capacity;
+    out6[3] = p->resident_capacity;
     out6[4] = p->max_chunk_tiles;
     out6[5] = p->aligned ? 1 : 0;
 }

@@ -204,7 +204,7 @@ def test_weight_decay_and_hyperparameters():
 
 
 def test_two_pass_chunk_next_to_one_pass_chunks():
-    cap = ob.onebit_device_coop_capacity()
+    cap = ob.onebit_device_resident_capacity()
     say(f"device capacity {cap} workgroups, one-pass chunks up to {ob.onebit_onepass_max_elements()}")
     big = max(ob.onebit_onepass_max_elements(), 1) + 4097
     off = W.offsets_from_sizes([5000, big, 3, 70001])
