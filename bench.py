@@ -4,7 +4,7 @@ Headline (one JSON line on stdout): params/s of onebit_compress_update on the
 BERT-Large-shaped flat vector (335,143,938 fp32 params in 393 tensors, one scale
 per tensor, 8 masked tensors, one compressed step per call), with inputs
 resident in HBM.  A "step" is one such call.  Also reported:
-  roofline     the dominant kernel (the one-pass cooperative compression kernel):
+  roofline     the dominant kernel (the one-pass persistent compression kernel):
                algorithmic bytes per launch / its mean launch time from HIP events
                recorded around each launch on the launch stream, against 8 TB/s;
   cpu_baseline the CPU oracle (single thread) on a bounded sample of the same
@@ -22,8 +22,10 @@ Profiling (rocprofv3 runs the program itself, so these modes only do the work):
                                        1 GiB device-to-device copy used to
                                        calibrate the FETCH_SIZE/WRITE_SIZE counters
   python bench.py --profile-allreduce  the same for the 16-worker simulated all-reduce
-  python bench.py --summarize-allreduce KT FETCH WRITE
+  python bench.py --summarize-allreduce KT FETCH WRITE SQ
   python bench.py --summarize-profile KT FETCH WRITE
+  python bench.py --ceilings           streaming ceilings by read/write mix, cache
+                                       policy and workgroup shape (markdown on stdout)
                                        turn three rocprofv3 CSV output directories
                                        (kernel trace+stats, --pmc FETCH_SIZE,
                                        --pmc WRITE_SIZE) into the text summary kept
@@ -143,15 +145,66 @@ def bench_compress(wl, steps, warmup, dev, bpe):
     return res
 
 
+def host_cpu():
+    """(CPU model name from /proc/cpuinfo, logical CPUs of the host, CPUs this process may use)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = sorted(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = list(range(os.cpu_count() or 1))
+    return model, os.cpu_count(), allowed
+
+
+class pinned_to_one_core:
+    """Run the enclosed block with this thread bound to one allowed CPU (the last
+    one), restoring the previous affinity afterwards."""
+
+    def __enter__(self):
+        self.core = None
+        try:
+            self.prev = os.sched_getaffinity(0)
+            self.core = max(self.prev)
+            os.sched_setaffinity(0, {self.core})
+        except (AttributeError, OSError):
+            self.prev = None
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            os.sched_setaffinity(0, self.prev)
+        return False
+
+
 def cpu_baseline(wl, dev, budget_s=12.0):
     """Time the CPU oracle on whole chunks of the workload (successive compressed
-    steps over the vector, chunk by chunk) until about budget_s of CPU work."""
+    steps over the vector, chunk by chunk) until about budget_s of CPU work, with the
+    timing thread pinned to one core."""
     import numpy as np
     import oracle
     from error_compensated_bit_amd import workloads as W
     state = [t.cpu().numpy() for t in W.init_state(wl, device=dev)]       # x, m, e, v
     g = W.gradient(wl, 1, device=dev)
     g = (g.float() if wl.grad_bf16 else g).cpu().numpy()
+    model, ncpu, allowed = host_cpu()
+    with pinned_to_one_core() as pin:
+        done, spent, calls, steps = _cpu_baseline_loop(wl, state, g, budget_s)
+    return dict(value=done / spent, unit="params/s", cores=1, kind="oracle",
+                sample=f"{calls} whole-chunk calls over {steps} compressed step(s) of the same workload "
+                       f"({done} params), single-threaded C oracle, in place on host copies",
+                seconds=spent, cpu_model=model, host_cpus=ncpu, cpus_allowed=len(allowed), pinned_core=pin.core)
+
+
+def _cpu_baseline_loop(wl, state, g, budget_s):
+    import numpy as np
+    import oracle
     done = 0
     spent = 0.0
     calls = 0
@@ -175,10 +228,7 @@ def cpu_baseline(wl, dev, budget_s=12.0):
             calls += 1
             if spent >= budget_s:
                 break
-    return dict(value=done / spent, unit="params/s", cores=1, kind="oracle",
-                sample=f"{calls} whole-chunk calls over {steps} compressed step(s) of the same workload "
-                       f"({done} params), single-threaded C oracle, in place on host copies",
-                seconds=spent)
+    return done, spent, calls, steps
 
 
 def _oracle_rate(call, units, budget_s):
@@ -539,14 +589,23 @@ def profile_allreduce(steps):
     log(f"[profile] {steps} all-reduce steps of {a.W} x {a.n} and one {CALIBRATION_FLOATS * 4} B copy done")
 
 
-def summarize_allreduce(kt_dir, fetch_dir, write_dir):
-    """Kernel time and HBM traffic of the worker (compress-only) and server launches."""
+ALLREDUCE_SUMMARY = os.path.join(ROOT, "profiles", "allreduce_worker_server_16x64M.md")
+SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+               "SQ_INSTS_SALU")
+
+
+def summarize_allreduce(kt_dir, fetch_dir, write_dir, sq_dir=None):
+    """Kernel time, HBM traffic and (with sq_dir) issue counters of the worker
+    (compress-only) and server launches."""
     import numpy as np
     from error_compensated_bit_amd import workloads as W
     a = W.AllreduceWorkload()
     stats = {_short(r["Name"]): r for r in _rows(kt_dir, "kernel_stats.csv")}
     per = {}
-    for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+    dirs = [("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)]
+    if sq_dir:
+        dirs += [(k, sq_dir) for k in SQ_COUNTERS]
+    for key, d in dirs:
         for r in _rows(d, "counter_collection.csv"):
             if r.get("Counter_Name") == key:
                 per.setdefault((key, _short(r["Kernel_Name"])), []).append(float(r["Counter_Value"]))
@@ -560,9 +619,12 @@ def summarize_allreduce(kt_dir, fetch_dir, write_dir):
            f"{len(a.chunk_off) - 1} chunks)", ""]
     out.append("Commands (from the repository root, on one MI355X):")
     out.append("```")
-    for d, extra in ((kt_dir, "--kernel-trace --stats"), (fetch_dir, "--pmc FETCH_SIZE"), (write_dir, "--pmc WRITE_SIZE")):
+    runs = [(kt_dir, "--kernel-trace --stats"), (fetch_dir, "--pmc FETCH_SIZE"), (write_dir, "--pmc WRITE_SIZE")]
+    if sq_dir:
+        runs.append((sq_dir, "--pmc " + " ".join(SQ_COUNTERS)))
+    for d, extra in runs:
         out.append(f"rocprofv3 {extra} --output-format csv -d {d} -o bench -- python3 bench.py --profile-allreduce")
-    out.append(f"python bench.py --summarize-allreduce {kt_dir} {fetch_dir} {write_dir}")
+    out.append(f"python bench.py --summarize-allreduce {kt_dir} {fetch_dir} {write_dir}" + (f" {sq_dir}" if sq_dir else ""))
     out.append("```")
     out.append(f"Library source digest: {source_digest()}")
     out.append("")
@@ -574,8 +636,9 @@ def summarize_allreduce(kt_dir, fetch_dir, write_dir):
     out.append("| launch | calls | average ns | read bytes | written bytes | traffic / algorithmic | "
                "algorithmic GB/s |")
     out.append("|---|---|---|---|---|---|---|")
-    for label, frag, bpe in (("worker (compress-only)", "k_compress_onepass<1, ", 16.125),
-                             ("server", "k_compress_onepass<2, ", a.W / 8 + 12.125)):
+    stages = (("worker (compress-only)", "worker", "k_compress_onepass<1, ", 16.125),
+              ("server", "server", "k_compress_onepass<2, ", a.W / 8 + 12.125))
+    for label, _, frag, bpe in stages:
         key = next((k for k in stats if frag in k), None)
         if key is None:
             continue
@@ -585,7 +648,47 @@ def summarize_allreduce(kt_dir, fetch_dir, write_dir):
         alg = bpe * a.n
         out.append(f"| {label} | {stats[key]['Calls']} | {ns:.0f} | {rd:.0f} | {wr:.0f} | {(rd + wr) / alg:.4f} | "
                    f"{alg / ns:.0f} |")
+    if sq_dir:
+        out.append("")
+        out.append(f"Issue counters (median per dispatch).  VALU issue bound: {VALU_LANE_OPS_PER_S / 1e12:.2f} T "
+                   f"lane-instructions/s (256 CUs x 4 SIMD16 x one wave64 instruction per 4 clocks x 2.4 GHz), so "
+                   f"VALU time = SQ_INSTS_VALU x 64 / that; fp64 and transcendental instructions issue at lower "
+                   f"rates, so it is a lower bound.  Waiting and VALU-active shares are of SQ_WAVE_CYCLES.")
+        out.append("")
+        out.append("| launch | " + " | ".join(SQ_COUNTERS) + " | VALU lane-instr per element | VALU-issue time ns | "
+                   "VALU time / kernel time | waiting share | VALU-active share |")
+        out.append("|---|" + "---|" * (len(SQ_COUNTERS) + 5))
+        for label, tag, frag, _ in stages:
+            key = next((k for k in stats if frag in k), None)
+            vals = {c: counter(c, frag) for c in SQ_COUNTERS}
+            if key is None or vals["SQ_INSTS_VALU"] is None:
+                continue
+            ns = float(stats[key]["AverageNs"])
+            per_elem = vals["SQ_INSTS_VALU"] * 64.0 / a.n
+            valu_ns = vals["SQ_INSTS_VALU"] * 64.0 / VALU_LANE_OPS_PER_S * 1e9
+            wait = vals["SQ_WAIT_ANY"] / vals["SQ_WAVE_CYCLES"] if vals["SQ_WAVE_CYCLES"] else float("nan")
+            act = vals["SQ_ACTIVE_INST_VALU"] / vals["SQ_WAVE_CYCLES"] if vals["SQ_WAVE_CYCLES"] else float("nan")
+            out.append(f"| {label} | " + " | ".join(f"{vals[c]:.0f}" for c in SQ_COUNTERS) +
+                       f" | {per_elem:.2f} | {valu_ns:.0f} | {valu_ns / ns:.3f} | {wait:.3f} | {act:.3f} |")
+            out.append(f"<!-- {tag} valu_lane_instr_per_element={per_elem:.4f} -->")
     return "\n".join(out) + "\n"
+
+
+def allreduce_valu():
+    """{"worker"/"server": VALU lane-instructions per element} from the committed
+    all-reduce summary, if the library sources still match."""
+    try:
+        text = open(ALLREDUCE_SUMMARY).read()
+    except OSError:
+        return {}
+    if f"Library source digest: {source_digest()}" not in text:
+        return {}
+    res = {}
+    for line in text.splitlines():
+        if line.startswith("<!-- ") and "valu_lane_instr_per_element=" in line:
+            label, kv = line[5:-4].split(" ", 1)
+            res[label] = float(kv.split("=")[1])
+    return res
 
 
 def _short(name):
@@ -672,10 +775,15 @@ def main():
     ap.add_argument("--summarize-profile", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-quantizers", action="store_true")
     ap.add_argument("--profile-allreduce", action="store_true")
-    ap.add_argument("--summarize-allreduce", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-allreduce", nargs="+", metavar="DIR",
+                    help="KT_DIR FETCH_DIR WRITE_DIR [SQ_DIR]")
     ap.add_argument("--summarize-quantizers", nargs=2, metavar=("KT_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("KT_DIR", "COMMAND"))
+    ap.add_argument("--ceilings", action="store_true")
     args = ap.parse_args()
+    if args.ceilings:
+        sys.stdout.write(ceilings())
+        return
     if args.summarize_profile:
         sys.stdout.write(summarize_profile(*args.summarize_profile))
         return
@@ -729,7 +837,8 @@ def main():
 
     base = None if args.no_cpu_baseline else cpu_baseline(wl, dev)
     if rows and not args.no_cpu_baseline:
-        cpu_row_baselines(rows)
+        with pinned_to_one_core():
+            cpu_row_baselines(rows)
         log(f"[bench] cpu oracle per row: {[(k, round(r['cpu_oracle']['value'], 3)) for k, r in rows.items() if 'cpu_oracle' in r]}")
     if base:
         log(f"[bench] cpu oracle {base['value'] / 1e6:.1f} M params/s on {base['sample']}")
@@ -758,9 +867,14 @@ def main():
                    "bytes_per_param": bpe, "plan": head["plan"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": (achieved / PEAK_HBM_GBPS) if achieved else None, "traffic": profile_traffic(),
-                     "kernel": "k_compress_onepass", "bytes_per_launch": bpe * head["onepass_elements"],
-                     "mean_launch_ms": k_ms},
-        "cpu_baseline": ({k: base[k] for k in ("value", "unit", "cores", "kind", "sample")} if base else None),
+                     "kernel": "k_compress_onepass (update mode): the dominant kernel, over the "
+                               f"{head['onepass_elements']} elements of the one-pass chunks; the whole step, "
+                               "two-pass chunk and launch gaps included, is step_frac",
+                     "bytes_per_launch": bpe * head["onepass_elements"], "mean_launch_ms": k_ms,
+                     "timing": "mean of HIP events recorded around each launch on its launch stream",
+                     "step_frac": head["gbps"] / PEAK_HBM_GBPS},
+        "cpu_baseline": ({k: base[k] for k in ("value", "unit", "cores", "kind", "sample", "cpu_model", "host_cpus",
+                                               "cpus_allowed", "pinned_core")} if base else None),
         "ceiling": dict(ceiling, kernel_frac_of_ceiling=(achieved / ceiling["gbps_5r3w"]) if achieved else None),
         "rows": rows,
     }
@@ -780,11 +894,11 @@ def stream_ceiling(dev, n=335_544_320):
     for name, ins, outs, bpe in (("5r3w", bufs[:5], bufs[5:], 32.0),):
         for block, mults in ((256, (1, 2, 3, 6, 16, 32)), (1024, (1, 2, 4, 6, 8))):
             for mult in mults:
-                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block)    # warm
+                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, True)    # warm
                 times = []
                 for _ in range(4):
                     ev0.record()
-                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block)
+                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, True)
                     ev1.record()
                     ev1.synchronize()
                     times.append(ev0.elapsed_time(ev1))
@@ -795,6 +909,63 @@ def stream_ceiling(dev, n=335_544_320):
     del bufs
     return {"gbps_5r3w": best["5r3w"][0], "grid_5r3w": best["5r3w"][1], "block_5r3w": best["5r3w"][2],
             "elements": n, "kernel": "onebit_stream_probe"}
+
+
+CEILING_MIXES = ((1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (1, 2), (4, 2), (5, 3))
+
+
+def ceilings(n=268_435_456):
+    """Streaming ceilings of this device: the plain probe kernel for each read/write
+    mix, with the streaming (nontemporal) and the default cache policy, over
+    256-thread workgroups (1-32 per CU) and 1024-thread workgroups (1-8 per CU);
+    the best rate of each, and the best with 256-thread workgroups (the compression
+    kernels' shape).  Returns the markdown summary kept under profiles/."""
+    import torch
+    from error_compensated_bit_amd import onebit as ob
+    ensure_built()
+    dev = "cuda:0"
+    bufs = [torch.zeros(n, device=dev) for _ in range(8)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    shapes = [(256, m) for m in (1, 2, 3, 4, 6, 8, 16, 32)] + [(1024, m) for m in (1, 2, 4, 6, 8)]
+    out = [f"# Streaming ceilings by read/write mix and cache policy ({n} fp32 elements per stream)", ""]
+    out.append("Command (from the repository root, on one MI355X):")
+    out.append("```")
+    out.append("python bench.py --ceilings")
+    out.append("```")
+    out.append(f"Device: {torch.cuda.get_device_name(0)}, {cus} CUs.  Kernel: onebit_stream_probe (four 16-byte "
+               f"vectors per thread and stream per iteration, grid-stride).  Bytes counted: (reads + writes) x 4 x "
+               f"n per launch; time: best of 4 launches between HIP events on the launch stream, after one warm "
+               f"launch.  Peak: {PEAK_HBM_GBPS:.0f} GB/s.")
+    out.append("")
+    out.append("| reads + writes | cache policy | best GB/s | fraction of 8 TB/s | best shape (threads x WG per CU) | "
+               "best GB/s with 256-thread WGs |")
+    out.append("|---|---|---|---|---|---|")
+    for reads, writes in CEILING_MIXES:
+        ins, outs = bufs[:reads], bufs[reads:reads + writes]
+        for nt in (True, False):
+            best, best256 = (0.0, None), 0.0
+            for block, mult in shapes:
+                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, nt)
+                times = []
+                for _ in range(4):
+                    ev0.record()
+                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, nt)
+                    ev1.record()
+                    ev1.synchronize()
+                    times.append(ev0.elapsed_time(ev1))
+                del keep
+                gbps = (reads + writes) * 4.0 * n / (min(times) * 1e-3) / 1e9
+                if gbps > best[0]:
+                    best = (gbps, f"{block} x {mult}")
+                if block == 256:
+                    best256 = max(best256, gbps)
+            pol = "nontemporal" if nt else "default"
+            out.append(f"| {reads} + {writes} | {pol} | {best[0]:.0f} | {best[0] / PEAK_HBM_GBPS:.3f} | {best[1]} | "
+                       f"{best256:.0f} |")
+            log(f"[ceilings] {reads}+{writes} {pol}: {best[0]:.0f} GB/s ({best[1]}), 256-thread {best256:.0f}")
+    del bufs
+    return "\n".join(out) + "\n"
 
 
 def roof(gbps, elems_per_s=None, label=None, valu=None):
@@ -917,6 +1088,7 @@ def secondary_rows(dev, args):
 
     # simulated compressed all-reduce: 16 workers x 64M fp32, 16 chunks of 4M
     a = W.AllreduceWorkload()
+    ar_valu = allreduce_valu()
     plan = ob.onebit_plan_create(a.chunk_off)
     words, nch = ob.onebit_plan_words(plan), ob.onebit_plan_chunks(plan)
     m = torch.zeros(a.n, device=dev)
@@ -951,8 +1123,10 @@ def secondary_rows(dev, args):
                                     server_kernel_gbps=14.125 * a.n / (s_ms * 1e-3) / 1e9,
                                     server_kernel_ms=s_ms, worker_kernel_ms=w_ms,
                                     ms_per_step_graph_replay=t_graph * 1e3,
-                                    worker_roofline=roof(B_WORKER * a.n / (w_ms * 1e-3) / 1e9),
-                                    server_roofline=roof(14.125 * a.n / (s_ms * 1e-3) / 1e9))
+                                    worker_roofline=roof(B_WORKER * a.n / (w_ms * 1e-3) / 1e9, a.n / (w_ms * 1e-3),
+                                                         "worker", ar_valu),
+                                    server_roofline=roof(14.125 * a.n / (s_ms * 1e-3) / 1e9, a.n / (s_ms * 1e-3),
+                                                         "server", ar_valu))
     # the same exchange as a full step: fp16 gradients, the server's result masked
     # per element into the momentum, frozen-v update of x
     g16 = grads.to(torch.float16)

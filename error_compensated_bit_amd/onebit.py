@@ -6,9 +6,12 @@ raises immediately: there is no fallback path.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
 import re
+import sys
+import weakref
 
 import numpy as np
 
@@ -24,6 +27,7 @@ _P, _I64, _I, _D, _U64, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_double, C.c_ui
 _SIGS = {
     "onebit_status_string": (C.c_char_p, [_I]),
     "onebit_set_spin_limit": (None, [C.c_uint32]),
+    "onebit_set_grid_cap": (None, [C.c_int32]),
     "onebit_plan_create": (_I, [_P, _I64, _P, _P, _I64, C.POINTER(_P)]),
     "onebit_plan_destroy": (None, [_P]),
     "onebit_plan_host_tables": (_I, [_P, _I64, _P, _P, _I64, _P, _P, _P, _P, _P]),
@@ -33,7 +37,7 @@ _SIGS = {
     "onebit_plan_workspace_bytes": (_SZ, [_P]),
     "onebit_workspace_init": (_I, [_P, _SZ, _P]),
     "onebit_workspace_status": (_I, [_P, C.POINTER(_U64), _P]),
-    "onebit_device_coop_capacity": (C.c_int32, []),
+    "onebit_device_resident_capacity": (C.c_int32, []),
     "onebit_plan_stats": (None, [_P, _P]),
     "onebit_onepass_max_elements": (_I64, []),
     "onebit_profile_begin": (None, []),
@@ -43,7 +47,7 @@ _SIGS = {
     "onebit_compress_update_packed": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
     "onebit_momentum_update_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _P]),
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
-    "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _I, _P]),
+    "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _I, _I, _P]),
     "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
     "qsgd_quantize": (_I, [_P, _I, _I64, _I, _I, _U64, _P, _P, _P]),
     "qsgd_reduce": (_I, [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P, _P]),
@@ -141,16 +145,31 @@ def onebit_status_string(status: int) -> str:
     return load().onebit_status_string(int(status)).decode()
 
 
+_live_plans = weakref.WeakSet()
+
+
 class Plan:
-    """Owning handle of an onebit_plan_t (destroyed with the object)."""
+    """Owning handle of an onebit_plan_t (destroyed with the object, or at interpreter
+    exit while the HIP runtime is still up; never from a finalizing interpreter)."""
 
     def __init__(self, handle):
         self.handle = handle
+        _live_plans.add(self)
 
-    def __del__(self):
+    def close(self):
         if getattr(self, "handle", None) and _lib is not None:
             _lib.onebit_plan_destroy(self.handle)
-            self.handle = None
+        self.handle = None
+
+    def __del__(self):
+        if not sys.is_finalizing():
+            self.close()
+
+
+@atexit.register
+def _release_plans():
+    for p in list(_live_plans):
+        p.close()
 
     @property
     def _as_parameter_(self):
@@ -190,9 +209,8 @@ def onebit_plan_host_tables(chunk_offsets, tensor_offsets=None, tensor_keep=None
 
 
 def onebit_plan_destroy(plan: Plan):
-    if plan.handle:
-        load().onebit_plan_destroy(plan.handle)
-        plan.handle = None
+    load()
+    plan.close()
 
 
 def onebit_plan_elements(plan) -> int:
@@ -214,12 +232,12 @@ def onebit_plan_workspace_bytes(plan) -> int:
 def onebit_plan_stats(plan) -> dict:
     out = np.zeros(6, dtype=np.int64)
     load().onebit_plan_stats(plan.handle, out.ctypes.data)
-    return dict(zip(("tiles", "onepass_tiles", "twopass_tiles", "coop_capacity", "max_chunk_tiles", "aligned"),
+    return dict(zip(("tiles", "onepass_tiles", "twopass_tiles", "resident_capacity", "max_chunk_tiles", "aligned"),
                     out.tolist()))
 
 
-def onebit_device_coop_capacity() -> int:
-    return int(load().onebit_device_coop_capacity())
+def onebit_device_resident_capacity() -> int:
+    return int(load().onebit_device_resident_capacity())
 
 
 def onebit_onepass_max_elements() -> int:
@@ -293,20 +311,25 @@ def onebit_server_reduce(plan, worker_bits, worker_scales, server_error, server_
                                        _stream(stream)), "onebit_server_reduce")
 
 
-def onebit_stream_probe(inputs, outputs, grid, block=256, stream=None):
-    """inputs / outputs: lists of equally long fp32 device tensors (5 + 3 or 1 + 1);
-    block: threads per workgroup (256, 512 or 1024)."""
+def onebit_stream_probe(inputs, outputs, grid, block=256, nontemporal=True, stream=None):
+    """inputs / outputs: lists of equally long fp32 device tensors (one of the mixes
+    the library supports); block: threads per workgroup (256, 512 or 1024)."""
     import torch
-    dev = inputs[0].device
-    pin = torch.tensor([t.data_ptr() for t in inputs], dtype=torch.int64, device=dev)
-    pout = torch.tensor([t.data_ptr() for t in outputs], dtype=torch.int64, device=dev)
-    _check(load().onebit_stream_probe(_ptr(pin), len(inputs), _ptr(pout), len(outputs), inputs[0].numel(), int(grid),
-                                      int(block), _stream(stream)), "onebit_stream_probe")
+    dev = (inputs or outputs)[0].device
+    n = (inputs or outputs)[0].numel()
+    pin = torch.tensor([t.data_ptr() for t in inputs] or [0], dtype=torch.int64, device=dev)
+    pout = torch.tensor([t.data_ptr() for t in outputs] or [0], dtype=torch.int64, device=dev)
+    _check(load().onebit_stream_probe(_ptr(pin), len(inputs), _ptr(pout), len(outputs), n, int(grid),
+                                      int(block), int(bool(nontemporal)), _stream(stream)), "onebit_stream_probe")
     return pin, pout           # keep the pointer arrays alive until the launch has run
 
 
 def onebit_set_spin_limit(limit: int) -> None:
     load().onebit_set_spin_limit(int(limit))
+
+
+def onebit_set_grid_cap(cap: int) -> None:
+    load().onebit_set_grid_cap(int(cap))
 
 
 def onebit_momentum_update(m, mask, v, x, x_bf16, *, lr, eps, weight_decay, stream=None):

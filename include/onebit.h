@@ -118,10 +118,10 @@ onebit_status_t onebit_workspace_init(void *workspace, size_t bytes, void *strea
 onebit_status_t onebit_workspace_status(const void *workspace, uint64_t *out, void *stream);
 
 /* Diagnostics: co-resident workgroups of the one-pass compression kernel on the
- * current device (0 when cooperative launch is unavailable), and a plan's tile
+ * current device (the grid it is launched with at most), and a plan's tile
  * split: out6 (host) = {tiles, one-pass tiles, two-pass tiles, capacity used,
  * largest chunk in tiles, 1 if every chunk starts on a multiple of 4 elements}. */
-int32_t onebit_device_coop_capacity(void);
+int32_t onebit_device_resident_capacity(void);
 void onebit_plan_stats(onebit_plan_t plan, int64_t *out6);
 /* Largest chunk (elements) the one-pass path takes on the current device;
  * larger chunks take the two-pass path. */
@@ -131,8 +131,17 @@ int64_t onebit_onepass_max_elements(void);
  * (0 restores the default, 2^20).  A wait that gives up stores an error code in the
  * workspace (read it with onebit_workspace_status) and the call still completes,
  * with unspecified results; a workspace with an error must be re-initialized with
- * onebit_workspace_init before further use.  Not thread-safe; applies to later calls. */
+ * onebit_workspace_init before further use.  Applies to later calls from any host
+ * thread. */
 void onebit_set_spin_limit(uint32_t limit);
+
+/* Diagnostics: launch the one-pass compression kernel with at most `cap`
+ * workgroups (0 or a negative value removes the cap), so that the chunk-norm
+ * exchange can be exercised with fewer resident workgroups than the device holds.
+ * A call whose plan has a one-pass chunk of more than 3 * grid tiles (the most the
+ * kernel's progress argument allows) returns ONEBIT_ERR_INVALID and launches
+ * nothing.  Applies to later calls from any host thread. */
+void onebit_set_grid_cap(int32_t cap);
 
 /* Launch timing.  Between onebit_profile_begin and onebit_profile_end every kernel
  * the library launches is bracketed by two HIP events on its own stream.
@@ -153,12 +162,15 @@ onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
  * output streams of n elements each (out_k = sum of the inputs + k), to measure what
  * HBM delivers for that mix on this device.  in / out: DEVICE arrays of `reads` /
  * `writes` device pointers, each 16-byte aligned; n a multiple of 4.  Supported
- * mixes: 5 reads + 3 writes (the compression kernel's), 1 + 1 (a copy); others
- * return ONEBIT_ERR_UNSUPPORTED.  grid: number of workgroups; block: threads per
- * workgroup, 256, 512 or 1024 (ONEBIT_ERR_INVALID otherwise).  Loads and stores
- * use the streaming (nontemporal) cache policy, as the compression kernels do. */
+ * mixes (reads + writes): 1 + 0 (read-only: the inputs are left unchanged unless a
+ * sum equals -3e38), 0 + 1 (write-only), 1 + 1, 2 + 1, 3 + 1, 1 + 2, 4 + 2 and
+ * 5 + 3 (the compression kernel's); others return ONEBIT_ERR_UNSUPPORTED.  grid:
+ * number of workgroups; block: threads per workgroup, 256, 512 or 1024
+ * (ONEBIT_ERR_INVALID otherwise).  nontemporal != 0: loads and stores use the
+ * streaming (nontemporal) cache policy, as the compression kernels do; 0: the
+ * default policy. */
 onebit_status_t onebit_stream_probe(const float *const *in, int reads, float *const *out, int writes,
-                                    int64_t n, int grid, int block, void *stream);
+                                    int64_t n, int grid, int block, int nontemporal, void *stream);
 
 /* Warmup step t (1-based) of full-precision Adam over n elements ([DSG] sec. 4,
  * phase one; [1BA]):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;

@@ -1,4 +1,6 @@
-"""The streaming probe (diagnostics) writes out_k = sum of its inputs + k."""
+"""The streaming probe (diagnostics) writes out_k = sum of its inputs + k, for every
+supported read/write mix and both cache policies; the read-only mix leaves its input
+unchanged; unsupported mixes and workgroup sizes are refused."""
 import pytest
 import torch
 
@@ -7,24 +9,36 @@ from gpu_helpers import DEV
 
 pytestmark = pytest.mark.gpu
 
+MIXES = [(1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (1, 2), (4, 2), (5, 3)]
 
+
+@pytest.mark.parametrize("nontemporal", [True, False])
 @pytest.mark.parametrize("block", [256, 1024])
-@pytest.mark.parametrize("reads,writes", [(5, 3), (1, 1)])
-def test_stream_probe_values(reads, writes, block):
+@pytest.mark.parametrize("reads,writes", MIXES)
+def test_stream_probe_values(reads, writes, block, nontemporal):
     n = 1024 * 4 * 4 * 3 + 44                   # several grid-stride spans and a ragged last one
     ins = [torch.randn(n, device=DEV) for _ in range(reads)]
+    before = [t.clone() for t in ins]
     outs = [torch.zeros(n, device=DEV) for _ in range(writes)]
-    keep = ob.onebit_stream_probe(ins, outs, 2, block)
+    keep = ob.onebit_stream_probe(ins, outs, 2, block, nontemporal)
     torch.cuda.synchronize()
     s = torch.zeros(n, device=DEV)
     for t in ins:
         s = s + t
     for k, o in enumerate(outs):
         assert torch.equal(o, s + float(k))
+    for a, b in zip(ins, before):
+        assert torch.equal(a, b)
     del keep
+
+
+def test_stream_probe_refusals():
+    n = 4096
+    ins = [torch.zeros(n, device=DEV) for _ in range(2)]
+    outs = [torch.zeros(n, device=DEV) for _ in range(2)]
     with pytest.raises(ob.OnebitError) as ei:
-        ob.onebit_stream_probe(ins[:1], outs, 2) if writes == 3 else ob.onebit_stream_probe(ins * 2, outs, 2)
+        ob.onebit_stream_probe(ins, outs, 2)                  # 2 + 2 is not a supported mix
     assert ei.value.status == ob.ONEBIT_ERR_UNSUPPORTED
     with pytest.raises(ob.OnebitError) as ei:
-        ob.onebit_stream_probe(ins, outs, 2, 300)
+        ob.onebit_stream_probe(ins[:1], outs[:1], 2, 300)
     assert ei.value.status == ob.ONEBIT_ERR_INVALID
