@@ -17,7 +17,16 @@ Host logic only: each step is one call of the library (onebit_adam_warmup_step o
 onebit_compress_update); m, v, the error, the packed words, the scales and the
 workspace are device tensors this object allocates next to x.  Bias correction,
 when enabled, applies to the warmup steps only (the compressed phase never
-corrects).
+corrects), so it is off by default, as in every configuration the guide prints
+(sec. 6.2): with it on, the step size changes by about (1 - b1^T) / sqrt(1 - b2^T)
+at the switch to compression, T = freeze_step.
+
+Failure detection: the compressed step's cross-workgroup waits are bounded; a wait
+that gives up records an error in the workspace and the step's outputs are not
+valid.  The error stays set until the workspace is re-initialized, and while it is
+set every later wait gives up at once, so the driver reads it (a synchronizing
+8-byte copy) after every `check_every`-th compressed step; when it is set the driver
+re-initializes the workspace and raises WaitTimeout.
 """
 from __future__ import annotations
 
@@ -25,6 +34,11 @@ import numpy as np
 import torch
 
 from . import onebit as ob
+
+
+class WaitTimeout(RuntimeError):
+    """A cross-workgroup wait of a compressed step gave up; that step's m, e and x
+    are not valid (restore them, e.g. from a checkpoint, before continuing)."""
 
 
 class OneBitAdam:
@@ -35,11 +49,14 @@ class OneBitAdam:
     tensor_offsets, tensor_keep
                     tensor table and keep flags (0 = masked: m and the error pinned
                     at zero in the compressed phase);
-    freeze_step     number of full-precision warmup steps.
+    freeze_step     number of full-precision warmup steps;
+    check_every     read the workspace's error word after every check_every-th
+                    compressed step (0: never).
     """
 
     def __init__(self, x, *, chunk_offsets=None, tensor_offsets=None, tensor_keep=None, lr=1e-3,
-                 betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, bias_correction=True, freeze_step=100000):
+                 betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, bias_correction=False, freeze_step=100000,
+                 check_every=1):
         if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.dim() != 1:
             raise TypeError("x must be a one-dimensional float32 tensor")
         if freeze_step < 0:
@@ -57,7 +74,9 @@ class OneBitAdam:
         self.eps, self.weight_decay = float(eps), float(weight_decay)
         self.bias_correction = bool(bias_correction)
         self.freeze_step = int(freeze_step)
+        self.check_every = int(check_every)
         self.step_count = 0
+        self.compressed_steps = 0
         self.m = torch.zeros_like(x)
         self.v = torch.zeros_like(x)
         self.e = torch.zeros_like(x)
@@ -86,7 +105,19 @@ class OneBitAdam:
             ob.onebit_compress_update(self.plan, g, self.m, self.e, self.v, self.x, None, self.bits, self.scales,
                                       lr=self.lr, beta1=self.beta1, eps=self.eps, weight_decay=self.weight_decay,
                                       workspace=self.workspace, stream=stream)
+            self.compressed_steps += 1
         self.step_count = t
+        if t > self.freeze_step and self.check_every > 0 and self.compressed_steps % self.check_every == 0:
+            self.check(stream)
+
+    def check(self, stream=None):
+        """Raise WaitTimeout (after re-initializing the workspace) if a bounded wait of a
+        compressed step since the last check gave up."""
+        status = ob.onebit_workspace_status(self.workspace, stream)
+        if status != 0:
+            ob.onebit_workspace_init(self.workspace, stream)
+            raise WaitTimeout(f"a cross-workgroup wait gave up (code {status}) during the compressed steps up to "
+                              f"step {self.step_count}; their outputs are not valid")
 
     def state_dict(self) -> dict:
         """Step count, momentum and variance (the compression error is not kept)."""

@@ -98,3 +98,41 @@ def test_masked_tensors_through_the_driver():
         if t > 2:
             assert np.all(host(o.m)[masked] == 0) and np.all(host(o.e)[masked] == 0)
             assert np.array_equal(host(o.x)[masked], x_prev[masked])
+
+
+def test_driver_raises_on_a_failed_wait_and_recovers_from_a_checkpoint():
+    """The host sets the workspace's error word before a compressed step (as a wait
+    that gave up in an earlier step would have left it): every bounded wait of that
+    step gives up at once and its kernels still exit; the driver reads the word after
+    the step, re-initializes the workspace and raises WaitTimeout.  Reloading the
+    checkpoint taken before that step and repeating it matches the oracle."""
+    from error_compensated_bit_amd.optimizer import WaitTimeout
+    off = W.fixed_chunks(3 << 20, 1 << 20)
+    n = int(off[-1])
+    rng = np.random.default_rng(12)
+    x0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hp = dict(W.HYPER)
+    kw = dict(chunk_offsets=off, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=0.0,
+              freeze_step=1)
+    o = OneBitAdam(torch.from_numpy(x0.copy()).to(DEV), **kw)
+    r = OracleAdam(x0, off, None, None, dict(hp, weight_decay=0.0), 1)
+    grads = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(3)]
+    for t in range(2):
+        x_prev = r.x.copy()
+        o.step(torch.from_numpy(grads[t]).to(DEV))
+        r.step(grads[t])
+        check(f"step {t + 1}", o, r, x_prev)
+    sd = o.state_dict()
+    x_saved = o.x.clone()
+    o.workspace[0] = 2
+    with pytest.raises(WaitTimeout):
+        o.step(torch.from_numpy(grads[2]).to(DEV))
+    say("  forced error word: WaitTimeout raised")
+    assert int(o.workspace[0].item()) == 0
+    o.x.copy_(x_saved)
+    o.load_state_dict(sd)
+    r.e[:] = 0.0
+    x_prev = r.x.copy()
+    o.step(torch.from_numpy(grads[2]).to(DEV))
+    r.step(grads[2])
+    check("step 3 after the reload", o, r, x_prev)

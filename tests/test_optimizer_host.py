@@ -25,8 +25,18 @@ def calls(monkeypatch):
         assert e is not None and v is not None and x is not None and xb is None
         log.append(("compress", plan[1], k["beta1"], k["lr"]))
 
+    def status(ws, stream=None):
+        log.append(("status",))
+        return int(ws[0])
+
+    def init(ws, stream=None):
+        log.append(("init",))
+        ws.zero_()
+
     monkeypatch.setattr(ob, "onebit_adam_warmup_step", warm)
     monkeypatch.setattr(ob, "onebit_compress_update", comp)
+    monkeypatch.setattr(ob, "onebit_workspace_status", status)
+    monkeypatch.setattr(ob, "onebit_workspace_init", init)
     return log
 
 
@@ -39,18 +49,19 @@ def test_warmup_then_compressed_steps(calls):
         o.step(torch.zeros(10))
     assert o.frozen and o.step_count == 5
     assert calls == [("warmup", 1, False, 0.99), ("warmup", 2, False, 0.99), ("warmup", 3, False, 0.99),
-                     ("compress", [0, 4, 10], 0.8, 2e-3), ("compress", [0, 4, 10], 0.8, 2e-3)]
+                     ("compress", [0, 4, 10], 0.8, 2e-3), ("status",), ("compress", [0, 4, 10], 0.8, 2e-3),
+                     ("status",)]
     assert o.bits.numel() == 3 and o.scales.numel() == 2 and o.workspace.numel() == 8
 
 
 def test_default_chunks_follow_tensors_then_whole_vector(calls):
     o = opt.OneBitAdam(torch.zeros(6), tensor_offsets=[0, 2, 6], tensor_keep=[1, 0], freeze_step=0)
     o.step(torch.zeros(6))
-    assert calls == [("compress", [0, 2, 6], 0.9, 1e-3)]
+    assert calls == [("compress", [0, 2, 6], 0.9, 1e-3), ("status",)]
     calls.clear()
     o = opt.OneBitAdam(torch.zeros(6), freeze_step=0)
     o.step(torch.zeros(6))
-    assert calls == [("compress", [0, 6], 0.9, 1e-3)]
+    assert calls == [("compress", [0, 6], 0.9, 1e-3), ("status",)]
 
 
 def test_checkpoint_keeps_moments_and_resets_error(calls):
@@ -86,3 +97,29 @@ def test_rejects_bad_arguments(calls):
     with pytest.raises(ValueError):
         o.step(torch.zeros(5))
     assert calls == []
+
+
+def test_bias_correction_is_off_by_default(calls):
+    o = opt.OneBitAdam(torch.zeros(4), freeze_step=1)
+    o.step(torch.zeros(4))
+    assert calls == [("warmup", 1, False, 0.999)]
+
+
+def test_error_word_is_checked_every_n_compressed_steps_and_raises(calls):
+    o = opt.OneBitAdam(torch.zeros(4), freeze_step=1, check_every=2)
+    for _ in range(5):
+        o.step(torch.zeros(4))
+    assert [c[0] for c in calls] == ["warmup", "compress", "compress", "status", "compress", "compress", "status"]
+    calls.clear()
+    o.workspace[0] = 2                     # a wait gave up
+    o.step(torch.zeros(4))
+    assert calls == [("compress", [0, 4], 0.9, 1e-3)]
+    with pytest.raises(opt.WaitTimeout):
+        o.step(torch.zeros(4))
+    assert [c[0] for c in calls][-2:] == ["status", "init"]
+    assert int(o.workspace[0]) == 0
+    calls.clear()
+    never = opt.OneBitAdam(torch.zeros(4), freeze_step=0, check_every=0)
+    never.workspace[0] = 1
+    never.step(torch.zeros(4))
+    assert calls == [("compress", [0, 4], 0.9, 1e-3)]
