@@ -24,7 +24,9 @@
 // zeroed workspace is always ready for the next call.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "device_common.h"
 #include "internal.h"
@@ -837,18 +839,75 @@ int32_t resident_capacity(int device) {
     return cap;
 }
 
+// ------------------------------------------- scratch of the allocation-free call
+// The workspace of onebit_compress_update_static lives in the library's own device
+// memory: an error word, one publish word per chunk and one partial slot per tile
+// for plans with chunks + tiles < kScratchWords (8 MiB; each device the library
+// runs on holds its own copy until the process ends).  Host code never uses the
+// array's name as an address: each device's address comes from
+// hipGetSymbolAddress, taken once with that device current.
+constexpr int64_t kScratchWords = int64_t(1) << 20;
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+
+static std::mutex g_scratch_mu;
+static uint64_t *g_scratch_ptr[64];
+
+static onebit_status_t scratch_address(int dev, uint64_t **out) {
+    if (dev < 0 || dev >= 64) return ONEBIT_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return ONEBIT_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = static_cast<uint64_t *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return ONEBIT_OK;
+}
+
+__global__ __launch_bounds__(256) void k_clear_words(uint64_t *p, int64_t words) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+__global__ void k_copy_word(uint64_t *dst, const uint64_t *src) {
+    if (threadIdx.x == 0) *dst = src ? ld_agent(src) : 0;
+}
+
+// What the allocation-free call adds around the shared dispatch: the scratch words
+// it clears before the kernels run, and the device word that receives the error
+// word after them (nullable).
+struct ScratchUse {
+    int64_t clear_words;
+    uint64_t *status_out;
+};
+
 }  // namespace onebit
 
 using namespace onebit;
 
 // Validation and dispatch shared by the fp32-momentum and the packed-momentum
-// entry points (exactly one of m and m_bits is given).
+// entry points (exactly one of m and m_bits is given), and by the allocation-free
+// call (sc non-null: workspace is the scratch).
 static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype, float *m,
                                       const uint32_t *m_bits, const float *m_scales, const uint8_t *m_mask,
                                       float *e, const float *v,
                                       float *x, uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
                                       double beta1, double eps, double weight_decay, void *workspace,
-                                      void *stream) {
+                                      void *stream, const ScratchUse *sc = nullptr);
+
+static onebit_status_t dispatch_compress(const onebit_plan_s *plan, const CompressArgs &a, onebit_dtype_t g_dtype,
+                                         bool packed, bool update, bool xb, hipStream_t s);
+
+static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype, float *m,
+                                      const uint32_t *m_bits, const float *m_scales, const uint8_t *m_mask,
+                                      float *e, const float *v,
+                                      float *x, uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
+                                      double beta1, double eps, double weight_decay, void *workspace,
+                                      void *stream, const ScratchUse *sc) {
     if (!plan) return ONEBIT_ERR_INVALID;
     if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
     const bool packed = m_bits != nullptr || m_scales != nullptr;
@@ -856,7 +915,13 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     if (update && (!v || !x)) return ONEBIT_ERR_INVALID;
     if (!update && x_bf16) return ONEBIT_ERR_INVALID;
     if (m_mask && !packed) return ONEBIT_ERR_INVALID;
-    if (plan->n_chunks == 0) return ONEBIT_OK;
+    if (sc && sc->status_out && !aligned_to(sc->status_out, 8)) return ONEBIT_ERR_ALIGN;
+    if (plan->n_chunks == 0) {
+        if (!sc || !sc->status_out) return ONEBIT_OK;
+        hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), sc->status_out,
+                           nullptr);
+        return hip_status(hipGetLastError());
+    }
     if (!scales || !workspace) return ONEBIT_ERR_INVALID;
     if (packed && (!m_scales || (plan->n > 0 && !m_bits) || m_scales == scales || (m_bits && m_bits == bits)))
         return ONEBIT_ERR_INVALID;
@@ -896,6 +961,25 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     a.slots = ws.slots;
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (sc) {
+        const int64_t blocks = std::min<int64_t>((sc->clear_words + 255) / 256, 1024);
+        hipLaunchKernelGGL(k_clear_words, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s,
+                           static_cast<uint64_t *>(workspace), sc->clear_words);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_status(e);
+    }
+    onebit_status_t st = dispatch_compress(plan, a, g_dtype, packed, update, x_bf16 != nullptr, s);
+    if (sc && sc->status_out) {
+        hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(64), 0, s, sc->status_out,
+                           static_cast<const uint64_t *>(workspace));
+        const hipError_t e = hipGetLastError();
+        if (st == ONEBIT_OK && e != hipSuccess) st = hip_status(e);
+    }
+    return st;
+}
+
+static onebit_status_t dispatch_compress(const onebit_plan_s *plan, const CompressArgs &a, onebit_dtype_t g_dtype,
+                                         bool packed, bool update, bool xb, hipStream_t s) {
     if (packed && !update) {
         switch (g_dtype) {
             case ONEBIT_BF16: return launch<kCompressPM, kGradBF16, false>(plan, a, s);
@@ -906,26 +990,26 @@ static onebit_status_t compress_entry(onebit_plan_t plan, const void *g, onebit_
     if (packed) {
         switch (g_dtype) {
             case ONEBIT_BF16:
-                return x_bf16 ? launch<kUpdatePM, kGradBF16, true>(plan, a, s)
-                              : launch<kUpdatePM, kGradBF16, false>(plan, a, s);
+                return xb ? launch<kUpdatePM, kGradBF16, true>(plan, a, s)
+                          : launch<kUpdatePM, kGradBF16, false>(plan, a, s);
             case ONEBIT_F16:
-                return x_bf16 ? launch<kUpdatePM, kGradF16, true>(plan, a, s)
-                              : launch<kUpdatePM, kGradF16, false>(plan, a, s);
+                return xb ? launch<kUpdatePM, kGradF16, true>(plan, a, s)
+                          : launch<kUpdatePM, kGradF16, false>(plan, a, s);
             default:
-                return x_bf16 ? launch<kUpdatePM, kGradF32, true>(plan, a, s)
-                              : launch<kUpdatePM, kGradF32, false>(plan, a, s);
+                return xb ? launch<kUpdatePM, kGradF32, true>(plan, a, s)
+                          : launch<kUpdatePM, kGradF32, false>(plan, a, s);
         }
     }
     switch (g_dtype) {
         case ONEBIT_BF16:
             if (!update) return launch<kCompressOnly, kGradBF16, false>(plan, a, s);
-            return x_bf16 ? launch<kUpdate, kGradBF16, true>(plan, a, s) : launch<kUpdate, kGradBF16, false>(plan, a, s);
+            return xb ? launch<kUpdate, kGradBF16, true>(plan, a, s) : launch<kUpdate, kGradBF16, false>(plan, a, s);
         case ONEBIT_F16:
             if (!update) return launch<kCompressOnly, kGradF16, false>(plan, a, s);
-            return x_bf16 ? launch<kUpdate, kGradF16, true>(plan, a, s) : launch<kUpdate, kGradF16, false>(plan, a, s);
+            return xb ? launch<kUpdate, kGradF16, true>(plan, a, s) : launch<kUpdate, kGradF16, false>(plan, a, s);
         default:
             if (!update) return launch<kCompressOnly, kGradF32, false>(plan, a, s);
-            return x_bf16 ? launch<kUpdate, kGradF32, true>(plan, a, s) : launch<kUpdate, kGradF32, false>(plan, a, s);
+            return xb ? launch<kUpdate, kGradF32, true>(plan, a, s) : launch<kUpdate, kGradF32, false>(plan, a, s);
     }
 }
 
@@ -947,6 +1031,24 @@ extern "C" onebit_status_t onebit_compress_update_packed(onebit_plan_t plan, con
     if (!m_scales) return ONEBIT_ERR_INVALID;
     return compress_entry(plan, g, g_dtype, nullptr, m_bits, m_scales, m_mask, e, v, x, x_bf16, bits, scales, lr,
                           beta1, eps, weight_decay, workspace, stream);
+}
+
+extern "C" onebit_status_t onebit_compress_update_static(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
+                                                         float *m, float *e, const float *v, float *x,
+                                                         uint16_t *x_bf16, uint32_t *bits, float *scales,
+                                                         double lr, double beta1, double eps, double weight_decay,
+                                                         uint64_t *wait_status, void *stream) {
+    if (!plan) return ONEBIT_ERR_INVALID;
+    const int64_t words = 1 + plan->n_chunks + plan->n_tiles;
+    if (words > kScratchWords) return ONEBIT_ERR_NOMEM;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return ONEBIT_ERR_INVALID;
+    uint64_t *ws = nullptr;
+    const onebit_status_t st = scratch_address(dev, &ws);
+    if (st != ONEBIT_OK) return st;
+    const ScratchUse sc{words, wait_status};
+    return compress_entry(plan, g, g_dtype, m, nullptr, nullptr, nullptr, e, v, x, x_bf16, bits, scales, lr, beta1,
+                          eps, weight_decay, ws, stream, &sc);
 }
 
 extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const uint32_t *worker_bits,

@@ -45,6 +45,7 @@ _SIGS = {
     "onebit_adam_warmup_step": (_I, [_P, _P, _P, _P, _I, _I64, _D, _D, _D, _D, _D, _I, _I64, _P]),
     "onebit_compress_update": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
     "onebit_compress_update_packed": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
+    "onebit_compress_update_static": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
     "onebit_momentum_update_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _P]),
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _I, _I, _P]),
@@ -284,6 +285,16 @@ def onebit_compress_update(plan, g, m, e, v, x, x_bf16, bits, scales, *, lr, bet
     _check(load().onebit_compress_update(plan.handle, _ptr(g), _dtype_code(g), _ptr(m), _ptr(e), _ptr(v), _ptr(x),
                                          _ptr(x_bf16), _ptr(bits), _ptr(scales), lr, beta1, eps, weight_decay,
                                          _ptr(workspace), _stream(stream)), "onebit_compress_update")
+
+
+def onebit_compress_update_static(plan, g, m, e, v, x, x_bf16, bits, scales, *, lr, beta1, eps, weight_decay,
+                                  wait_status=None, stream=None):
+    """onebit_compress_update without a workspace (the library's scratch instead);
+    wait_status: optional int64 device tensor of one element."""
+    _check(load().onebit_compress_update_static(plan.handle, _ptr(g), _dtype_code(g), _ptr(m), _ptr(e), _ptr(v),
+                                                _ptr(x), _ptr(x_bf16), _ptr(bits), _ptr(scales), lr, beta1, eps,
+                                                weight_decay, _ptr(wait_status), _stream(stream)),
+           "onebit_compress_update_static")
 
 
 def onebit_compress_update_packed(plan, g, m_bits, m_scales, e, v, x, x_bf16, bits, scales, *, lr, beta1, eps,

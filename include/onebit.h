@@ -227,6 +227,28 @@ onebit_status_t onebit_compress_update_packed(onebit_plan_t plan, const void *g,
                                               double beta1, double eps, double weight_decay,
                                               void *workspace, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): onebit_compress_update
+ * with the same arguments and results, minus the workspace.  Its kernels use an
+ * 8 MiB scratch area inside the library (one per device, held until the process
+ * ends) instead; the call itself allocates nothing.  Limit: the plan's chunks +
+ * tiles (one tile per 2048 elements of a chunk, rounded up) + 1 may not exceed
+ * 2^20 (about 2.1e9 elements); a larger plan returns ONEBIT_ERR_NOMEM and launches
+ * nothing.  Each call first clears the scratch words it uses (a kernel, no memset),
+ * so a failed earlier call does not affect it.  wait_status: nullable DEVICE
+ * uint64, 8-byte aligned; it receives the call's error word after the call's
+ * kernels (0: every cross-workgroup wait ended normally; non-zero: a bounded wait
+ * gave up and the outputs are not valid; 0 for a plan with no chunks).  Every call
+ * on one GPU shares that GPU's scratch: calls that may overlap in time on one GPU
+ * (several streams or host threads) race and give unspecified results.  Errors as
+ * onebit_compress_update, plus ONEBIT_ERR_HIP if the scratch's address cannot be
+ * obtained. */
+onebit_status_t onebit_compress_update_static(onebit_plan_t plan, const void *g, onebit_dtype_t g_dtype,
+                                              float *m, float *e, const float *v, float *x,
+                                              uint16_t *x_bf16, uint32_t *bits, float *scales, double lr,
+                                              double beta1, double eps, double weight_decay,
+                                              uint64_t *wait_status, void *stream);
+
 /* Server stage of the compressed all-reduce over W workers' streams held in one
  * GPU's memory ([DSG] sec. 4, server_error; [1BA] "proposed method"):
  *   a_i = fl32( (sum_{w=0..W-1} (bit_{w,i} ? -s_{w,j} : +s_{w,j})) / W )   (fp64)
