@@ -800,10 +800,10 @@ def main():
         profile_quantizers()
         return
     if args.profile_allreduce:
-        profile_allreduce(max(1, min(args.steps, 3)))
+        profile_allreduce(max(1, min(args.steps, 10)))
         return
     if args.profile:
-        profile_mode(max(1, min(args.steps, 5)))
+        profile_mode(max(1, min(args.steps, 20)))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
