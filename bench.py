@@ -333,7 +333,8 @@ def cpu_row_baselines(rows, budget_s=1.0):
 
     scale = a.n / n * 1e3
     for key, grads, fin in (("allreduce_16x64M", gs, False), ("full_step_16x64M_f16_mask", g16, True),
-                            ("full_step_16x64M_f16_mask_packed_m", g16, True)):
+                            ("full_step_16x64M_f16_mask_packed_m", g16, True),
+                            ("driver_workers_16x64M_f16_mask_packed_m", g16, True)):
         r, c = _oracle_rate(lambda: exchange(grads, fin), 1.0, budget_s)
         put(key, scale / r, "ms_per_step", f"{a.W} workers over a {n}-element sample, time scaled by {a.n // n}", c)
 
@@ -1201,7 +1202,22 @@ def secondary_rows(dev, args):
     t2, _ = timed(gpu_share_packed, steps, 1)
     rows["gpu_share_of_16_64M_f16_mask"] = dict(ms_per_step=t1 * 1e3, params_per_s=a.n / t1)
     rows["gpu_share_of_16_64M_f16_mask_packed_m"] = dict(ms_per_step=t2 * 1e3, params_per_s=a.n / t2)
-    del m, e, es, g16, v, x, mask, wbits, wsc, sbits, ssc, wsp, plan, pb, pss, plan_s, ws_s, wbits_s, wsc_s, es_s
+    del m, e, es, v, wbits, wsc, sbits, ssc, wsp, plan, pb, pss, plan_s, ws_s, wbits_s, wsc_s, es_s
+    torch.cuda.empty_cache()
+    # the same full step through the driver (OneBitAdamWorkers: worker and server
+    # errors, element mask, packed momentum after its first compressed step); the
+    # error word is read once after the timed steps instead of after every step
+    from error_compensated_bit_amd.optimizer import OneBitAdamWorkers
+    drv = OneBitAdamWorkers(x, a.W, chunk_offsets=a.chunk_off, exp_avg_mask=mask, lr=1e-3, eps=1e-8,
+                            weight_decay=0.01, freeze_step=0, packed_momentum=True, check_every=0)
+    drv.v.copy_(torch.rand(a.n, device=dev) * 1e-6 + 1e-7)
+    gd = drv.gradient_buffer(torch.float16)
+    gd.copy_(g16)
+    del g16
+    t, _ = timed(lambda: drv.step(gd), steps, 2)
+    drv.check()
+    rows["driver_workers_16x64M_f16_mask_packed_m"] = dict(ms_per_step=t * 1e3, params_per_s=a.n / t)
+    del drv, gd, x, mask
     torch.cuda.empty_cache()
     log(f"[bench] allreduce {rows['allreduce_16x64M']} full step {rows['full_step_16x64M_f16_mask']} "
         f"packed {rows['full_step_16x64M_f16_mask_packed_m']} one GPU's share "

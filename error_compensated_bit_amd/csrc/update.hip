@@ -6,6 +6,8 @@
 // and 8 written with one (the masked momentum is stored back), plus 2 written for
 // the optional bf16 copy of x.  Per group of four elements: one 128-bit access for
 // each fp32 array, one 32-bit mask load, one 64-bit bf16 store.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -161,9 +163,159 @@ __global__ __launch_bounds__(256) void k_momentum_update_packed(PackedUpdateArgs
     }
 }
 
+// Decompression of a plan's sign words and chunk scales into fp32 (the
+// all-gather-decompress of the compressed all-reduce): out = +-scale times the
+// mask, with the tile layout of the packed finish.
+struct DecompressArgs {
+    const TileDesc *tiles;
+    int64_t n_tiles;
+    const uint32_t *bits;
+    const float *scales;
+    const uint8_t *mask;
+    float *out;
+};
+
+__global__ __launch_bounds__(256) void k_decompress(DecompressArgs a) {
+    for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+        const TileDesc t = a.tiles[tile];
+        if (t.len == 0) continue;
+        const float s = a.scales[t.chunk];
+        const bool full = t.len == kTile && (t.start & 3) == 0;
+#pragma unroll
+        for (int r = 0; r < kGroups; ++r) {
+            const uint32_t k0 = 4u * (threadIdx.x + kBlock * r);
+            if (k0 >= (uint32_t)t.len) continue;
+            const uint32_t nib = a.bits[t.word + (k0 >> 5)] >> (k0 & 31u);
+            const int64_t i0 = t.start + k0;
+            float o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool in = k0 + q < (uint32_t)t.len;
+                const float mq = ((nib >> q) & 1u) ? -s : s;
+                o[q] = a.mask ? mul_rn(mq, (in && a.mask[i0 + q] != 0) ? 1.0f : 0.0f) : mq;
+            }
+            if (full) {
+                st_stream(reinterpret_cast<float4 *>(a.out + i0), make_float4(o[0], o[1], o[2], o[3]));
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (k0 + q < (uint32_t)t.len) a.out[i0 + q] = o[q];
+            }
+        }
+    }
+}
+
+// The workers' full-precision gradient average of the warmup phase (the
+// all-reduce, simulated over W rows in one GPU's memory): fp64 sum in worker order,
+// one division by W, one rounding.  Four elements per thread and row per
+// iteration, the rows' loads of a group issued before they are summed.
+struct AverageArgs {
+    const void *g;
+    int64_t row_stride;
+    int64_t n;
+    int32_t W;
+    double invW;  // 1 / W when W is a power of two (exact), else 0
+    float *out;
+};
+
+template <int GT>
+__device__ __forceinline__ void load_row4(const AverageArgs &a, int w, int64_t i0, bool full, double (&acc)[4]) {
+    float f[4];
+    if (full) {
+        if (GT == kGradF32) {
+            const float4 t = ld_stream(reinterpret_cast<const float4 *>(static_cast<const float *>(a.g) + w * a.row_stride + i0));
+            f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
+        } else {
+            const uint2 t = ld_stream(reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.g) + w * a.row_stride + i0));
+            f[0] = half_bits_to_float<GT>(t.x & 0xffffu);
+            f[1] = half_bits_to_float<GT>(t.x >> 16);
+            f[2] = half_bits_to_float<GT>(t.y & 0xffffu);
+            f[3] = half_bits_to_float<GT>(t.y >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t i = i0 + q;
+            f[q] = i < a.n ? (GT == kGradF32 ? static_cast<const float *>(a.g)[w * a.row_stride + i]
+                                             : half_bits_to_float<GT>(static_cast<const uint16_t *>(a.g)[w * a.row_stride + i]))
+                           : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = __dadd_rn(acc[q], (double)f[q]);
+}
+
+template <int GT>
+__global__ __launch_bounds__(256) void k_average_rows(AverageArgs a) {
+    const int64_t groups = (a.n + 3) / 4;
+    const bool vec = ((uintptr_t)a.g & 15u) == 0 && (a.row_stride & 3) == 0;
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < groups; q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i0 = 4 * q;
+        const bool full = vec && i0 + 4 <= a.n;
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int w = 0; w < a.W; ++w) load_row4<GT>(a, w, i0, full, acc);
+        float o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = (float)(a.invW != 0.0 ? __dmul_rn(acc[k], a.invW) : __ddiv_rn(acc[k], (double)a.W));
+        if (full) {
+            st_stream(reinterpret_cast<float4 *>(a.out + i0), make_float4(o[0], o[1], o[2], o[3]));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (i0 + k < a.n) a.out[i0 + k] = o[k];
+        }
+    }
+}
+
+static int64_t grid_for(int64_t work_items, int per_cu) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    int64_t blocks = (work_items + 255) / 256;
+    const int64_t cap = (int64_t)cus * per_cu;
+    if (blocks > cap) blocks = cap;
+    return blocks < 1 ? 1 : blocks;
+}
+
 }  // namespace onebit
 
 using namespace onebit;
+
+extern "C" onebit_status_t onebit_decompress(onebit_plan_t plan, const uint32_t *bits, const float *scales,
+                                             const uint8_t *mask, float *out, void *stream) {
+    if (!plan) return ONEBIT_ERR_INVALID;
+    if (plan->n == 0) return ONEBIT_OK;
+    if (!bits || !scales || !out) return ONEBIT_ERR_INVALID;
+    if (!aligned_to(bits, 4) || !aligned_to(scales, 4) || !aligned16(out)) return ONEBIT_ERR_ALIGN;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return ONEBIT_ERR_INVALID;
+    DecompressArgs a{plan->d_tiles, plan->n_tiles, bits, scales, mask, out};
+    const int64_t blocks = std::min<int64_t>(plan->n_tiles, grid_for(plan->n_tiles * 256, 8));
+    hipLaunchKernelGGL(k_decompress, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" onebit_status_t onebit_average_rows(const void *g, onebit_dtype_t g_dtype, int W, int64_t row_stride,
+                                               int64_t n, float *out, void *stream) {
+    if (n < 0 || W < 1 || W > 65536) return ONEBIT_ERR_INVALID;
+    if (g_dtype != ONEBIT_F32 && g_dtype != ONEBIT_BF16 && g_dtype != ONEBIT_F16) return ONEBIT_ERR_INVALID;
+    if (n == 0) return ONEBIT_OK;
+    if (!g || !out || (W > 1 && row_stride < n)) return ONEBIT_ERR_INVALID;
+    if (!aligned16(out)) return ONEBIT_ERR_ALIGN;
+    AverageArgs a{g, W > 1 ? row_stride : 0, n, W, (W & (W - 1)) == 0 ? 1.0 / (double)W : 0.0, out};
+    const dim3 grid((unsigned)grid_for((n + 3) / 4, 8)), block(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (g_dtype == ONEBIT_BF16)
+        hipLaunchKernelGGL(k_average_rows<kGradBF16>, grid, block, 0, s, a);
+    else if (g_dtype == ONEBIT_F16)
+        hipLaunchKernelGGL(k_average_rows<kGradF16>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(k_average_rows<kGradF32>, grid, block, 0, s, a);
+    return hip_status(hipGetLastError());
+}
 
 extern "C" onebit_status_t onebit_momentum_update_packed(onebit_plan_t plan, const uint32_t *m_bits,
                                                          const float *m_scales, const uint8_t *mask, const float *v,

@@ -50,6 +50,8 @@ _SIGS = {
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _I, _I, _P]),
     "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
+    "onebit_decompress": (_I, [_P, _P, _P, _P, _P, _P]),
+    "onebit_average_rows": (_I, [_P, _I, _I, _I64, _I64, _P, _P]),
     "qsgd_quantize": (_I, [_P, _I, _I64, _I, _I, _U64, _P, _P, _P]),
     "qsgd_reduce": (_I, [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P, _P]),
     "loco_quantize": (_I, [_P, _I, _P, _I64, _I, _I, _D, _U64, _P, _P, _P]),
@@ -347,6 +349,20 @@ def onebit_momentum_update(m, mask, v, x, x_bf16, *, lr, eps, weight_decay, stre
     """mask: uint8 (or bool) tensor of n elements, or None."""
     _check(load().onebit_momentum_update(_ptr(m), _ptr(mask), _ptr(v), _ptr(x), _ptr(x_bf16), x.numel(), lr, eps,
                                          weight_decay, _stream(stream)), "onebit_momentum_update")
+
+
+def onebit_decompress(plan, bits, scales, mask, out, stream=None):
+    _check(load().onebit_decompress(plan.handle, _ptr(bits), _ptr(scales), _ptr(mask), _ptr(out), _stream(stream)),
+           "onebit_decompress")
+
+
+def onebit_average_rows(g, out, stream=None):
+    """g: [W, n] (or 1-D for one row) fp32, bf16 or fp16 tensor with contiguous rows; out: fp32 [n]."""
+    W = g.shape[0] if g.dim() == 2 else 1
+    n = g.shape[-1]
+    stride = g.stride(0) if g.dim() == 2 else n
+    _check(load().onebit_average_rows(_ptr(g), _dtype_code(g), W, stride, n, _ptr(out), _stream(stream)),
+           "onebit_average_rows")
 
 
 def qsgd_quantize(g, bucket, bits, seed, codes, norms, stream=None):

@@ -290,6 +290,28 @@ onebit_status_t onebit_momentum_update_packed(onebit_plan_t plan, const uint32_t
                                               float *x, uint16_t *x_bf16, double lr, double eps,
                                               double weight_decay, void *stream);
 
+/* Decompression of a plan's sign words and chunk scales (the all-gather-decompress
+ * of the compressed all-reduce, [DSG] sec. 4: every value travels as one bit and
+ * is rebuilt as +-scale; sec. 3.5: the momentum is then masked per element):
+ *   out_i = (bit_i ? -scales[j] : +scales[j]) * (mask_i ? 1 : 0)   (mask nullable: +-scales[j])
+ * with the product one binary32 multiplication (a masked negative value gives -0,
+ * as onebit_momentum_update leaves it).  bits: uint32 [plan_words], 4-byte aligned;
+ * scales: fp32 [n_chunks]; mask: uint8 [n]; out: fp32 [n], 16-byte aligned. */
+onebit_status_t onebit_decompress(onebit_plan_t plan, const uint32_t *bits, const float *scales,
+                                  const uint8_t *mask, float *out, void *stream);
+
+/* The full-precision gradient exchange of the warmup phase ([DSG] sec. 4, phase
+ * one: Adam runs on the workers' averaged gradient), simulated over W workers'
+ * gradients held in one GPU's memory:
+ *   out_i = fl32( (sum_{w=0..W-1} g_{w,i}) / W )
+ * with the sum in fp64 in worker order (each value widened exactly), one fp64
+ * division (a product with 1/W when W is a power of two, the same value), one
+ * rounding.  g: W rows of n fp32, bf16 or fp16 values, row w starting
+ * w * row_stride elements after g (row_stride >= n when W > 1); out: fp32 [n],
+ * 16-byte aligned.  1 <= W <= 65536. */
+onebit_status_t onebit_average_rows(const void *g, onebit_dtype_t g_dtype, int W, int64_t row_stride, int64_t n,
+                                    float *out, void *stream);
+
 /* QSGD gradient quantizer, the gradient side of QSDP ([QSDP] "proposed method":
  * gradients take the standard unbiased compressor of Alistarh et al. 2017; [QSGD]
  * sec. 3.1), per bucket of `bucket` elements (the last one may be short):

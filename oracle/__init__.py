@@ -43,6 +43,7 @@ def _load():
         lib.oracle_qsgd_reduce.argtypes = [_I, _P, _I64, _P, _I64, _I64, _I, _I, _P, _P]
         lib.oracle_loco_quantize.argtypes = [_P, _I, _P, _I64, _I, _I, _D, C.c_uint64, _I64, _P, _P]
         lib.oracle_momentum_update.argtypes = [_P, _P, _P, _P, _P, _I64, _D, _D, _D]
+        lib.oracle_average_rows.argtypes = [_P, _I, _I64, _I64, _P]
         lib.oracle_philox4x32_10.argtypes = [_P, _P, _P]
         lib.oracle_philox4x32_10.restype = None
         lib.oracle_qsdp_uniform.argtypes = [C.c_uint64, _I64]
@@ -53,7 +54,7 @@ def _load():
         lib.oracle_f32_to_bf16.restype = C.c_uint16
         for name in ("oracle_adam_warmup_step", "oracle_compress_update", "oracle_server_reduce",
                      "oracle_momentum_update", "oracle_qsgd_quantize", "oracle_qsgd_reduce",
-                     "oracle_loco_quantize",
+                     "oracle_loco_quantize", "oracle_average_rows",
                      "oracle_decompress", "oracle_qsdp_quantize", "oracle_qsdp_dequantize"):
             getattr(lib, name).restype = C.c_int
         _lib = lib
@@ -290,3 +291,17 @@ def loco_quantize(g, err_avg, *, bucket, bits, beta, seed, first_index=0):
     _check(lib.oracle_loco_quantize(_ptr(g), dt, _ptr(err_avg), n, bucket, bits, beta, seed, first_index,
                                     _ptr(codes), _ptr(norms)), "loco_quantize")
     return codes[:nbytes], norms[:nb]
+
+
+def average_rows(g):
+    """Mean over the rows of g ([W, n] float32, or bf16 bit patterns as uint16, widened
+    exactly) as the warmup phase's full-precision exchange forms it.  Returns fp32 [n]."""
+    lib = _load()
+    g = np.atleast_2d(g)
+    if g.dtype == np.uint16:
+        g = (g.astype(np.uint32) << 16).view(np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    W, n = g.shape
+    out = np.zeros(max(n, 1), dtype=np.float32)
+    _check(lib.oracle_average_rows(_ptr(g), W, n, n, _ptr(out)), "average_rows")
+    return out[:n]

@@ -660,6 +660,29 @@ int oracle_qsgd_reduce(int W, const uint8_t *codes, int64_t code_stride, const f
     return ORACLE_OK;
 }
 
+/* ------------------------------------- O9: the warmup phase's gradient average
+ * [DSG] sec. 4, phase one: the Adam step runs on the gradient averaged over the
+ * workers at full precision.  Reading: out_i = fl32( (sum_w g_{w,i}) / W ), the sum
+ * taken in fp64 in worker order 0..W-1 (each fp32 value exact in fp64), one fp64
+ * division, one rounding.  Row w of g starts w * row_stride values after g. */
+int oracle_average_rows(const float *g, int W, int64_t row_stride, int64_t n, float *out)
+{
+    if (W < 1 || n < 0 || (W > 1 && row_stride < n))
+        return ORACLE_ERR_INVALID;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!g || !out)
+        return ORACLE_ERR_INVALID;
+    for (int64_t i = 0; i < n; ++i) {
+        double sum = 0.0;
+        for (int w = 0; w < W; ++w)
+            sum += (double)g[(int64_t)w * row_stride + i];
+        const double mean = sum / (double)W;
+        out[i] = (float)mean;
+    }
+    return ORACLE_OK;
+}
+
 /* ------------------------------- O8: LoCo-style compensated gradient quantizer
  * [LOCO] method details, steps 2-4: estimate the compression error by the moving
  * average of past errors, add it to the gradient, compress the sum.  Reading

@@ -123,3 +123,86 @@ def test_error_word_is_checked_every_n_compressed_steps_and_raises(calls):
     never.workspace[0] = 1
     never.step(torch.zeros(4))
     assert calls == [("compress", [0, 4], 0.9, 1e-3)]
+
+
+@pytest.fixture
+def wcalls(monkeypatch):
+    """Recorders for the W-worker driver's library calls."""
+    log = []
+    monkeypatch.setattr(ob, "onebit_plan_create", lambda co, to=None, tk=None: ("plan", np.asarray(co).tolist()))
+    monkeypatch.setattr(ob, "onebit_plan_words", lambda p: 3)
+    monkeypatch.setattr(ob, "onebit_plan_chunks", lambda p: 2)
+    monkeypatch.setattr(ob, "onebit_plan_workspace_bytes", lambda p: 64)
+    monkeypatch.setattr(ob, "onebit_average_rows", lambda g, out, stream=None: log.append(("average", g.shape[0])))
+    monkeypatch.setattr(ob, "onebit_adam_warmup_step", lambda x, m, v, g, **k: log.append(("warmup", k["step"])))
+
+    def comp(plan, g, m, e, v, x, xb, bits, scales, **k):
+        assert v is None and x is None and xb is None and k["lr"] == 0.0
+        log.append(("worker", "fp32"))
+
+    def comp_packed(plan, g, mb, ms, e, v, x, xb, bits, scales, **k):
+        assert v is None and x is None and xb is None
+        log.append(("worker", "packed", id(mb)))
+
+    def server(plan, wb, ws, es, sb, ss, m_out, wsp, stream=None):
+        log.append(("server", m_out is not None, id(sb)))
+
+    monkeypatch.setattr(ob, "onebit_compress_update", comp)
+    monkeypatch.setattr(ob, "onebit_compress_update_packed", comp_packed)
+    monkeypatch.setattr(ob, "onebit_server_reduce", server)
+    monkeypatch.setattr(ob, "onebit_momentum_update", lambda m, mask, v, x, xb, **k: log.append(("finish", "fp32")))
+    monkeypatch.setattr(ob, "onebit_momentum_update_packed",
+                        lambda plan, mb, ms, mask, v, x, xb, **k: log.append(("finish", "packed", id(mb))))
+    monkeypatch.setattr(ob, "onebit_workspace_status", lambda ws, stream=None: log.append(("status",)) or 0)
+    monkeypatch.setattr(ob, "onebit_decompress", lambda plan, b, s, mask, out, stream=None: log.append(("decompress",)))
+    return log
+
+
+def test_workers_phases_and_call_sequence(wcalls):
+    o = opt.OneBitAdamWorkers(torch.zeros(10), 3, chunk_offsets=[0, 4, 10], freeze_step=2)
+    g = o.gradient_buffer()
+    for _ in range(4):
+        o.step(g)
+    kinds = [c[0] for c in wcalls]
+    assert kinds == ["average", "warmup", "average", "warmup",
+                     "worker", "worker", "worker", "server", "finish", "status",
+                     "worker", "worker", "worker", "server", "finish", "status"]
+    assert all(c[1] == "fp32" for c in wcalls if c[0] in ("worker", "finish"))
+    assert all(c[1] is True for c in wcalls if c[0] == "server")          # m_out written
+    assert o.worker_error.shape == (3, 10) and o.server_error.shape == (10,)
+    with pytest.raises(ValueError):
+        o.step(torch.zeros(2, 10))
+
+
+def test_workers_packed_momentum_alternates_pairs_and_checkpoint_resets_errors(wcalls):
+    o = opt.OneBitAdamWorkers(torch.zeros(8), 2, freeze_step=0, packed_momentum=True,
+                              exp_avg_mask=torch.ones(8, dtype=torch.bool))
+    g = o.gradient_buffer()
+    for _ in range(3):
+        o.step(g)
+    steps = [c for c in wcalls if c[0] != "status"]
+    b0, b1 = id(o.server_bits[0]), id(o.server_bits[1])
+    # step 1: fp32 momentum, server writes pair 0; step 2: workers read pair 0, server writes 1; step 3: read 1, write 0
+    assert steps[:4] == [("worker", "fp32"), ("worker", "fp32"), ("server", True, b0), ("finish", "fp32")]
+    assert steps[4:8] == [("worker", "packed", b0), ("worker", "packed", b0), ("server", False, b1),
+                          ("finish", "packed", b1)]
+    assert steps[8:12] == [("worker", "packed", b1), ("worker", "packed", b1), ("server", False, b0),
+                           ("finish", "packed", b0)]
+    o.worker_error.fill_(1.0)
+    o.server_error.fill_(2.0)
+    sd = o.state_dict()
+    assert wcalls[-1] == ("decompress",) and set(sd) == {"step", "exp_avg", "exp_avg_sq"}
+    o.load_state_dict(sd)
+    assert o.current is None and torch.count_nonzero(o.worker_error) == 0 and torch.count_nonzero(o.server_error) == 0
+    wcalls.clear()
+    o.step(g)
+    assert wcalls[0] == ("worker", "fp32")
+
+
+def test_workers_rejects_bad_arguments(wcalls):
+    with pytest.raises(ValueError):
+        opt.OneBitAdamWorkers(torch.zeros(4), 0)
+    with pytest.raises(ValueError):
+        opt.OneBitAdamWorkers(torch.zeros(4), 2, exp_avg_mask=torch.ones(3, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        opt.OneBitAdamWorkers(torch.zeros(4), 2, exp_avg_mask=torch.ones(4, dtype=torch.float32))

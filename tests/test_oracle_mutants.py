@@ -13,6 +13,7 @@ import pytest
 import oracle
 from oracle import build as obuild
 
+import test_oracle_average as TA
 import test_oracle_compress as TC  # noqa: E402
 import test_oracle_qsdp as TQ
 import test_oracle_loco as TL
@@ -71,6 +72,12 @@ def _loco():
     TL.test_moving_average_closed_form(0.9)
 
 
+def _avg():
+    TA.test_one_row_copies_and_negation()
+    TA.test_exact_mean_rounded_once(3, False)
+    TA.test_exact_mean_rounded_once(5, True)
+
+
 def _finish():
     TS.test_worker_server_finish_composition_equals_fused_step()
     TS.test_momentum_update_mask_and_closed_form()
@@ -127,6 +134,11 @@ MUTANTS = [
      "err_avg[i] = one_minus_beta * err_avg[i] + beta * (h[i] - y[i]);", _loco),
     ("loco error sign", "err_avg[i] = beta * err_avg[i] + one_minus_beta * (h[i] - y[i]);",
      "err_avg[i] = beta * err_avg[i] + one_minus_beta * (y[i] - h[i]);", _loco),
+    ("average summed in fp32", "            sum += (double)g[(int64_t)w * row_stride + i];",
+     "            sum = (double)((float)sum + g[(int64_t)w * row_stride + i]);", _avg),
+    ("average not divided", "        const double mean = sum / (double)W;", "        const double mean = sum;", _avg),
+    ("average skips the last row", "        for (int w = 0; w < W; ++w)\n            sum +=",
+     "        for (int w = 0; w + 1 < W; ++w)\n            sum +=", _avg),
     ("finish ignores the mask", "m[i] = m[i] * (mask[i] ? 1.0f : 0.0f);", "m[i] = m[i];", _finish),
     ("finish weight decay sign", "const float update = m[i] / (sqrtf(v[i]) + eps) + weight_decay * x[i];",
      "const float update = m[i] / (sqrtf(v[i]) + eps) - weight_decay * x[i];", _finish),
