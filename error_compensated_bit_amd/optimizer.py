@@ -296,3 +296,69 @@ class OneBitAdamWorkers:
         self.current = None
         self.worker_error.zero_()
         self.server_error.zero_()
+
+
+def variance_update_steps(var_freeze_step, var_update_scaler):
+    """The steps (1-based) at which 0/1 Adam's adaptive variance freezing updates v.
+
+    The DeepSpeed guide (sec. 8, from 1-bit Adam to 0/1 Adam) names the method's
+    adaptive variance freezing and its parameters var_freeze_step and
+    var_update_scaler, but gives no rule.  Reading taken here: v is updated at step 1;
+    the spacing between consecutive updates starts at 1 step and doubles after every
+    var_update_scaler updates (var_update_scaler spacings of 1, then as many of 2,
+    then of 4, ...); no update comes after var_freeze_step, from which on v stays
+    frozen.
+    """
+    if var_update_scaler < 1 or var_freeze_step < 0:
+        raise ValueError("var_update_scaler must be >= 1 and var_freeze_step >= 0")
+    steps, t = [], 1
+    while t <= var_freeze_step:
+        # after update j (0-based) the next one is 2^(j // var_update_scaler) steps later
+        t_next = t + (1 << (len(steps) // var_update_scaler))
+        steps.append(t)
+        t = t_next
+    return steps
+
+
+class ZeroOneAdam(OneBitAdam):
+    """0/1 Adam's adaptive variance freezing over one flat vector (a reading: the
+    guide names the method and its parameters only; see variance_update_steps).
+
+    At the variance-update steps the step is full-precision Adam (m and v updated,
+    onebit_adam_warmup_step); every other step is the error-compensated 1-bit
+    compressed momentum step with the current v held fixed (onebit_compress_update),
+    and after var_freeze_step v never changes again.  The compression error carries
+    over the full-precision steps unchanged.  With var_update_scaler large enough that
+    the spacing never doubles before var_freeze_step, every step up to it updates v
+    and this is 1-bit Adam with freeze_step = var_freeze_step.  The guide's local
+    steps (local_step_scaler, local_step_clipper) skip the synchronization between
+    GPUs and are not modelled on one GPU.
+    """
+
+    def __init__(self, x, *, var_freeze_step=100000, var_update_scaler=16, **kw):
+        if "freeze_step" in kw:
+            raise TypeError("ZeroOneAdam takes var_freeze_step, not freeze_step")
+        super().__init__(x, freeze_step=var_freeze_step, **kw)
+        self.var_update_scaler = int(var_update_scaler)
+        self._var_steps = set(variance_update_steps(self.freeze_step, self.var_update_scaler))
+
+    def is_variance_step(self, t: int) -> bool:
+        return t in self._var_steps
+
+    def step(self, g, stream=None):
+        if g.numel() != self.x.numel():
+            raise ValueError("gradient and parameters differ in length")
+        t = self.step_count + 1
+        if self.is_variance_step(t):
+            ob.onebit_adam_warmup_step(self.x, self.m, self.v, g, lr=self.lr, beta1=self.beta1, beta2=self.beta2,
+                                       eps=self.eps, weight_decay=self.weight_decay,
+                                       bias_correction=self.bias_correction, step=t, stream=stream)
+            self.step_count = t
+            return
+        ob.onebit_compress_update(self.plan, g, self.m, self.e, self.v, self.x, None, self.bits, self.scales,
+                                  lr=self.lr, beta1=self.beta1, eps=self.eps, weight_decay=self.weight_decay,
+                                  workspace=self.workspace, stream=stream)
+        self.compressed_steps += 1
+        self.step_count = t
+        if self.check_every > 0 and self.compressed_steps % self.check_every == 0:
+            _check_workspace(self, stream)

@@ -136,3 +136,40 @@ def test_driver_raises_on_a_failed_wait_and_recovers_from_a_checkpoint():
     o.step(torch.from_numpy(grads[2]).to(DEV))
     r.step(grads[2])
     check("step 3 after the reload", o, r, x_prev)
+
+
+def test_zero_one_adam_variance_schedule_through_the_driver():
+    """0/1 Adam's adaptive variance freezing as read here (the guide names only the
+    method and its parameters; parity unpinned as to the method): var_freeze_step = 10,
+    var_update_scaler = 2, so v is updated at steps 1, 2, 3, 5, 7 (spacings 1, 1, 2, 2,
+    4) by full-precision Adam steps and every other step is the compressed step with
+    the current v.  The driver matches the oracle run through that schedule for 14
+    steps: m, v and the error bit for bit, x within tolerance."""
+    from error_compensated_bit_amd.optimizer import ZeroOneAdam
+    off = W.offsets_from_sizes([5000, 2 * 4096 + 1, 70001])
+    n = int(off[-1])
+    rng = np.random.default_rng(13)
+    x0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hp = dict(W.HYPER, weight_decay=0.01)
+    o = ZeroOneAdam(torch.from_numpy(x0.copy()).to(DEV), chunk_offsets=off, lr=hp["lr"],
+                    betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=hp["weight_decay"],
+                    var_freeze_step=10, var_update_scaler=2)
+    var_steps = {1, 2, 3, 5, 7}
+    x, m, v, e = x0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, 15):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        x_prev = x.copy()
+        o.step(torch.from_numpy(g).to(DEV))
+        if t in var_steps:
+            oracle.adam_warmup_step(x, m, v, g, lr=hp["lr"], beta1=hp["beta1"], beta2=hp["beta2"], eps=hp["eps"],
+                                    weight_decay=hp["weight_decay"], bias_correction=False, step=t)
+        else:
+            oracle.compress_update(off, g, m, e, v, x, lr=hp["lr"], beta1=hp["beta1"], eps=hp["eps"],
+                                   weight_decay=hp["weight_decay"])
+        torch.cuda.synchronize()
+        tag = f"0/1 Adam step {t} ({'variance update' if t in var_steps else 'compressed'})"
+        say(f"  {tag}")
+        assert_exact(f"{tag} m", host(o.m), m)
+        assert_exact(f"{tag} v", host(o.v), v)
+        assert_exact(f"{tag} e", host(o.e), e)
+        check_x(f"{tag} x", host(o.x), x, x_prev)

@@ -206,3 +206,43 @@ def test_workers_rejects_bad_arguments(wcalls):
         opt.OneBitAdamWorkers(torch.zeros(4), 2, exp_avg_mask=torch.ones(3, dtype=torch.uint8))
     with pytest.raises(ValueError):
         opt.OneBitAdamWorkers(torch.zeros(4), 2, exp_avg_mask=torch.ones(4, dtype=torch.float32))
+
+
+def closed_form_variance_steps(freeze, kappa):
+    """Update k (0-based) sits at 1 + sum_{j<k} 2^floor(j / kappa); with k = q kappa + r
+    that sum is kappa (2^q - 1) + r 2^q."""
+    out, k = [], 0
+    while True:
+        q, r = divmod(k, kappa)
+        t = 1 + kappa * (2 ** q - 1) + r * 2 ** q
+        if t > freeze:
+            return out
+        out.append(t)
+        k += 1
+
+
+@pytest.mark.parametrize("freeze,kappa", [(0, 1), (1, 1), (100, 1), (1000, 16), (37, 3), (5000, 7)])
+def test_variance_schedule_closed_form(freeze, kappa):
+    steps = opt.variance_update_steps(freeze, kappa)
+    assert steps == closed_form_variance_steps(freeze, kappa)
+    if kappa == 1 and freeze >= 1:
+        assert steps == [2 ** i for i in range(freeze.bit_length()) if 2 ** i <= freeze]
+
+
+def test_zero_one_adam_reduces_to_one_bit_adam_without_doubling(calls):
+    o = opt.ZeroOneAdam(torch.zeros(4), var_freeze_step=5, var_update_scaler=10)
+    for _ in range(7):
+        o.step(torch.zeros(4))
+    assert [c[0] for c in calls if c[0] != "status"] == ["warmup"] * 5 + ["compress"] * 2
+
+
+def test_zero_one_adam_alternates_by_the_schedule(calls):
+    o = opt.ZeroOneAdam(torch.zeros(4), var_freeze_step=20, var_update_scaler=2)
+    for _ in range(24):
+        o.step(torch.zeros(4))
+    kinds = [c for c in calls if c[0] in ("warmup", "compress")]
+    var_steps = [c[1] for c in kinds if c[0] == "warmup"]
+    assert var_steps == [1, 2, 3, 5, 7, 11, 15] == opt.variance_update_steps(20, 2)
+    assert len(kinds) == 24
+    with pytest.raises(TypeError):
+        opt.ZeroOneAdam(torch.zeros(4), freeze_step=3)
