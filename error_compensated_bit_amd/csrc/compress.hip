@@ -126,8 +126,9 @@ __device__ __forceinline__ void load4(const float *base, uint32_t k0, float (&v)
 // Server tiles: average of the W workers' decompressed values, summed in fp64 in
 // worker order 0..W-1.  Workers are taken kWBatch at a time: their scales for the
 // chunk and the tile's packed words are staged in LDS (each worker's words load as
-// one 256-byte run), then every thread adds +-s for its elements, forming -s by
-// flipping the sign bit of s.
+// one 256-byte run), then every thread adds +-s for its elements as fma(+-1, s,
+// acc), the +-1.0 built from the sign bit in two instructions (server 0.304 ->
+// 0.294 ms on 16 x 64M against a sign-bit xor on s).
 constexpr int kWBatch = 16;
 constexpr int kTileWords = kTile / 32;
 
@@ -164,12 +165,16 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
             const uint32_t wi = k0 >> 5;
             const uint32_t sh = k0 & 31u;
             for (int w = 0; w < wn; ++w) {
-                const uint32_t bw = s_words[w * kTileWords + wi] >> sh;
-                const long long sb = __double_as_longlong(s_wscale_d[w]);
+                const uint32_t word = s_words[w * kTileWords + wi];
+                const double sw = s_wscale_d[w];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const long long flip = (long long)((bw >> q) & 1u) << 63;
-                    acc[4 * r + q] = __dadd_rn(acc[4 * r + q], __longlong_as_double(sb ^ flip));
+                    // +-1.0 from bit sh + q of the word: the bit shifted into the sign,
+                    // 1.0's exponent field or-ed in ((a & b) | c, truth table 0xEA);
+                    // fma(+-1, s, acc) = acc +- s with one rounding, as the ordered sum
+                    const uint32_t hi = __builtin_amdgcn_bitop3_b32(word << (31u - sh - (uint32_t)q), 0x80000000u,
+                                                                    0x3FF00000u, 0xEA);
+                    acc[4 * r + q] = __fma_rn(__hiloint2double((int)hi, 0), sw, acc[4 * r + q]);
                 }
             }
         }
