@@ -24,12 +24,14 @@ Profiling (rocprofv3 runs the program itself, so these modes only do the work):
   python bench.py --profile-allreduce  the same for the 16-worker simulated all-reduce
   python bench.py --summarize-allreduce KT FETCH WRITE SQ
   python bench.py --summarize-profile KT FETCH WRITE
-  python bench.py --ceilings           streaming ceilings by read/write mix, cache
-                                       policy and workgroup shape (markdown on stdout)
                                        turn three rocprofv3 CSV output directories
                                        (kernel trace+stats, --pmc FETCH_SIZE,
                                        --pmc WRITE_SIZE) into the text summary kept
                                        under profiles/ (printed to stdout)
+  python bench.py --ceilings [--ceilings-elems N]
+                                       streaming ceilings by read/write mix, cache
+                                       policy and workgroup shape, N fp32 elements
+                                       per stream (default 2^28; markdown on stdout)
 """
 import argparse
 import csv
@@ -781,9 +783,11 @@ def main():
     ap.add_argument("--summarize-quantizers", nargs=2, metavar=("KT_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("KT_DIR", "COMMAND"))
     ap.add_argument("--ceilings", action="store_true")
+    ap.add_argument("--ceilings-elems", type=int, default=268_435_456,
+                    help="fp32 elements per stream for --ceilings (a multiple of 4)")
     args = ap.parse_args()
     if args.ceilings:
-        sys.stdout.write(ceilings())
+        sys.stdout.write(ceilings(args.ceilings_elems))
         return
     if args.summarize_profile:
         sys.stdout.write(summarize_profile(*args.summarize_profile))
@@ -912,7 +916,7 @@ def stream_ceiling(dev, n=335_544_320):
             "elements": n, "kernel": "onebit_stream_probe"}
 
 
-CEILING_MIXES = ((1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (1, 2), (4, 2), (5, 3))
+CEILING_MIXES = ((1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (1, 2), (2, 2), (4, 2), (5, 3))
 
 
 def ceilings(n=268_435_456):
@@ -932,7 +936,7 @@ def ceilings(n=268_435_456):
     out = [f"# Streaming ceilings by read/write mix and cache policy ({n} fp32 elements per stream)", ""]
     out.append("Command (from the repository root, on one MI355X):")
     out.append("```")
-    out.append("python bench.py --ceilings")
+    out.append("python bench.py --ceilings" + ("" if n == 268_435_456 else f" --ceilings-elems {n}"))
     out.append("```")
     out.append(f"Device: {torch.cuda.get_device_name(0)}, {cus} CUs.  Kernel: onebit_stream_probe (four 16-byte "
                f"vectors per thread and stream per iteration, grid-stride).  Bytes counted: (reads + writes) x 4 x "

@@ -91,7 +91,7 @@ extern "C" onebit_status_t onebit_stream_probe(const float *const *in, int reads
     if (n % 4 != 0) return ONEBIT_ERR_ALIGN;
     const int mix = reads * 10 + writes;
     switch (mix) {
-        case 10: case 1: case 11: case 21: case 31: case 12: case 42: case 53: break;
+        case 10: case 1: case 11: case 21: case 31: case 12: case 22: case 42: case 53: break;
         default: return ONEBIT_ERR_UNSUPPORTED;
     }
     if (n == 0) return ONEBIT_OK;
@@ -107,6 +107,7 @@ extern "C" onebit_status_t onebit_stream_probe(const float *const *in, int reads
         case 21: launch_probe<2, 1>(nt, i4, o4, n4, grid, block, s); break;
         case 31: launch_probe<3, 1>(nt, i4, o4, n4, grid, block, s); break;
         case 12: launch_probe<1, 2>(nt, i4, o4, n4, grid, block, s); break;
+        case 22: launch_probe<2, 2>(nt, i4, o4, n4, grid, block, s); break;
         case 42: launch_probe<4, 2>(nt, i4, o4, n4, grid, block, s); break;
         default: launch_probe<5, 3>(nt, i4, o4, n4, grid, block, s); break;
     }

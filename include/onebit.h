@@ -163,8 +163,9 @@ onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
  * HBM delivers for that mix on this device.  in / out: DEVICE arrays of `reads` /
  * `writes` device pointers, each 16-byte aligned; n a multiple of 4.  Supported
  * mixes (reads + writes): 1 + 0 (read-only: the inputs are left unchanged unless a
- * sum equals -3e38), 0 + 1 (write-only), 1 + 1, 2 + 1, 3 + 1, 1 + 2, 4 + 2 and
- * 5 + 3 (the compression kernel's); others return ONEBIT_ERR_UNSUPPORTED.  grid:
+ * sum equals -3e38), 0 + 1 (write-only), 1 + 1, 2 + 1, 3 + 1 (near the
+ * compress-only worker's), 1 + 2, 2 + 2 (near the server stage's), 4 + 2 and 5 + 3
+ * (the update-mode compression kernel's); others return ONEBIT_ERR_UNSUPPORTED.  grid:
  * number of workgroups; block: threads per workgroup, 256, 512 or 1024
  * (ONEBIT_ERR_INVALID otherwise).  nontemporal != 0: loads and stores use the
  * streaming (nontemporal) cache policy, as the compression kernels do; 0: the

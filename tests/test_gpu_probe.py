@@ -9,7 +9,7 @@ from gpu_helpers import DEV
 
 pytestmark = pytest.mark.gpu
 
-MIXES = [(1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (1, 2), (4, 2), (5, 3)]
+MIXES = [(1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (1, 2), (2, 2), (4, 2), (5, 3)]
 
 
 @pytest.mark.parametrize("nontemporal", [True, False])
@@ -34,10 +34,10 @@ def test_stream_probe_values(reads, writes, block, nontemporal):
 
 def test_stream_probe_refusals():
     n = 4096
-    ins = [torch.zeros(n, device=DEV) for _ in range(2)]
+    ins = [torch.zeros(n, device=DEV) for _ in range(3)]
     outs = [torch.zeros(n, device=DEV) for _ in range(2)]
     with pytest.raises(ob.OnebitError) as ei:
-        ob.onebit_stream_probe(ins, outs, 2)                  # 2 + 2 is not a supported mix
+        ob.onebit_stream_probe(ins, outs, 2)                  # 3 + 2 is not a supported mix
     assert ei.value.status == ob.ONEBIT_ERR_UNSUPPORTED
     with pytest.raises(ob.OnebitError) as ei:
         ob.onebit_stream_probe(ins[:1], outs[:1], 2, 300)
