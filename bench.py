@@ -72,11 +72,15 @@ def ensure_built():
 
 
 class KernelTimer:
-    """Per-kernel-class HIP event timing over a region (library launch profiler)."""
+    """Per-kernel-class HIP event timing over a region (library launch profiler);
+    classes: the kernel classes to bracket with events (None: all)."""
+
+    def __init__(self, classes=None):
+        self.classes = classes
 
     def __enter__(self):
         from error_compensated_bit_amd import onebit as ob
-        ob.onebit_profile_begin()
+        ob.onebit_profile_begin(self.classes)
         return self
 
     def __exit__(self, *exc):
@@ -89,17 +93,27 @@ class KernelTimer:
         return ms / n if n else None
 
 
-def timed(fn, steps, warmup):
+def timed(fn, steps, warmup, classes=()):
+    """Seconds per call over `steps` timed calls after `warmup` untimed ones, and the
+    library's per-kernel event times.  Each HIP event adds a few microseconds between
+    launches, so the timed calls carry events only around the kernel classes named in
+    `classes` (kt.timed); kt itself times every kernel class in a separate pass of up
+    to 10 calls."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    with KernelTimer() as kt:
+    with KernelTimer(classes) as kt_timed:
         t0 = time.perf_counter()
         for _ in range(steps):
             fn()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+    with KernelTimer() as kt:
+        for _ in range(min(steps, 10)):
+            fn()
+        torch.cuda.synchronize()
+    kt.timed = kt_timed
     return (t1 - t0) / steps, kt
 
 
@@ -133,12 +147,14 @@ def onepass_elements(wl, plan):
 
 
 def bench_compress(wl, steps, warmup, dev, bpe):
+    """The timed steps carry HIP events around the one-pass launches only; the
+    breakdown over every kernel of the step comes from timed()'s separate pass."""
     from error_compensated_bit_amd import onebit as ob
     plan, step, ws = compress_setup(wl, dev)
-    t, kt = timed(step, steps, warmup)
+    t, kt = timed(step, steps, warmup, classes=("compress_onepass",))
     assert ob.onebit_workspace_status(ws) == 0, "a cross-workgroup wait timed out"
     n1 = onepass_elements(wl, plan)
-    k_ms = kt.mean_ms("compress_onepass")
+    k_ms = kt.timed.mean_ms("compress_onepass")
     res = dict(seconds_per_call=t, params_per_s=wl.n / t, gbps=bpe * wl.n / t / 1e9,
                onepass_elements=n1, onepass_ms=k_ms, plan=ob.onebit_plan_stats(plan),
                kernels={k: v for k, v in kt.result.items() if v[1]})
@@ -876,7 +892,8 @@ def main():
                                f"{head['onepass_elements']} elements of the one-pass chunks; the whole step, "
                                "two-pass chunk and launch gaps included, is step_frac",
                      "bytes_per_launch": bpe * head["onepass_elements"], "mean_launch_ms": k_ms,
-                     "timing": "mean of HIP events recorded around each launch on its launch stream",
+                     "timing": "mean of HIP events recorded around each one-pass launch on its launch stream "
+                               "inside the timed steps, the only events there",
                      "step_frac": head["gbps"] / PEAK_HBM_GBPS},
         "cpu_baseline": ({k: base[k] for k in ("value", "unit", "cores", "kind", "sample", "cpu_model", "host_cpus",
                                                "cpus_allowed", "pinned_core")} if base else None),
@@ -899,11 +916,11 @@ def stream_ceiling(dev, n=335_544_320):
     for name, ins, outs, bpe in (("5r3w", bufs[:5], bufs[5:], 32.0),):
         for block, mults in ((256, (1, 2, 3, 6, 16, 32)), (1024, (1, 2, 4, 6, 8))):
             for mult in mults:
-                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, True)    # warm
+                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, 1)    # warm
                 times = []
                 for _ in range(4):
                     ev0.record()
-                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, True)
+                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, 1)
                     ev1.record()
                     ev1.synchronize()
                     times.append(ev0.elapsed_time(ev1))
@@ -922,7 +939,8 @@ CEILING_MIXES = ((1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (1, 2), (2, 2), (4, 2),
 def ceilings(n=268_435_456):
     """Streaming ceilings of this device: the plain probe kernel for each read/write
     mix, with the streaming (nontemporal) and the default cache policy, over
-    256-thread workgroups (1-32 per CU) and 1024-thread workgroups (1-8 per CU);
+    256-thread workgroups (1-32 per CU) and 1024-thread workgroups (1-8 per CU),
+    and with its loads staged in LDS by the load unit (256-thread workgroups);
     the best rate of each, and the best with 256-thread workgroups (the compression
     kernels' shape).  Returns the markdown summary kept under profiles/."""
     import torch
@@ -939,23 +957,28 @@ def ceilings(n=268_435_456):
     out.append("python bench.py --ceilings" + ("" if n == 268_435_456 else f" --ceilings-elems {n}"))
     out.append("```")
     out.append(f"Device: {torch.cuda.get_device_name(0)}, {cus} CUs.  Kernel: onebit_stream_probe (four 16-byte "
-               f"vectors per thread and stream per iteration, grid-stride).  Bytes counted: (reads + writes) x 4 x "
-               f"n per launch; time: best of 4 launches between HIP events on the launch stream, after one warm "
-               f"launch.  Peak: {PEAK_HBM_GBPS:.0f} GB/s.")
+               f"vectors per thread and stream per iteration, grid-stride; with loads staged in LDS, each wave "
+               f"double-buffers four 1 KiB global-to-LDS loads per input stream and reads them back).  Bytes "
+               f"counted: (reads + writes) x 4 x n per launch; time: best of 4 launches between HIP events on the "
+               f"launch stream, after one warm launch.  Peak: {PEAK_HBM_GBPS:.0f} GB/s.")
     out.append("")
     out.append("| reads + writes | cache policy | best GB/s | fraction of 8 TB/s | best shape (threads x WG per CU) | "
                "best GB/s with 256-thread WGs |")
     out.append("|---|---|---|---|---|---|")
     for reads, writes in CEILING_MIXES:
         ins, outs = bufs[:reads], bufs[reads:reads + writes]
-        for nt in (True, False):
+        for policy in (1, 0, 2):
+            if policy == 2 and reads == 0:
+                continue
             best, best256 = (0.0, None), 0.0
             for block, mult in shapes:
-                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, nt)
+                if policy == 2 and block != 256:
+                    continue
+                keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, policy)
                 times = []
                 for _ in range(4):
                     ev0.record()
-                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, nt)
+                    keep = ob.onebit_stream_probe(ins, outs, cus * mult, block, policy)
                     ev1.record()
                     ev1.synchronize()
                     times.append(ev0.elapsed_time(ev1))
@@ -965,7 +988,7 @@ def ceilings(n=268_435_456):
                     best = (gbps, f"{block} x {mult}")
                 if block == 256:
                     best256 = max(best256, gbps)
-            pol = "nontemporal" if nt else "default"
+            pol = ("default", "nontemporal", "nontemporal, loads staged in LDS")[policy]
             out.append(f"| {reads} + {writes} | {pol} | {best[0]:.0f} | {best[0] / PEAK_HBM_GBPS:.3f} | {best[1]} | "
                        f"{best256:.0f} |")
             log(f"[ceilings] {reads}+{writes} {pol}: {best[0]:.0f} GB/s ({best[1]}), 256-thread {best256:.0f}")

@@ -594,7 +594,10 @@ __device__ __forceinline__ void tile_load_c(const CompressArgs &a, const TileDes
     }
 }
 
+// Waves per SIMD the one-pass kernel is built for: six, five for the server tiles,
+// whose staged worker words and fp64 sums need more registers than six waves leave.
 constexpr int kOnepassWavesPerSimd = 6;
+constexpr int kServerWavesPerSimd = 5;
 constexpr int kMaxW = 1024;
 
 // c of a posted tile waits in LDS (each thread reads back only what it wrote).
@@ -641,7 +644,8 @@ __device__ __forceinline__ Posted produce(const CompressArgs &a, int tile_id, co
 }
 
 template <int MODE, int GT, bool XB>
-__global__ __launch_bounds__(kBlock, kOnepassWavesPerSimd) void k_compress_onepass(CompressArgs a) {
+__global__ __launch_bounds__(kBlock, MODE == kServer ? kServerWavesPerSimd : kOnepassWavesPerSimd) void
+k_compress_onepass(CompressArgs a) {
     __shared__ float4 s_c[kDepth][kGroups * kBlock];
     __shared__ TileDesc s_tile[kDepth];
     __shared__ Posted s_post[kDepth];

@@ -53,6 +53,8 @@ struct ProfRec {
 };
 static struct {
     bool on = false;
+    uint32_t mask = 0;        // classes bracketed by events
+    bool open = false;        // the last prof_before pushed a record
     std::vector<ProfRec> recs;
     std::vector<hipEvent_t> pool;
     size_t used = 0;
@@ -68,15 +70,18 @@ static hipEvent_t prof_event() {
 }
 
 void prof_before(int cls, hipStream_t s) {
-    if (!g_prof.on) return;
+    g_prof.open = false;
+    if (!g_prof.on || !(g_prof.mask >> cls & 1u)) return;
     ProfRec r{cls, prof_event(), prof_event()};
     if (!r.a || !r.b) return;
     (void)hipEventRecord(r.a, s);
     g_prof.recs.push_back(r);
+    g_prof.open = true;
 }
 
 void prof_after(hipStream_t s) {
-    if (!g_prof.on || g_prof.recs.empty()) return;
+    if (!g_prof.open) return;
+    g_prof.open = false;
     (void)hipEventRecord(g_prof.recs.back().b, s);
 }
 
@@ -303,11 +308,15 @@ extern "C" onebit_status_t onebit_workspace_status(const void *workspace, uint64
     return hip_status(e);
 }
 
-extern "C" void onebit_profile_begin(void) {
+extern "C" void onebit_profile_begin_classes(uint32_t class_mask) {
     g_prof.on = true;
+    g_prof.mask = class_mask;
+    g_prof.open = false;
     g_prof.recs.clear();
     g_prof.used = 0;
 }
+
+extern "C" void onebit_profile_begin(void) { onebit_profile_begin_classes((1u << kProfClasses) - 1u); }
 
 extern "C" onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches) {
     g_prof.on = false;

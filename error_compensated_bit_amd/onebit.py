@@ -41,6 +41,7 @@ _SIGS = {
     "onebit_plan_stats": (None, [_P, _P]),
     "onebit_onepass_max_elements": (_I64, []),
     "onebit_profile_begin": (None, []),
+    "onebit_profile_begin_classes": (None, [C.c_uint32]),
     "onebit_profile_end": (_I, [_P, _P]),
     "onebit_adam_warmup_step": (_I, [_P, _P, _P, _P, _I, _I64, _D, _D, _D, _D, _D, _I, _I64, _P]),
     "onebit_compress_update": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
@@ -252,8 +253,16 @@ PROFILE_CLASSES = ("warmup", "compress_pass1", "compress_onepass", "compress_pas
                    "momentum_update", "qsgd_quantize", "qsgd_reduce", "loco_quantize")
 
 
-def onebit_profile_begin():
-    load().onebit_profile_begin()
+def onebit_profile_begin(classes=None):
+    """classes: names from PROFILE_CLASSES to bracket with events (None: all; an
+    empty list: none)."""
+    if classes is None:
+        load().onebit_profile_begin()
+        return
+    mask = 0
+    for name in classes:
+        mask |= 1 << PROFILE_CLASSES.index(name)
+    load().onebit_profile_begin_classes(mask)
 
 
 def onebit_profile_end() -> dict:
@@ -324,16 +333,18 @@ def onebit_server_reduce(plan, worker_bits, worker_scales, server_error, server_
                                        _stream(stream)), "onebit_server_reduce")
 
 
-def onebit_stream_probe(inputs, outputs, grid, block=256, nontemporal=True, stream=None):
+def onebit_stream_probe(inputs, outputs, grid, block=256, policy=1, stream=None):
     """inputs / outputs: lists of equally long fp32 device tensors (one of the mixes
-    the library supports); block: threads per workgroup (256, 512 or 1024)."""
+    the library supports); block: threads per workgroup (256, 512 or 1024); policy:
+    0 default cache policy, 1 (or True) nontemporal, 2 nontemporal loads staged in
+    LDS by the load unit (256-thread workgroups, at least one input)."""
     import torch
     dev = (inputs or outputs)[0].device
     n = (inputs or outputs)[0].numel()
     pin = torch.tensor([t.data_ptr() for t in inputs] or [0], dtype=torch.int64, device=dev)
     pout = torch.tensor([t.data_ptr() for t in outputs] or [0], dtype=torch.int64, device=dev)
     _check(load().onebit_stream_probe(_ptr(pin), len(inputs), _ptr(pout), len(outputs), n, int(grid),
-                                      int(block), int(bool(nontemporal)), _stream(stream)), "onebit_stream_probe")
+                                      int(block), int(policy), _stream(stream)), "onebit_stream_probe")
     return pin, pout           # keep the pointer arrays alive until the launch has run
 
 

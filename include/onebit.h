@@ -152,10 +152,14 @@ void onebit_set_grid_cap(int32_t cap);
  * pass 1 / one-pass / pass 2, 9 chunk-norm finalization of two-pass chunks, 10
  * momentum update, 11 QSGD quantize, 12 QSGD reduce, 13 LoCo quantize.  A QSGD or
  * LoCo call with buckets of 1024 and a ragged last bucket launches two kernels (whole
- * buckets, then the last one) inside one bracket, counted as one launch.  Not
- * thread-safe; diagnostics only. */
+ * buckets, then the last one) inside one bracket, counted as one launch.
+ * onebit_profile_begin_classes brackets only the classes whose bit (1 << class) is
+ * set in class_mask, so that a timed region carries the events of the kernel being
+ * measured and no others (each event adds a few microseconds between launches).
+ * Not thread-safe; diagnostics only. */
 #define ONEBIT_PROFILE_CLASSES 14
 void onebit_profile_begin(void);
+void onebit_profile_begin_classes(uint32_t class_mask);
 onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
 
 /* Diagnostics: a plain streaming kernel over `reads` fp32 input streams and `writes`
@@ -167,11 +171,14 @@ onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
  * compress-only worker's), 1 + 2, 2 + 2 (near the server stage's), 4 + 2 and 5 + 3
  * (the update-mode compression kernel's); others return ONEBIT_ERR_UNSUPPORTED.  grid:
  * number of workgroups; block: threads per workgroup, 256, 512 or 1024
- * (ONEBIT_ERR_INVALID otherwise).  nontemporal != 0: loads and stores use the
- * streaming (nontemporal) cache policy, as the compression kernels do; 0: the
- * default policy. */
+ * (ONEBIT_ERR_INVALID otherwise).  policy 1: loads and stores use the streaming
+ * (nontemporal) cache policy, as the compression kernels do; 0: the default
+ * policy; 2: streaming policy with every wave's loads going straight into LDS
+ * (the 16-byte global-to-LDS loads of gfx950), double-buffered, and read back from
+ * there, so the next loads are in flight without holding registers (block must be
+ * 256 and reads at least 1); any other policy or combination: ONEBIT_ERR_INVALID. */
 onebit_status_t onebit_stream_probe(const float *const *in, int reads, float *const *out, int writes,
-                                    int64_t n, int grid, int block, int nontemporal, void *stream);
+                                    int64_t n, int grid, int block, int policy, void *stream);
 
 /* Warmup step t (1-based) of full-precision Adam over n elements ([DSG] sec. 4,
  * phase one; [1BA]):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;

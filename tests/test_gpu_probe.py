@@ -1,6 +1,8 @@
 """The streaming probe (diagnostics) writes out_k = sum of its inputs + k, for every
-supported read/write mix and both cache policies; the read-only mix leaves its input
-unchanged; unsupported mixes and workgroup sizes are refused."""
+supported read/write mix and both cache policies, and with the loads staged in LDS
+(ragged lengths, fewer chunks than waves, grids that leave waves idle or give each
+wave many chunks); the read-only mix leaves its input unchanged; unsupported mixes,
+workgroup sizes and policies are refused."""
 import pytest
 import torch
 
@@ -20,13 +22,31 @@ def test_stream_probe_values(reads, writes, block, nontemporal):
     ins = [torch.randn(n, device=DEV) for _ in range(reads)]
     before = [t.clone() for t in ins]
     outs = [torch.zeros(n, device=DEV) for _ in range(writes)]
-    keep = ob.onebit_stream_probe(ins, outs, 2, block, nontemporal)
+    keep = ob.onebit_stream_probe(ins, outs, 2, block, 1 if nontemporal else 0)
     torch.cuda.synchronize()
     s = torch.zeros(n, device=DEV)
     for t in ins:
         s = s + t
     for k, o in enumerate(outs):
         assert torch.equal(o, s + float(k))
+    for a, b in zip(ins, before):
+        assert torch.equal(a, b)
+    del keep
+
+
+@pytest.mark.parametrize("n,grid", [(4, 1), (516, 3), (1024 * 4 * 4 * 3 + 44, 2), (1 << 20, 7), ((1 << 20) + 12, 300)])
+@pytest.mark.parametrize("reads,writes", [m for m in MIXES if m[0] > 0])
+def test_stream_probe_lds_staged_values(reads, writes, n, grid):
+    ins = [torch.randn(n, device=DEV) for _ in range(reads)]
+    before = [t.clone() for t in ins]
+    outs = [torch.zeros(n, device=DEV) for _ in range(writes)]
+    keep = ob.onebit_stream_probe(ins, outs, grid, 256, 2)
+    torch.cuda.synchronize()
+    s = torch.zeros(n, device=DEV)
+    for t in ins:
+        s = s + t
+    for k, o in enumerate(outs):
+        assert torch.equal(o, s + float(k)), (reads, writes, n, grid, k)
     for a, b in zip(ins, before):
         assert torch.equal(a, b)
     del keep
@@ -42,3 +62,8 @@ def test_stream_probe_refusals():
     with pytest.raises(ob.OnebitError) as ei:
         ob.onebit_stream_probe(ins[:1], outs[:1], 2, 300)
     assert ei.value.status == ob.ONEBIT_ERR_INVALID
+    for args in [(ins[:1], outs[:1], 2, 1024, 2), ([], outs[:1], 2, 256, 2), (ins[:1], outs[:1], 2, 256, 3),
+                 (ins[:1], outs[:1], 2, 256, -1)]:
+        with pytest.raises(ob.OnebitError) as ei:
+            ob.onebit_stream_probe(*args)
+        assert ei.value.status == ob.ONEBIT_ERR_INVALID
