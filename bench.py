@@ -827,8 +827,8 @@ def main():
         profile_mode(max(1, min(args.steps, 20)))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
-              f"multi-GPU path: the compressed all-reduce is simulated inside one GPU's memory)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library "
+              f"has no multi-GPU path: the compressed all-reduce is simulated inside one GPU's memory)", file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs as a single process on one GPU", file=sys.stderr)

@@ -58,7 +58,7 @@ typedef enum {
     ONEBIT_ERR_ALIGN = 2,       /* a base pointer misses its required alignment */
     ONEBIT_ERR_HIP = 3,         /* a HIP runtime call or launch failed */
     ONEBIT_ERR_NOMEM = 4,       /* plan tables could not be allocated */
-    ONEBIT_ERR_UNSUPPORTED = 5  /* valid request this build does not serve */
+    ONEBIT_ERR_UNSUPPORTED = 5  /* valid request the library does not serve */
 } onebit_status_t;
 
 typedef enum { ONEBIT_F32 = 0, ONEBIT_BF16 = 1, ONEBIT_F16 = 2 } onebit_dtype_t;

@@ -3,7 +3,7 @@
 Source: shd-paper.top summary of LoCo (core points; method details, steps 2-4): the
 gradient is compensated, before compression, by a moving average of the historical
 compensation errors.  The page gives no formula, window or weights, so the step is
-this build's reading (parity unpinned as to the method itself); what is pinned is
+a reading of that description (parity unpinned as to the method itself); what is pinned is
 the reading's own structure:
 
 - beta = 0 and a zero average: the codes are the plain QSGD codes of g and the new
