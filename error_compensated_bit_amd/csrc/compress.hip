@@ -128,7 +128,9 @@ __device__ __forceinline__ void load4(const float *base, uint32_t k0, float (&v)
 // chunk and the tile's packed words are staged in LDS (each worker's words load as
 // one 256-byte run), then every thread adds +-s for its elements as fma(+-1, s,
 // acc), the +-1.0 built from the sign bit in two instructions (server 0.304 ->
-// 0.294 ms on 16 x 64M against a sign-bit xor on s).
+// 0.294 ms on 16 x 64M against a sign-bit xor on s).  The server error is loaded
+// before the words are staged, so the two loads are in flight together (0.291 ->
+// 0.285 ms).
 constexpr int kWBatch = 16;
 constexpr int kTileWords = kTile / 32;
 
@@ -136,6 +138,21 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
                                               double *s_wscale_d, uint32_t *s_words) {
     const bool full = tile_full(a, t);
     const int nwords = (t.len + 31) / 32;
+    const float *eb = a.e + t.start;
+    float es[kPerThread];
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+        const uint32_t k0 = lane_k0(r);
+        float e4[4];
+        if (full) {
+            load4(eb, k0, e4);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) e4[q] = (k0 + q < (uint32_t)t.len) ? eb[k0 + q] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) es[4 * r + q] = e4[q];
+    }
     double acc[kPerThread];
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) acc[j] = 0.0;
@@ -179,23 +196,15 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
             }
         }
     }
-    const float *eb = a.e + t.start;
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
         const uint32_t k0 = lane_k0(r);
-        float es[4];
-        if (full) {
-            load4(eb, k0, es);
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) es[q] = (k0 + q < (uint32_t)t.len) ? eb[k0 + q] : 0.0f;
-        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             // a power-of-two W divides exactly by scaling
             const double x = acc[4 * r + q];
             const double mean = a.w_pow2_scale != 0.0 ? __dmul_rn(x, a.w_pow2_scale) : __ddiv_rn(x, (double)a.W);
-            c[4 * r + q] = (full || k0 + q < (uint32_t)t.len) ? add_rn((float)mean, es[q]) : 0.0f;
+            c[4 * r + q] = (full || k0 + q < (uint32_t)t.len) ? add_rn((float)mean, es[4 * r + q]) : 0.0f;
         }
     }
 }
@@ -779,8 +788,6 @@ k_compress_onepass(CompressArgs a) {
 template <int MODE, int GT>
 __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     __shared__ DD s_red[kWaves];
-    __shared__ uint32_t s_u32[2];
-    __shared__ double s_total;
     __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
     __shared__ __align__(16) uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int tile_id = a.list[blockIdx.x];
@@ -791,8 +798,6 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     tile_store_c(a, t, c);
     const double part = tile_sum_squares(c, s_red);
     if (threadIdx.x == 0) st_agent(a.slots + tile_id, tag_partial(part));
-    (void)s_u32;
-    (void)s_total;
 }
 
 // One 1024-thread workgroup per two-pass chunk, 16 slot loads per thread in flight:
