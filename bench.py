@@ -996,17 +996,49 @@ def ceilings(n=268_435_456):
     return "\n".join(out) + "\n"
 
 
-def roof(gbps, elems_per_s=None, label=None, valu=None):
+def roof(gbps, elems_per_s=None, label=None, valu=None, rng=None):
     """Roofline of a row: HBM fraction of 8 TB/s, and for the quantizers the fraction of
     the VALU issue-rate bound (from the committed instruction counts); bound = the
-    larger fraction."""
+    larger fraction.  rng: the element rate that drawing the quantizer's random
+    numbers alone reaches (the Philox probe), reported beside it."""
     r = {"hbm_frac": gbps / PEAK_HBM_GBPS}
     per = (valu or {}).get(label)
     if per and elems_per_s:
         r["alu_peak_elems_per_s"] = VALU_LANE_OPS_PER_S / per
         r["alu_frac"] = elems_per_s / r["alu_peak_elems_per_s"]
+    if rng and elems_per_s:
+        r["rng_only_elems_per_s"] = rng
+        r["rng_frac"] = elems_per_s / rng
     r["bound"] = "alu" if r.get("alu_frac", 0.0) > r["hbm_frac"] else "hbm"
     return r
+
+
+def philox_ceiling(dev, n_elems):
+    """Elements per second that drawing Philox4x32-10 numbers alone allows (one block
+    of four words per four elements, as the quantizers draw them): the Philox probe
+    over n_elems / 4 blocks, best grid, best of 3 launches each."""
+    import torch
+    from error_compensated_bit_amd import onebit as ob
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_blocks = (n_elems + 3) // 4
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = (0.0, None)
+    for block, mults in ((256, (2, 4, 8, 16, 32)), (1024, (1, 2, 4, 8))):
+        for mult in mults:
+            out = torch.empty(cus * mult * block, dtype=torch.int32, device=dev)
+            ob.onebit_philox_probe(0, n_blocks, out, cus * mult, block)
+            times = []
+            for _ in range(3):
+                ev0.record()
+                ob.onebit_philox_probe(0, n_blocks, out, cus * mult, block)
+                ev1.record()
+                ev1.synchronize()
+                times.append(ev0.elapsed_time(ev1))
+            rate = n_elems / (min(times) * 1e-3)
+            if rate > best[0]:
+                best = (rate, f"{block} x {mult}")
+    return {"elems_per_s": best[0], "blocks_per_s": best[0] / 4.0, "shape": best[1], "elements": n_elems,
+            "kernel": "onebit_philox_probe"}
 
 
 def secondary_rows(dev, args):
@@ -1039,6 +1071,9 @@ def secondary_rows(dev, args):
 
     # QSDP on 1.3e9 bf16 weights
     q = W.QsdpWorkload()
+    rng = philox_ceiling(dev, q.n)
+    rows["philox4x32_10_only"] = rng
+    log(f"[bench] philox only {rng}")
     xq = W.qsdp_weights(q, device=dev)
     nb = (q.n + q.bucket - 1) // q.bucket
     bmin = torch.zeros(nb, device=dev)
@@ -1049,7 +1084,8 @@ def secondary_rows(dev, args):
         tq, ktq = timed(lambda: ob.qsdp_quantize(xq, q.bucket, bits, 0, codes, bmin, bmax), steps, 1)
         td, ktd = timed(lambda: ob.qsdp_dequantize(codes, bmin, bmax, q.n, q.bucket, bits, out), steps, 1)
         rows[f"qsdp{bits}_quantize"] = dict(elems_per_s=q.n / tq, gbps=bpe * q.n / tq / 1e9)
-        rows[f"qsdp{bits}_quantize"]["roofline"] = roof(bpe * q.n / tq / 1e9, q.n / tq, f"qsdp{bits}_quantize", valu)
+        rows[f"qsdp{bits}_quantize"]["roofline"] = roof(bpe * q.n / tq / 1e9, q.n / tq, f"qsdp{bits}_quantize", valu,
+                                                         rng["elems_per_s"])
         rows[f"qsdp{bits}_dequantize"] = dict(elems_per_s=q.n / td, gbps=bpe * q.n / td / 1e9)
         rows[f"qsdp{bits}_dequantize"]["roofline"] = roof(bpe * q.n / td / 1e9)
         del codes, out
@@ -1100,14 +1136,16 @@ def secondary_rows(dev, args):
         bq = 2.0 + bits / 8.0 + 4.0 / qg.bucket
         br = qg.W * (bits / 8.0 + 4.0 / qg.bucket) + 4.0
         rows[f"qsgd{bits}_quantize"] = dict(elems_per_s=qg.n / tq, gbps=bq * qg.n / tq / 1e9,
-                                            roofline=roof(bq * qg.n / tq / 1e9, qg.n / tq, f"qsgd{bits}_quantize", valu))
+                                            roofline=roof(bq * qg.n / tq / 1e9, qg.n / tq, f"qsgd{bits}_quantize", valu,
+                                                          rng["elems_per_s"]))
         rows[f"qsgd{bits}_reduce_{qg.W}x{qg.shard}"] = dict(elems_per_s=qg.shard / tr, gbps=br * qg.shard / tr / 1e9,
                                                             roofline=roof(br * qg.shard / tr / 1e9))
         if bits == 4:
             err = torch.zeros(qg.n, device=dev)
             tl, _ = timed(lambda: ob.loco_quantize(gq, err, qg.bucket, bits, 0.9, 7, codes[0], norms[0]), steps, 1)
             rows["loco4_quantize"] = dict(elems_per_s=qg.n / tl, gbps=(bq + 8.0) * qg.n / tl / 1e9,
-                                          roofline=roof((bq + 8.0) * qg.n / tl / 1e9, qg.n / tl, "loco4_quantize", valu))
+                                          roofline=roof((bq + 8.0) * qg.n / tl / 1e9, qg.n / tl, "loco4_quantize", valu,
+                                                        rng["elems_per_s"]))
             del err
         del codes, out
     del gq, norms

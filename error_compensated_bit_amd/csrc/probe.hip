@@ -244,3 +244,33 @@ extern "C" onebit_status_t onebit_stream_probe(const float *const *in, int reads
     }
     return hip_status(hipGetLastError());
 }
+
+// ------------------------------------------------------------ Philox probe
+// The random numbers of the quantizers alone: thread t of the grid draws the
+// Philox4x32-10 blocks t, t + T, t + 2T, ... below n_blocks (T = threads in the
+// grid; counter = block index, key = the seed's two words, as the quantizers draw
+// them) and folds the four words of every block into one word by XOR, stored to
+// out[t].  One block serves four quantized elements.
+namespace onebit {
+
+__global__ __launch_bounds__(1024) void k_philox_probe(uint32_t k0, uint32_t k1, int64_t n_blocks, uint32_t *out) {
+    const int64_t T = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0u;
+    for (int64_t blk = t; blk < n_blocks; blk += T) {
+        const U4 r = philox4x32_10(U4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u}, k0, k1);
+        acc ^= r.a ^ r.b ^ r.c ^ r.d;
+    }
+    out[t] = acc;
+}
+
+}  // namespace onebit
+
+extern "C" onebit_status_t onebit_philox_probe(uint64_t seed, int64_t n_blocks, uint32_t *out, int grid, int block,
+                                               void *stream) {
+    if (n_blocks < 0 || grid < 1 || !out) return ONEBIT_ERR_INVALID;
+    if (block != 256 && block != 512 && block != 1024) return ONEBIT_ERR_INVALID;
+    hipLaunchKernelGGL(k_philox_probe, dim3(grid), dim3(block), 0, static_cast<hipStream_t>(stream),
+                       (uint32_t)seed, (uint32_t)(seed >> 32), n_blocks, out);
+    return hip_status(hipGetLastError());
+}

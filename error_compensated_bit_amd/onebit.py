@@ -50,6 +50,7 @@ _SIGS = {
     "onebit_momentum_update_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _D, _D, _D, _P]),
     "onebit_server_reduce": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "onebit_stream_probe": (_I, [_P, _I, _P, _I, _I64, _I, _I, _I, _P]),
+    "onebit_philox_probe": (_I, [_U64, _I64, _P, _I, _I, _P]),
     "onebit_momentum_update": (_I, [_P, _P, _P, _P, _P, _I64, _D, _D, _D, _P]),
     "onebit_decompress": (_I, [_P, _P, _P, _P, _P, _P]),
     "onebit_average_rows": (_I, [_P, _I, _I, _I64, _I64, _P, _P]),
@@ -346,6 +347,14 @@ def onebit_stream_probe(inputs, outputs, grid, block=256, policy=1, stream=None)
     _check(load().onebit_stream_probe(_ptr(pin), len(inputs), _ptr(pout), len(outputs), n, int(grid),
                                       int(block), int(policy), _stream(stream)), "onebit_stream_probe")
     return pin, pout           # keep the pointer arrays alive until the launch has run
+
+
+def onebit_philox_probe(seed, n_blocks, out, grid, block=256, stream=None):
+    """out: int32/uint32 device tensor of grid * block words (one XOR-folded word per thread)."""
+    if out.numel() != grid * block:
+        raise ValueError("out must hold grid * block words")
+    _check(load().onebit_philox_probe(int(seed), int(n_blocks), _ptr(out), int(grid), int(block), _stream(stream)),
+           "onebit_philox_probe")
 
 
 def onebit_set_spin_limit(limit: int) -> None:

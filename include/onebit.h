@@ -180,6 +180,17 @@ onebit_status_t onebit_profile_end(double *total_ms, int64_t *launches);
 onebit_status_t onebit_stream_probe(const float *const *in, int reads, float *const *out, int writes,
                                     int64_t n, int grid, int block, int policy, void *stream);
 
+/* Diagnostics: the cost of the quantizers' random numbers alone (QSDP, "Proposed
+ * method": unbiased stochastic rounding, here with Philox4x32-10 keyed by the
+ * seed's low / high words and counter = block index).  Thread t of a grid of
+ * grid x block threads draws the blocks t, t + T, t + 2T, ... below n_blocks
+ * (T = grid x block) and stores the XOR of the four words of all its blocks to
+ * out[t]: a DEVICE array of grid x block words.  One block serves four quantized
+ * elements.  block: 256, 512 or 1024; grid >= 1; n_blocks >= 0 (else
+ * ONEBIT_ERR_INVALID). */
+onebit_status_t onebit_philox_probe(uint64_t seed, int64_t n_blocks, uint32_t *out, int grid, int block,
+                                    void *stream);
+
 /* Warmup step t (1-based) of full-precision Adam over n elements ([DSG] sec. 4,
  * phase one; [1BA]):  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
  *   x -= lr * ( mhat / (sqrt(vhat) + eps) + weight_decay * x ),
