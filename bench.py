@@ -405,11 +405,24 @@ CALIBRATION_FLOATS = 1 << 28          # 1 GiB copied by the profile mode
 DIGEST_FILES = ("csrc/compress.hip", "csrc/device_common.h", "csrc/internal.h", "csrc/plan.hip", "build.py")
 
 
+def _code_text(path):
+    """A source file without its comments and with runs of whitespace collapsed, so
+    that the digests below change with the code and not with its commentary."""
+    import re
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    if path.endswith(".py"):
+        text = re.sub(r"#[^\n]*", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split()).encode()
+
+
 def source_digest():
     h = hashlib.sha256()
     for rel in DIGEST_FILES:
-        with open(os.path.join(ROOT, "error_compensated_bit_amd", rel), "rb") as f:
-            h.update(f.read())
+        h.update(_code_text(os.path.join(ROOT, "error_compensated_bit_amd", rel)))
     return h.hexdigest()[:16]
 
 
@@ -439,8 +452,7 @@ VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9     # 256 CUs x 64 lanes (4 SIMD16, one w
 def quant_digest():
     h = hashlib.sha256()
     for rel in QUANT_FILES:
-        with open(os.path.join(ROOT, "error_compensated_bit_amd", rel), "rb") as f:
-            h.update(f.read())
+        h.update(_code_text(os.path.join(ROOT, "error_compensated_bit_amd", rel)))
     return h.hexdigest()[:16]
 
 

@@ -19,8 +19,8 @@
 //  - larger chunks take two passes: pass 1 stores c in place of e, pass 2 reads it
 //    back with v and x once the chunk scale is known.
 // Cross-workgroup communication uses only single-location relaxed agent-scope
-// atomics on self-validating words (tagged partials, {epoch, count} and
-// {epoch, scale}); no cache-wide write-back or invalidate is ever needed, and a
+// atomics on self-validating words (a tagged partial per tile, an {epoch, scale}
+// word per chunk); no cache-wide write-back or invalidate is ever needed, and a
 // zeroed workspace is always ready for the next call.
 #include <math.h>
 
