@@ -130,9 +130,26 @@ __device__ __forceinline__ void load4(const float *base, uint32_t k0, float (&v)
 // acc), the +-1.0 built from the sign bit in two instructions (server 0.304 ->
 // 0.294 ms on 16 x 64M against a sign-bit xor on s).  The server error is loaded
 // before the words are staged, so the two loads are in flight together (0.291 ->
-// 0.285 ms).
+// 0.285 ms).  For W <= kWBatch and scales whose partial sums are all exact, the
+// sums come from per-group tables instead (below; 0.284 -> 0.253 ms).
 constexpr int kWBatch = 16;
 constexpr int kTileWords = kTile / 32;
+
+// Exact-sum tables (W <= kWBatch): for each group of four workers, the 16 signed
+// sums +-s_4g +-s_4g+1 +-s_4g+2 +-s_4g+3 (bit k of the entry index set: worker 4g+k
+// negative), so that an element adds four table entries instead of W scales.  The
+// regrouped sum equals the ordered one exactly when no partial sum of either rounds:
+// every scale is finite and, with u the smallest unit in the last place of the
+// nonzero scales (2^(e_min - 150) for biased exponent fields e, subnormals counted
+// as e = 1), every partial sum is an integer multiple of u below W * 2^(e_max - 126)
+// <= 2^53 u, i.e. e_max - e_min <= 29 - ceil(log2 W).  Both forms start from +0 and
+// never produce -0, so zeros agree in sign too.  Otherwise the ordered loop runs.
+constexpr int kWGroups = kWBatch / 4;
+constexpr int kServerLdsDoubles = kWBatch + kWGroups * 16 + 1;  // scales, tables, exact flag
+
+// Bit q of a 4-bit value moved to bit 8q (the four copies of the product do not
+// overlap, so no carry crosses them).
+__device__ __forceinline__ uint32_t spread_nibble(uint32_t n) { return (n * 0x00204081u) & 0x01010101u; }
 
 __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileDesc &t, float (&c)[kPerThread],
                                               double *s_wscale_d, uint32_t *s_words) {
@@ -159,8 +176,43 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
     for (int w0 = 0; w0 < a.W; w0 += kWBatch) {
         const int wn = min(kWBatch, a.W - w0);
         __syncthreads();  // previous batch fully consumed
-        for (int w = threadIdx.x; w < wn; w += kBlock)
-            s_wscale_d[w] = (double)a.wscales[(int64_t)(w0 + w) * a.n_chunks + t.chunk];
+        double *s_tab = s_wscale_d + kWBatch;
+        int *s_exact = reinterpret_cast<int *>(s_wscale_d + kWBatch + kWGroups * 16);
+        const bool tables = a.W <= kWBatch;
+        const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        if (tables && wave == 0) {
+            // wave 0: the scales, and whether the regrouped sum is exact.  The lane
+            // index is made opaque here so that nothing derived from it is hoisted
+            // out of the tile loop and held in registers for the whole kernel.
+            int j = (int)threadIdx.x;
+            asm volatile("" : "+v"(j));
+            const float sv = j < wn ? a.wscales[(int64_t)j * a.n_chunks + t.chunk] : 0.0f;
+            if (j < wn) s_wscale_d[j] = (double)sv;
+            const uint32_t bits = __float_as_uint(sv) & 0x7FFFFFFFu;
+            const int ef = (int)(bits >> 23);
+            int emin = bits != 0u ? max(ef, 1) : 255, emax = bits != 0u ? max(ef, 1) : 0;
+            int bad = ef == 255;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                emin = min(emin, __shfl_xor(emin, o));
+                emax = max(emax, __shfl_xor(emax, o));
+                bad |= __shfl_xor(bad, o);
+            }
+            const int lg = 32 - __clz(wn - 1);  // ceil(log2 W), 0 for W = 1
+            if (j == 0) *s_exact = !bad && (emax == 0 || emax - emin <= 29 - lg);
+            // table entry j (lane j) of group j / 16 from the scales of lanes 4g .. 4g+3
+            const int g = j >> 4;
+            double T = 0.0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float sw = __shfl(sv, 4 * g + k);
+                if (4 * g + k < wn) T = __fma_rn((j >> k) & 1 ? -1.0 : 1.0, (double)sw, T);
+            }
+            s_tab[j] = T;
+        } else if (!tables) {
+            for (int w = threadIdx.x; w < wn; w += kBlock)
+                s_wscale_d[w] = (double)a.wscales[(int64_t)(w0 + w) * a.n_chunks + t.chunk];
+        }
         // a full batch of a full tile with 16-byte aligned rows: one 16-byte load per
         // thread (thread k takes words 4k..4k+3 of the batch), else one word each
         const bool vec = kWBatch * kTileWords == 4 * kBlock && full && wn == kWBatch &&
@@ -176,6 +228,30 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
             }
         }
         __syncthreads();
+        if (tables && *s_exact) {
+            const int ng = (wn + 3) >> 2;
+#pragma unroll
+            for (int r = 0; r < kGroups; ++r) {
+                const uint32_t k0 = lane_k0(r);
+                const uint32_t wi = k0 >> 5;
+                const uint32_t sh = k0 & 31u;
+#pragma unroll 1
+                for (int g = 0; g < ng; ++g) {
+                    // byte q of idx: the entry index of element q (bit k from worker 4g+k)
+                    uint32_t idx = 0u;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t nib = __builtin_amdgcn_ubfe(s_words[(4 * g + k) * kTileWords + wi], sh, 4);
+                        idx |= spread_nibble(nib) << k;
+                    }
+                    const double *tg = s_tab + 16 * g;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[4 * r + q] = __dadd_rn(acc[4 * r + q], tg[__builtin_amdgcn_ubfe(idx, 8 * q, 4)]);
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int r = 0; r < kGroups; ++r) {
             const uint32_t k0 = lane_k0(r);
@@ -736,7 +812,7 @@ k_compress_onepass(CompressArgs a) {
     __shared__ DD s_red[kWaves];
     __shared__ uint32_t s_u32[2];
     __shared__ double s_total;
-    __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
+    __shared__ double s_wscale_d[MODE == kServer ? kServerLdsDoubles : 1];
     __shared__ __align__(16) uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int G = (int)gridDim.x;
     // Workgroups are dispatched to the eight XCDs in turn; outside the server stage
@@ -788,7 +864,7 @@ k_compress_onepass(CompressArgs a) {
 template <int MODE, int GT>
 __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     __shared__ DD s_red[kWaves];
-    __shared__ double s_wscale_d[MODE == kServer ? kWBatch : 1];
+    __shared__ double s_wscale_d[MODE == kServer ? kServerLdsDoubles : 1];
     __shared__ __align__(16) uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
     const int tile_id = a.list[blockIdx.x];
     const TileDesc t = a.tiles[tile_id];

@@ -116,3 +116,75 @@ def test_server_scale_exponent_cases(Wn):
         assert_exact(f"server e step {step}", host(esd), es)
         assert_exact(f"server m step {step}", host(md), m_out)
         assert ob.onebit_workspace_status(buf.ws) == 0
+
+
+def _boundary_cases(rng, Wn):
+    """Worker scales per chunk around the server's exact-sum condition (every scale
+    finite and an exponent-field spread of at most 29 - ceil(log2 W)): the widest
+    spread that still qualifies, with full mantissas at the top and an odd one at the
+    bottom so that the sums need all 53 bits; one step wider; a spread of 40, where
+    the ordered sum does round; the subnormal floor at the widest qualifying spread;
+    an infinite and a NaN scale; signed zeros; equal scales."""
+    f32 = np.float32
+    lg = int(np.ceil(np.log2(Wn))) if Wn > 1 else 0
+    d = 29 - lg
+
+    def spread(top_exp, width):
+        s = np.ldexp(rng.uniform(1, 2, Wn), rng.integers(top_exp - width, top_exp + 1, Wn)).astype(f32)
+        s[0] = np.float32(np.ldexp(2.0 - 2.0 ** -23, top_exp))
+        if Wn > 1:
+            s[-1] = np.float32(np.ldexp(1.0 + 2.0 ** -23, top_exp - width))
+        return s
+
+    cases = [spread(0, d), spread(-3, d + 1), spread(5, 40)]
+    floor = spread(-126 + d, d)                                  # lowest field 1 (smallest normals)
+    if Wn > 1:
+        floor[-1] = np.float32(2.0 ** -149)                      # a subnormal counts as field 1
+    cases.append(floor)
+    inf_case = spread(-2, 3)
+    inf_case[Wn // 2] = np.inf
+    nan_case = spread(-2, 3)
+    nan_case[0] = np.nan
+    zeros = spread(-8, 2)
+    zeros[0] = -0.0
+    if Wn > 2:
+        zeros[1] = 0.0
+    cases += [inf_case, nan_case, zeros, np.full(Wn, 2.0 ** -9 * 1.375, f32)]
+    return cases
+
+
+def _assert_same_or_both_nan(name, got, ref):
+    got, ref = np.asarray(got), np.asarray(ref)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), (name, int(np.isnan(got).sum()), int(nan.sum()))
+    assert_exact(name, got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("Wn", [2, 5, 16])
+def test_server_exact_sum_boundary(Wn):
+    """The regrouped (table) sum is taken only where it equals the ordered fp64 sum:
+    every output matches the oracle's ordered sum at, just beyond and far beyond the
+    exactness bound, and with non-finite scales."""
+    sizes = [4096, 2048 * 3 + 5, 31, 4096 + 64, 8192, 2053, 4096, 999]
+    off = W.offsets_from_sizes(sizes)
+    buf = CompressBuffers(off)
+    n, words, nch = buf.n, buf.words, buf.n_chunks
+    rng = np.random.default_rng(1700 + Wn)
+    wb = rng.integers(0, 1 << 32, size=(Wn, words), dtype=np.uint64).astype(np.uint32)
+    sc = np.stack(_boundary_cases(rng, Wn), axis=1)  # [Wn, nch]
+    assert sc.shape == (Wn, nch)
+    es = (rng.standard_normal(n) * 1e-5).astype(np.float32)
+    say(f"server exact-sum boundary W={Wn}")
+    wbd = torch.from_numpy(wb.view(np.int32).copy()).to(DEV)
+    scd = torch.from_numpy(sc.copy()).to(DEV)
+    esd = torch.from_numpy(es.copy()).to(DEV)
+    sbits = torch.zeros(words, dtype=torch.int32, device=DEV)
+    sscales = torch.zeros(nch, dtype=torch.float32, device=DEV)
+    md = torch.zeros(n, dtype=torch.float32, device=DEV)
+    ob.onebit_server_reduce(buf.plan, wbd, scd, esd, sbits, sscales, md, buf.ws)
+    rb, rs, m_out = oracle.server_reduce(off, wb, sc, es)
+    torch.cuda.synchronize()
+    assert_bits_exact("server bits", host(sbits).view(np.uint32), rb)
+    _assert_same_or_both_nan("server scales", host(sscales), rs)
+    _assert_same_or_both_nan("server e", host(esd), es)
+    _assert_same_or_both_nan("server m", host(md), m_out)
