@@ -28,6 +28,7 @@ Profiling (rocprofv3 runs the program itself, so these modes only do the work):
                                        (kernel trace+stats, --pmc FETCH_SIZE,
                                        --pmc WRITE_SIZE) into the text summary kept
                                        under profiles/ (printed to stdout)
+  python bench.py --placement          LoCo and an in-place stream by buffer placement
   python bench.py --ceilings [--ceilings-elems N]
                                        streaming ceilings by read/write mix, cache
                                        policy and workgroup shape, N fp32 elements
@@ -811,11 +812,15 @@ def main():
     ap.add_argument("--summarize-quantizers", nargs=2, metavar=("KT_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("KT_DIR", "COMMAND"))
     ap.add_argument("--ceilings", action="store_true")
+    ap.add_argument("--placement", action="store_true")
     ap.add_argument("--ceilings-elems", type=int, default=268_435_456,
                     help="fp32 elements per stream for --ceilings (a multiple of 4)")
     args = ap.parse_args()
     if args.ceilings:
         sys.stdout.write(ceilings(args.ceilings_elems))
+        return
+    if args.placement:
+        sys.stdout.write(placement())
         return
     if args.summarize_profile:
         sys.stdout.write(summarize_profile(*args.summarize_profile))
@@ -1005,6 +1010,81 @@ def ceilings(n=268_435_456):
                        f"{best256:.0f} |")
             log(f"[ceilings] {reads}+{writes} {pol}: {best[0]:.0f} GB/s ({best[1]}), 256-thread {best256:.0f}")
     del bufs
+    return "\n".join(out) + "\n"
+
+
+def placement():
+    """LoCo quantize (4-bit, buckets of 1024, the QSGD workload's 1.3e9-element bf16
+    gradient) and the plain streaming probe with two inputs, the second written in
+    place (as LoCo's error average is), by the placement of the second buffer: its
+    own allocation, or in one allocation at several gaps after the first.  Returns
+    the markdown summary kept under profiles/."""
+    import torch
+    from error_compensated_bit_amd import onebit as ob
+    from error_compensated_bit_amd import workloads as W
+    ensure_built()
+    dev = "cuda:0"
+    qg = W.QsgdWorkload()
+    n = qg.n
+    nb = (n + qg.bucket - 1) // qg.bucket
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_ms(call, reps=4):
+        call()
+        ts = []
+        for _ in range(reps):
+            ev0.record()
+            call()
+            ev1.record()
+            ev1.synchronize()
+            ts.append(ev0.elapsed_time(ev1))
+        return min(ts)
+
+    gaps_kib = [0, 4, 64, 1024, 2048, 65536]
+    out = [f"# Buffer placement: LoCo quantize and an in-place 2-read/1-write stream ({n} elements)", ""]
+    out.append("Command (from the repository root, on one MI355X):")
+    out.append("```")
+    out.append("python bench.py --placement")
+    out.append("```")
+    out.append("LoCo: 4-bit codes, buckets of 1024, bf16 gradient (N(0, 1) x 10^U(-4, -2) per 2^20 block), fp32 error "
+               "average updated in place, beta 0.9; best of 4 calls between HIP events.  Stream: onebit_stream_probe "
+               f"over {n // 4} fp32 elements per stream, inputs a and b, output b (in place), nontemporal, best of "
+               "grids 4 and 6 per CU.")
+    out.append("")
+    out.append("| second buffer | LoCo ms | LoCo G elem/s | stream GB/s |")
+    out.append("|---|---|---|---|")
+    codes = torch.zeros((n + 1) // 2, dtype=torch.uint8, device=dev)
+    norms = torch.zeros(nb, device=dev)
+    g = W.qsgd_gradient(qg, 0, device=dev)
+    ns = n // 4
+    pool = torch.zeros(2 * n + max(gaps_kib) * 1024 + 4 * n + 4096, dtype=torch.uint8, device=dev)
+
+    def stream_gbps(a, b):
+        ms = min(best_ms(lambda m=m: ob.onebit_stream_probe([a, b], [b], cus * m, 256, 1), 3) for m in (4, 6))
+        return 12.0 * ns / (ms * 1e-3) / 1e9
+
+    e = torch.zeros(n, device=dev)
+    t = best_ms(lambda: ob.loco_quantize(g, e, qg.bucket, 4, 0.9, 7, codes, norms))
+    a_sep, b_sep = e[:ns], torch.zeros(ns, device=dev)
+    out.append(f"| own allocation | {t:.3f} | {n / t / 1e6:.0f} | {stream_gbps(a_sep, b_sep):.0f} |")
+    log(f"[placement] separate: {t:.3f} ms")
+    del e, a_sep, b_sep
+    gv = pool[:2 * n].view(torch.bfloat16)
+    gv.copy_(g)
+    del g
+    torch.cuda.empty_cache()
+    spool = torch.zeros(8 * ns + max(gaps_kib) * 1024 + 4096, dtype=torch.uint8, device=dev)   # the stream's own
+    for gap in gaps_kib:
+        start = (2 * n + gap * 1024 + 255) // 256 * 256
+        ev_ = pool[start:start + 4 * n].view(torch.float32)
+        t = best_ms(lambda: ob.loco_quantize(gv, ev_, qg.bucket, 4, 0.9, 7, codes, norms))
+        a = spool[:4 * ns].view(torch.float32)
+        sb = (4 * ns + gap * 1024 + 255) // 256 * 256
+        b = spool[sb:sb + 4 * ns].view(torch.float32)
+        out.append(f"| same allocation, {gap} KiB after the first | {t:.3f} | {n / t / 1e6:.0f} | {stream_gbps(a, b):.0f} |")
+        log(f"[placement] gap {gap} KiB: {t:.3f} ms")
+    del pool, spool
     return "\n".join(out) + "\n"
 
 
