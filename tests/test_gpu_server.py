@@ -160,7 +160,7 @@ def _assert_same_or_both_nan(name, got, ref):
     assert_exact(name, got[~nan], ref[~nan])
 
 
-@pytest.mark.parametrize("Wn", [2, 5, 16])
+@pytest.mark.parametrize("Wn", [2, 5, 16, 33, 1024])
 def test_server_exact_sum_boundary(Wn):
     """The regrouped (table) sum is taken only where it equals the ordered fp64 sum:
     every output matches the oracle's ordered sum at, just beyond and far beyond the
