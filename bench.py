@@ -881,6 +881,13 @@ def main():
     if base:
         log(f"[bench] cpu oracle {base['value'] / 1e6:.1f} M params/s on {base['sample']}")
 
+    line = headline_line(wl, bpe, head, base, ceiling, rows, args.steps, args.warmup)
+    print(json.dumps(line), flush=True)
+
+
+def headline_line(wl, bpe, head, base, ceiling, rows, steps, warmup):
+    """The one JSON line: the headline measurement (head, from bench_compress), the CPU
+    baseline (base, or None), the live streaming ceiling and the other rows."""
     k_ms = head.get("onepass_ms")
     achieved = head.get("onepass_gbps")
     line = {
@@ -888,8 +895,8 @@ def main():
         "value": head["params_per_s"],
         "unit": "params/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": head["seconds_per_call"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -917,7 +924,7 @@ def main():
         "ceiling": dict(ceiling, kernel_frac_of_ceiling=(achieved / ceiling["gbps_5r3w"]) if achieved else None),
         "rows": rows,
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def stream_ceiling(dev, n=335_544_320):

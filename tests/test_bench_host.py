@@ -1,6 +1,7 @@
 """Host-side contract of bench.py (no GPU): the multi-GPU flag is refused with a
 message, the committed profile summaries parse and match the sources they were
-taken from, and every secondary row gets its CPU-oracle timing."""
+taken from, every secondary row gets its CPU-oracle timing, and the JSON line
+carries every field the benchmark contract names."""
 import os
 import subprocess
 import sys
@@ -52,3 +53,33 @@ def test_every_row_gets_a_cpu_oracle_timing():
         c = rows[k].get("cpu_oracle")
         assert c is not None, k
         assert c["value"] > 0 and c["cores"] == 1 and c["kind"] == "oracle" and c["unit"]
+
+
+def test_headline_line_carries_every_field_of_the_contract():
+    """The JSON line built from made-up measurements of the BERT-Large workload has the
+    fields the benchmark contract names, with the roofline and CPU baseline objects."""
+    import json
+    from error_compensated_bit_amd import workloads as W
+    wl = W.bert_like()
+    bpe = bench.B_COMPRESS_F32
+    head = {"params_per_s": 1.7e11, "seconds_per_call": 1.97e-3, "gbps": 5460.0, "onepass_ms": 1.76,
+            "onepass_gbps": 5550.0, "onepass_elements": 303_889_410, "plan": {"tiles": 1}, "kernels": {}}
+    base = {"value": 1.57e8, "unit": "params/s", "cores": 1, "kind": "oracle", "sample": "two chunks",
+            "cpu_model": "x", "host_cpus": 16, "cpus_allowed": [0], "pinned_core": 0}
+    ceiling = {"gbps_5r3w": 5800.0, "grid_5r3w": 1024, "block_5r3w": 1024, "elements": 1, "kernel": "probe"}
+    line = json.loads(json.dumps(bench.headline_line(wl, bpe, head, base, ceiling, {}, 30, 3)))
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+              "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in line, k
+    assert line["n_gpus"] == 1 and line["steps"] == 30 and line["warmup"] == 3
+    assert line["unit"] == "params/s" and line["higher_is_better"] is True and line["vs_baseline"] is None
+    assert "workload" in line["config"] and "model" not in line["config"]
+    r = line["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in r, k
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["frac"] - 5550.0 / 8000.0) < 1e-12
+    assert abs(r["bytes_per_launch"] - bpe * 303_889_410) < 1.0
+    for k in ("value", "unit", "cores", "kind", "sample"):
+        assert k in line["cpu_baseline"], k
+    assert line["cpu_baseline"]["kind"] == "oracle"
