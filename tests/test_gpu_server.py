@@ -188,3 +188,36 @@ def test_server_exact_sum_boundary(Wn):
     _assert_same_or_both_nan("server scales", host(sscales), rs)
     _assert_same_or_both_nan("server e", host(esd), es)
     _assert_same_or_both_nan("server m", host(md), m_out)
+
+
+def test_server_exact_sum_boundary_on_a_two_pass_chunk():
+    """The same boundary cases with the first chunk too large for the one-pass kernel,
+    so that its server tiles take the two-pass kernels (W = 16)."""
+    Wn = 16
+    big = max(ob.onebit_onepass_max_elements(), 1) + 4097
+    off = W.offsets_from_sizes([big, 2048 * 3 + 5, 31, 4096 + 64, 8192, 2053, 4096, 999])
+    buf = CompressBuffers(off)
+    n, words, nch = buf.n, buf.words, buf.n_chunks
+    rng = np.random.default_rng(2900)
+    wb = rng.integers(0, 1 << 32, size=(Wn, words), dtype=np.uint64).astype(np.uint32)
+    cases = _boundary_cases(rng, Wn)
+    for first in (0, 2):                       # the widest exact spread, then one where the orders differ
+        order = [first] + list(range(1, nch))
+        sc = np.stack([cases[k] for k in order], axis=1)
+        assert sc.shape == (Wn, nch)
+        es = (rng.standard_normal(n) * 1e-5).astype(np.float32)
+        say(f"server two-pass boundary, first chunk case {first}")
+        wbd = torch.from_numpy(wb.view(np.int32).copy()).to(DEV)
+        scd = torch.from_numpy(sc.copy()).to(DEV)
+        esd = torch.from_numpy(es.copy()).to(DEV)
+        sbits = torch.zeros(words, dtype=torch.int32, device=DEV)
+        sscales = torch.zeros(nch, dtype=torch.float32, device=DEV)
+        md = torch.zeros(n, dtype=torch.float32, device=DEV)
+        ob.onebit_server_reduce(buf.plan, wbd, scd, esd, sbits, sscales, md, buf.ws)
+        rb, rs, m_out = oracle.server_reduce(off, wb, sc, es)
+        torch.cuda.synchronize()
+        assert_bits_exact("server bits", host(sbits).view(np.uint32), rb)
+        _assert_same_or_both_nan("server scales", host(sscales), rs)
+        _assert_same_or_both_nan("server e", host(esd), es)
+        _assert_same_or_both_nan("server m", host(md), m_out)
+        assert ob.onebit_workspace_status(buf.ws) == 0
