@@ -87,6 +87,35 @@ __device__ __forceinline__ float norm_of(DD acc) {
     return (float)__dsqrt_rn(t.hi);
 }
 
+// The bucket norm fl32(sqrt(S)) from a plain fp64 sum S' of the (exact) squares,
+// where that is provably the value the compensated sum gives.  All terms are
+// non-negative, so in any order |S' - S| <= (n - 1) 2^-53 S < 2^-43 S for n <= 1024,
+// and sqrt(S') is within 2^-44 of sqrt(S), relatively; the compensated sum is within
+// 2^-52 of S.  Where sqrt(S') lies farther than 2^-40 of itself from the midpoint
+// between the two fp32 values around it, all of them round to the same fp32 value.
+// The butterfly sum leaves the same bits in every lane (each step adds the same two
+// values, in either order), so the answer is the same over the wave.  Returns false
+// (the caller takes the compensated sum) near a midpoint, about once in 2^16
+// buckets, for a non-finite sum and at the top of the fp32 range.  Each lane passes
+// the plain sum of its own squares.
+__device__ __forceinline__ bool norm_from_plain_sum(double s, float &norm) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s = __dadd_rn(s, __shfl_xor(s, o));
+    const double r = __dsqrt_rn(s);
+    if (r == 0.0) {
+        norm = 0.0f;
+        return true;
+    }
+    const float f = (float)r;
+    const uint32_t fb = __float_as_uint(f);
+    const float nb = __uint_as_float((double)f <= r ? fb + 1u : fb - 1u);   // the neighbour on r's side
+    if (!isfinite(r) || !isfinite(f) || !isfinite(nb)) return false;
+    const double mid = 0.5 * ((double)f + (double)nb);                        // exact
+    if (!(fabs(r - mid) > 0x1p-40 * r)) return false;
+    norm = f;
+    return true;
+}
+
 // Group j (four elements) of this lane's sixteen in a whole bucket staged in LDS:
 // the value that is quantized (g, or with LoCo h = g + err) and, with LoCo, err.
 template <int GT, bool LOCO>
@@ -152,15 +181,26 @@ template <int BITS, int GT, bool LOCO>
 __device__ __forceinline__ void quantize_whole_bucket(const GArgs &a, int64_t b, int64_t base, int lane, float4 *wg,
                                                       float4 *we) {
     const int k0 = 16 * lane;
-    DD acc{0.0, 0.0};
+    float norm;
+    double ps = 0.0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float h[4], e[4];
         staged_group<GT, LOCO>(wg, we, lane, j, h, e);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dd_add_term(acc, (double)h[q] * (double)h[q]);   // each square exact
+        for (int q = 0; q < 4; ++q) ps = __fma_rn((double)h[q], (double)h[q], ps);   // each square exact
     }
-    const float norm = norm_of(acc);
+    if (!norm_from_plain_sum(ps, norm)) {
+        DD acc{0.0, 0.0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float h[4], e[4];
+            staged_group<GT, LOCO>(wg, we, lane, j, h, e);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dd_add_term(acc, (double)h[q] * (double)h[q]);
+        }
+        norm = norm_of(acc);
+    }
     const double rnorm = recip_rn64(norm);
     if (lane == 0) a.norms[b] = norm;
     uint32_t code[16];
@@ -287,10 +327,16 @@ __global__ __launch_bounds__(256) void k_qsgd_quantize_1024(GArgs a) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) f[q] = add_rn(f[q], ea[q]);     // compensated gradient h
         }
-        DD acc{0.0, 0.0};
+        float norm;
+        double ps = 0.0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) dd_add_term(acc, (double)f[q] * (double)f[q]);   // each square exact
-        const float norm = norm_of(acc);
+        for (int q = 0; q < 16; ++q) ps = __fma_rn((double)f[q], (double)f[q], ps);   // each square exact
+        if (!norm_from_plain_sum(ps, norm)) {
+            DD acc{0.0, 0.0};
+#pragma unroll
+            for (int q = 0; q < 16; ++q) dd_add_term(acc, (double)f[q] * (double)f[q]);
+            norm = norm_of(acc);
+        }
         const double rnorm = recip_rn64(norm);
         if (lane == 0) a.norms[b] = norm;
         uint32_t code[16];

@@ -346,3 +346,55 @@ def test_loco_full_size_two_steps():
             assert_exact(f"step {step} bucket {b} err_avg", host(e[lo:hi]), es)
         del gd
         say(f"  loco step {step}: {len(sample_b)} buckets match")
+
+
+# (a, b) with a^2 + b^2 = m^2 and m odd just above 2^24: m lies exactly halfway
+# between the fp32 values m - 1 and m + 1, so the bucket norm is a rounding tie (to
+# the even one, m - 1) and the quantizer must take its compensated sum.
+NORM_TIES = [(16777215, 8192, 16777217), (16777207, 24576, 16777225), (8470365, 14482028, 16777253)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("loco", [False, True])
+def test_norm_ties_take_the_compensated_sum(bits, loco):
+    """Buckets whose norm is an exact fp32 rounding tie (whole buckets of 1024 and the
+    ragged last one, several binades), next to ordinary buckets: norms, codes (and the
+    LoCo error average) equal the oracle's, and the norms are the tie's even value."""
+    n = 6 * 1024 + 300
+    rng = np.random.default_rng(4400 + bits + 10 * loco)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    want = {}
+    for b, (scale, (a_, b_, m)) in enumerate(zip([2.0 ** -30, 2.0 ** -90, 2.0 ** 40, 2.0 ** -12, 1.0, 2.0 ** -40],
+                                                 NORM_TIES * 2)):
+        if b == 4:
+            continue                                       # an ordinary bucket
+        lo = 1024 * b
+        g[lo:lo + 1024] = 0.0
+        g[lo + 7] = np.float32(a_ * scale)
+        g[lo + 900] = np.float32(-b_ * scale)
+        want[b] = np.float32((m - 1) * scale)
+    tail = 6 * 1024
+    g[tail:] = 0.0
+    g[tail + 5], g[tail + 299] = np.float32(NORM_TIES[0][0] * 2.0 ** -20), np.float32(NORM_TIES[0][1] * 2.0 ** -20)
+    want[6] = np.float32((NORM_TIES[0][2] - 1) * 2.0 ** -20)
+    gd = torch.from_numpy(g).to(DEV)
+    nb = 7
+    codes = torch.zeros(code_bytes(n, bits), dtype=torch.uint8, device=DEV)
+    norms = torch.zeros(nb, device=DEV)
+    if loco:
+        err = np.zeros(n, np.float32)
+        errd = torch.from_numpy(err.copy()).to(DEV)
+        ob.loco_quantize(gd, errd, 1024, bits, 0.9, 77, codes, norms)
+        rc, rn = oracle.loco_quantize(g, err, bucket=1024, bits=bits, beta=0.9, seed=77)
+    else:
+        ob.qsgd_quantize(gd, 1024, bits, 77, codes, norms)
+        rc, rn = oracle.qsgd_quantize(g, bucket=1024, bits=bits, seed=77)
+    torch.cuda.synchronize()
+    for b, v in want.items():
+        assert rn[b] == v, (b, rn[b], v)                    # the oracle's norm is the tie's even value
+    tag = f"norm ties bits {bits} loco {loco}"
+    say(tag)
+    assert_exact(f"{tag} norms", host(norms), rn)
+    assert_exact(f"{tag} codes", host(codes), rc)
+    if loco:
+        assert_exact(f"{tag} error average", host(errd), err)
