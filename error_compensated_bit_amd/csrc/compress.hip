@@ -36,7 +36,11 @@ namespace onebit {
 // kUpdatePM / kCompressPM: the update / compress-only modes with the momentum held
 // in its compressed form (the previous step's sign words and chunk scales) instead
 // of an fp32 array.
-enum Mode { kUpdate = 0, kCompressOnly = 1, kServer = 2, kUpdatePM = 3, kCompressPM = 4 };
+// kServerWide: the server stage for more than kWBatch workers (its exact-sum tables
+// are built batch by batch; a separate instantiation, so that the common case of at
+// most kWBatch workers keeps its own code).
+enum Mode { kUpdate = 0, kCompressOnly = 1, kServer = 2, kUpdatePM = 3, kCompressPM = 4, kServerWide = 5 };
+constexpr bool is_server(int mode) { return mode == kServer || mode == kServerWide; }
 constexpr bool packed_m(int mode) { return mode == kUpdatePM || mode == kCompressPM; }
 constexpr bool compress_only(int mode) { return mode == kCompressOnly || mode == kCompressPM; }
 
@@ -151,6 +155,7 @@ constexpr int kServerLdsDoubles = kWBatch + kWGroups * 16 + 1;  // scales, table
 // overlap, so no carry crosses them).
 __device__ __forceinline__ uint32_t spread_nibble(uint32_t n) { return (n * 0x00204081u) & 0x01010101u; }
 
+template <bool WIDE>
 __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileDesc &t, float (&c)[kPerThread],
                                               double *s_wscale_d, uint32_t *s_words) {
     const bool full = tile_full(a, t);
@@ -178,28 +183,45 @@ __device__ __forceinline__ void server_tile_c(const CompressArgs &a, const TileD
         __syncthreads();  // previous batch fully consumed
         double *s_tab = s_wscale_d + kWBatch;
         int *s_exact = reinterpret_cast<int *>(s_wscale_d + kWBatch + kWGroups * 16);
-        const bool tables = a.W <= kWBatch;
+        const bool tables = WIDE || a.W <= kWBatch;
         const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
         if (tables && wave == 0) {
-            // wave 0: the scales, and whether the regrouped sum is exact.  The lane
-            // index is made opaque here so that nothing derived from it is hoisted
-            // out of the tile loop and held in registers for the whole kernel.
+            // wave 0: this batch's scales and tables, and (with the first batch)
+            // whether the regrouped sum is exact over all W workers.  The lane index
+            // is made opaque here so that nothing derived from it is hoisted out of
+            // the tile loop and held in registers for the whole kernel.
             int j = (int)threadIdx.x;
             asm volatile("" : "+v"(j));
-            const float sv = j < wn ? a.wscales[(int64_t)j * a.n_chunks + t.chunk] : 0.0f;
+            const int wj = WIDE ? w0 + j : j;  // one batch only when !WIDE
+            const float sv = j < wn ? a.wscales[(int64_t)wj * a.n_chunks + t.chunk] : 0.0f;
             if (j < wn) s_wscale_d[j] = (double)sv;
-            const uint32_t bits = __float_as_uint(sv) & 0x7FFFFFFFu;
-            const int ef = (int)(bits >> 23);
-            int emin = bits != 0u ? max(ef, 1) : 255, emax = bits != 0u ? max(ef, 1) : 0;
-            int bad = ef == 255;
+            if (!WIDE || w0 == 0) {
+                // lane j: worker j's scale (in sv), then with WIDE workers j + 64,
+                // j + 128, ... (from j itself for the lanes past the first batch)
+                const uint32_t bits = __float_as_uint(sv) & 0x7FFFFFFFu;
+                const int ef = (int)(bits >> 23);
+                int emin = bits != 0u ? max(ef, 1) : 255, emax = bits != 0u ? max(ef, 1) : 0;
+                int bad = ef == 255;
+                if (WIDE) {
+                    for (int w = j < kWBatch ? j + 64 : j; w < a.W; w += 64) {
+                        const uint32_t wb = __float_as_uint(a.wscales[(int64_t)w * a.n_chunks + t.chunk]) & 0x7FFFFFFFu;
+                        const int we = (int)(wb >> 23);
+                        if (wb != 0u) {
+                            emin = min(emin, max(we, 1));
+                            emax = max(emax, max(we, 1));
+                        }
+                        bad |= we == 255;
+                    }
+                }
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                emin = min(emin, __shfl_xor(emin, o));
-                emax = max(emax, __shfl_xor(emax, o));
-                bad |= __shfl_xor(bad, o);
+                for (int o = 32; o > 0; o >>= 1) {
+                    emin = min(emin, __shfl_xor(emin, o));
+                    emax = max(emax, __shfl_xor(emax, o));
+                    bad |= __shfl_xor(bad, o);
+                }
+                const int lg = 32 - __clz((WIDE ? a.W : wn) - 1);  // ceil(log2 W), 0 for W = 1
+                if (j == 0) *s_exact = !bad && (emax == 0 || emax - emin <= 29 - lg);
             }
-            const int lg = 32 - __clz(wn - 1);  // ceil(log2 W), 0 for W = 1
-            if (j == 0) *s_exact = !bad && (emax == 0 || emax - emin <= 29 - lg);
             // table entry j (lane j) of group j / 16 from the scales of lanes 4g .. 4g+3
             const int g = j >> 4;
             double T = 0.0;
@@ -349,7 +371,7 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
                                                float (&c)[kPerThread], double *s_wscale_d,
                                                uint32_t *s_words) {
     const bool full = tile_full(a, t);
-    if (MODE != kServer) {
+    if (!is_server(MODE)) {
         const float *mb = packed_m(MODE) ? nullptr : a.m + t.start;
         const float *eb = a.e + t.start;
         // the packed momentum is 0 where the fp32 one would hold 0: +0 in masked
@@ -386,7 +408,7 @@ __device__ __forceinline__ void tile_compute_c(const CompressArgs &a, const Tile
             }
         }
     } else {
-        server_tile_c(a, t, c, s_wscale_d, s_words);
+        server_tile_c<MODE == kServerWide>(a, t, c, s_wscale_d, s_words);
     }
 }
 
@@ -566,7 +588,7 @@ template <int MODE, bool XB>
 __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDesc &t,
                                             const float (&c)[kPerThread], float scale) {
     const bool full = tile_full(a, t);
-    const uint32_t masked = MODE != kServer ? thread_mask_bits(a, t) : 0u;
+    const uint32_t masked = !is_server(MODE) ? thread_mask_bits(a, t) : 0u;
     float *eb = a.e + t.start;
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
@@ -582,7 +604,7 @@ __device__ __forceinline__ void tile_finish(const CompressArgs &a, const TileDes
                 e4[q] = 0.0f;
             }
         }
-        if (MODE == kServer) {
+        if (is_server(MODE)) {
             float *mo = a.m_out ? a.m_out + t.start : nullptr;
             if (full) {
                 store4(eb, k0, e4);
@@ -787,7 +809,7 @@ __device__ __forceinline__ void tile_queue_pop(const CompressArgs &a, TileQueue 
 }
 
 // Modes that load tile descriptors ahead (the light ones: compress-only and server).
-constexpr bool loads_ahead(int mode) { return mode == kCompressOnly || mode == kServer || mode == kCompressPM; }
+constexpr bool loads_ahead(int mode) { return mode == kCompressOnly || is_server(mode) || mode == kCompressPM; }
 
 template <int MODE, int GT>
 __device__ __forceinline__ Posted produce(const CompressArgs &a, int tile_id, const TileDesc &t, float4 *slot_c,
@@ -804,7 +826,7 @@ __device__ __forceinline__ Posted produce(const CompressArgs &a, int tile_id, co
 }
 
 template <int MODE, int GT, bool XB>
-__global__ __launch_bounds__(kBlock, MODE == kServer ? kServerWavesPerSimd : kOnepassWavesPerSimd) void
+__global__ __launch_bounds__(kBlock, is_server(MODE) ? kServerWavesPerSimd : kOnepassWavesPerSimd) void
 k_compress_onepass(CompressArgs a) {
     __shared__ float4 s_c[kDepth][kGroups * kBlock];
     __shared__ TileDesc s_tile[kDepth];
@@ -812,14 +834,14 @@ k_compress_onepass(CompressArgs a) {
     __shared__ DD s_red[kWaves];
     __shared__ uint32_t s_u32[2];
     __shared__ double s_total;
-    __shared__ double s_wscale_d[MODE == kServer ? kServerLdsDoubles : 1];
-    __shared__ __align__(16) uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
+    __shared__ double s_wscale_d[is_server(MODE) ? kServerLdsDoubles : 1];
+    __shared__ __align__(16) uint32_t s_words[is_server(MODE) ? kWBatch * kTileWords : 1];
     const int G = (int)gridDim.x;
     // Workgroups are dispatched to the eight XCDs in turn; outside the server stage
     // the ones on one XCD take consecutive list positions (one-pass BERT-Large step
     // 1.80 -> 1.78 ms; the server tiles were 3% slower with it).  Any bijection of
     // the workgroup ids keeps the progress argument above.
-    const bool xcd_runs = MODE != kServer && (G & 7) == 0;
+    const bool xcd_runs = !is_server(MODE) && (G & 7) == 0;
     const int b = xcd_runs ? (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
     const int mine = a.list_len > b ? (a.list_len - b + G - 1) / G : 0;  // tiles of this workgroup
     TileQueue q = tile_queue<loads_ahead(MODE)>(a, b, G, mine);
@@ -864,8 +886,8 @@ k_compress_onepass(CompressArgs a) {
 template <int MODE, int GT>
 __global__ __launch_bounds__(kBlock) void k_compress_pass1(CompressArgs a) {
     __shared__ DD s_red[kWaves];
-    __shared__ double s_wscale_d[MODE == kServer ? kServerLdsDoubles : 1];
-    __shared__ __align__(16) uint32_t s_words[MODE == kServer ? kWBatch * kTileWords : 1];
+    __shared__ double s_wscale_d[is_server(MODE) ? kServerLdsDoubles : 1];
+    __shared__ __align__(16) uint32_t s_words[is_server(MODE) ? kWBatch * kTileWords : 1];
     const int tile_id = a.list[blockIdx.x];
     const TileDesc t = a.tiles[tile_id];
     float c[kPerThread];
@@ -902,7 +924,7 @@ __global__ __launch_bounds__(kBlock) void k_compress_pass2(CompressArgs a) {
 // ---------------------------------------------------------- host side
 template <int MODE, int GT, bool XB>
 static onebit_status_t launch(const onebit_plan_s *p, CompressArgs a, hipStream_t stream) {
-    const int base = MODE == kServer ? kProfServerPass1 : kProfPass1;
+    const int base = is_server(MODE) ? kProfServerPass1 : kProfPass1;
     // Two-pass chunks first, pass 2 right after pass 1 so that the c it re-reads
     // is still in the memory-side cache; then the one-pass kernel for the rest.
     if (p->n_big > 0) {
@@ -987,6 +1009,7 @@ int32_t resident_capacity(int device) {
         reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, kGradBF16, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kCompressOnly, kGradF16, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kServer, kGradF32, false>),
+        reinterpret_cast<const void *>(&k_compress_onepass<kServerWide, kGradF32, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF32, false>),
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradF32, true>),
         reinterpret_cast<const void *>(&k_compress_onepass<kUpdatePM, kGradBF16, false>),
@@ -1255,6 +1278,7 @@ extern "C" onebit_status_t onebit_server_reduce(onebit_plan_t plan, int W, const
     a.publish = ws.publish;
     a.slots = ws.slots;
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    if (W > kWBatch) return launch<kServerWide, kGradF32, false>(plan, a, static_cast<hipStream_t>(stream));
     return launch<kServer, kGradF32, false>(plan, a, static_cast<hipStream_t>(stream));
 }
 
