@@ -134,14 +134,16 @@ __device__ __forceinline__ void load4(const float *base, uint32_t k0, float (&v)
 // acc), the +-1.0 built from the sign bit in two instructions (server 0.304 ->
 // 0.294 ms on 16 x 64M against a sign-bit xor on s).  The server error is loaded
 // before the words are staged, so the two loads are in flight together (0.291 ->
-// 0.285 ms).  For W <= kWBatch and scales whose partial sums are all exact, the
-// sums come from per-group tables instead (below; 0.284 -> 0.253 ms).
+// 0.285 ms).  For scales whose partial sums are all exact, the sums come from
+// per-group tables instead (below; W = 16: 0.284 -> 0.253 ms; with more than
+// kWBatch workers the kServerWide instantiation builds them batch by batch).
 constexpr int kWBatch = 16;
 constexpr int kTileWords = kTile / 32;
 
-// Exact-sum tables (W <= kWBatch): for each group of four workers, the 16 signed
-// sums +-s_4g +-s_4g+1 +-s_4g+2 +-s_4g+3 (bit k of the entry index set: worker 4g+k
-// negative), so that an element adds four table entries instead of W scales.  The
+// Exact-sum tables: for each group of four workers of a batch, the 16 signed sums
+// +-s_4g +-s_4g+1 +-s_4g+2 +-s_4g+3 (bit k of the entry index set: worker 4g+k
+// negative), so that an element adds four table entries per batch of kWBatch
+// workers instead of kWBatch scales.  The
 // regrouped sum equals the ordered one exactly when no partial sum of either rounds:
 // every scale is finite and, with u the smallest unit in the last place of the
 // nonzero scales (2^(e_min - 150) for biased exponent fields e, subnormals counted
